@@ -1,0 +1,235 @@
+"""bit_packing_amd -- Python binding of the MI355X Invariant Bit Packing codec.
+
+Argument marshalling only: every step of the codec runs in the HIP kernels of
+``libibp.so`` (built from ``csrc/`` for gfx950, C ABI in ``include/ibp.h``).
+torch supplies device memory, pinned host memory and streams.  The functions
+have the names of the C entry points:
+
+* ``ibp_build_metadata`` -- Mask/Bitval from a sample batch (IBP page,
+  "Algoritmo Core", step 1);
+* ``ibp_compress`` -- fused size / look-back / pack compression (step 2);
+* ``ibp_decompress`` -- device-resident decompression (step 3);
+* ``ibp_decompress_gather`` -- rows decoded straight from pinned host memory
+  over PCIe ("Integrazione del Sistema", PCIe transfer compression);
+* ``ibp_gather_raw`` -- the uncompressed zero-copy gather the codec is
+  measured against.
+
+There is no fallback: if ``libibp.so`` is missing or no GPU is present the calls
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # imported first so that libibp.so binds to the HIP runtime torch loaded
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libibp.so")
+
+IBP_OK, IBP_ERR_INVALID_ARG, IBP_ERR_SIZE, IBP_ERR_CAPACITY, IBP_ERR_DEVICE = 0, 1, 2, 3, 4
+IBP_DEVERR_CORRUPT, IBP_DEVERR_BAD_ID, IBP_DEVERR_TIMEOUT = 1, 2, 4
+IBP_MAX_S = 1024
+
+EXPORTS = (
+    "ibp_status_str", "ibp_num_segments", "ibp_max_stream_bytes", "ibp_stream_bytes",
+    "ibp_metadata_workspace_bytes", "ibp_compress_workspace_bytes", "ibp_build_metadata",
+    "ibp_compress", "ibp_decompress", "ibp_decompress_gather", "ibp_gather_raw",
+)
+
+
+class ibp_meta_t(ctypes.Structure):
+    """Mask and Bitval of a dataset; only the low W bits are used."""
+    _fields_ = [("W", ctypes.c_uint32), ("reserved", ctypes.c_uint32),
+                ("mask", ctypes.c_uint64), ("bitval", ctypes.c_uint64)]
+
+    def __repr__(self):
+        return f"ibp_meta_t(W={self.W}, mask={self.mask:#x}, bitval={self.bitval:#x})"
+
+
+def make_meta(W: int, mask: int, bitval: int) -> ibp_meta_t:
+    return ibp_meta_t(W, 0, mask, bitval)
+
+
+class IBPError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_name(status)}")
+
+
+_lib = None
+_u64, _u32, _vp, _dbl, _int = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_double, ctypes.c_int
+_metap = ctypes.POINTER(ibp_meta_t)
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libibp.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(bit_packing_amd.build.build_library())")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.ibp_status_str.argtypes = [_int]
+        lib.ibp_status_str.restype = ctypes.c_char_p
+        lib.ibp_num_segments.argtypes = [_u64, _u32]
+        lib.ibp_max_stream_bytes.argtypes = [_u64, _u32]
+        lib.ibp_stream_bytes.argtypes = [_u64]
+        lib.ibp_metadata_workspace_bytes.argtypes = [_u64, _u32]
+        lib.ibp_compress_workspace_bytes.argtypes = [_u64, _u32]
+        for f in ("ibp_num_segments", "ibp_max_stream_bytes", "ibp_stream_bytes",
+                  "ibp_metadata_workspace_bytes", "ibp_compress_workspace_bytes"):
+            getattr(lib, f).restype = _u64
+        lib.ibp_build_metadata.argtypes = [_vp, _u64, _u32, _dbl, _metap, _vp, _vp, _u64, _vp]
+        lib.ibp_compress.argtypes = [_metap, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _u64, _vp, _vp]
+        lib.ibp_decompress.argtypes = [_metap, _vp, _u64, _vp, _u64, _u32, _vp, _vp, _vp]
+        lib.ibp_decompress_gather.argtypes = [_metap, _vp, _u64, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_gather_raw.argtypes = [_vp, _u64, _u64, _vp, _u64, _vp, _vp, _vp]
+        for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",
+                  "ibp_gather_raw"):
+            getattr(lib, f).restype = _int
+        _lib = lib
+    return _lib
+
+
+def status_name(status: int) -> str:
+    return load_library().ibp_status_str(status).decode()
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != IBP_OK:
+        raise IBPError(rc, what)
+
+
+def _ptr(t: torch.Tensor | None):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the codec must be contiguous")
+    return t.data_ptr()
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _device(*tensors) -> torch.device:
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            return t.device
+    return torch.device("cuda", torch.cuda.current_device())
+
+
+# ------------------------------------------------------------------ size queries
+
+def ibp_num_segments(n_chunks: int, S: int) -> int:
+    return int(load_library().ibp_num_segments(n_chunks, S))
+
+
+def ibp_max_stream_bytes(n_chunks: int, W: int) -> int:
+    return int(load_library().ibp_max_stream_bytes(n_chunks, W))
+
+
+def ibp_stream_bytes(total_bits: int) -> int:
+    return int(load_library().ibp_stream_bytes(total_bits))
+
+
+def ibp_metadata_workspace_bytes(n_sample_chunks: int, W: int) -> int:
+    return int(load_library().ibp_metadata_workspace_bytes(n_sample_chunks, W))
+
+
+def ibp_compress_workspace_bytes(n_chunks: int, S: int) -> int:
+    return int(load_library().ibp_compress_workspace_bytes(n_chunks, S))
+
+
+# ------------------------------------------------------------------ codec
+
+def ibp_build_metadata(samples: torch.Tensor, W: int, T: float, stream=None,
+                       workspace: torch.Tensor | None = None) -> tuple[ibp_meta_t, list[int]]:
+    """(meta, per-position one-counts) of a device sample batch of W-bit chunks."""
+    n = _nbytes(samples) // (W // 8) if W in (32, 64) else 0
+    if workspace is None:
+        workspace = torch.empty(max(ibp_metadata_workspace_bytes(n, W), 8), dtype=torch.uint8,
+                                device=_device(samples))
+    meta = ibp_meta_t()
+    counts = (ctypes.c_uint64 * 64)()
+    rc = load_library().ibp_build_metadata(_ptr(samples), n, W, T, ctypes.byref(meta), counts,
+                                           _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(rc, "ibp_build_metadata")
+    return meta, [int(c) for c in counts[:W]]
+
+
+@dataclass
+class Compressed:
+    """A compressed tensor: stream bytes, nseg + 1 bit offsets and the format parameters."""
+    stream: torch.Tensor    # uint8, capacity >= used bytes
+    offsets: torch.Tensor   # int64 bit offsets, nseg + 1 entries
+    n_chunks: int
+    S: int
+    meta: ibp_meta_t
+
+
+def ibp_compress(meta: ibp_meta_t, x: torch.Tensor, S: int, stream=None, err: torch.Tensor | None = None,
+                 out_stream: torch.Tensor | None = None, out_offsets: torch.Tensor | None = None,
+                 workspace: torch.Tensor | None = None) -> Compressed:
+    """Compress the bytes of x (read as W-bit little-endian chunks) with segments of S chunks."""
+    W = meta.W
+    n_bytes = _nbytes(x)
+    n = n_bytes // (W // 8) if W in (32, 64) else 0
+    dev = _device(x)
+    if out_stream is None:
+        out_stream = torch.empty(max(ibp_max_stream_bytes(n, W), 16), dtype=torch.uint8, device=dev)
+    if out_offsets is None:
+        out_offsets = torch.empty(ibp_num_segments(n, S) + 1, dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(ibp_compress_workspace_bytes(n, S), 8), dtype=torch.uint8, device=dev)
+    rc = load_library().ibp_compress(ctypes.byref(meta), _ptr(x), n_bytes, S, _ptr(out_stream),
+                                     _nbytes(out_stream), _ptr(out_offsets), _ptr(workspace),
+                                     _nbytes(workspace), _ptr(err), _stream(stream))
+    _check(rc, "ibp_compress")
+    return Compressed(out_stream, out_offsets, n, S, meta)
+
+
+def ibp_decompress(meta: ibp_meta_t, stream_buf: torch.Tensor, offsets: torch.Tensor, n_chunks: int, S: int,
+                   out: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decompress n_chunks chunks; returns out (uint8 unless an output tensor is given)."""
+    if out is None:
+        out = torch.empty(n_chunks * (meta.W // 8), dtype=torch.uint8, device=_device(offsets, stream_buf))
+    rc = load_library().ibp_decompress(ctypes.byref(meta), _ptr(stream_buf), _nbytes(stream_buf), _ptr(offsets),
+                                       n_chunks, S, _ptr(out), _ptr(err), _stream(stream))
+    _check(rc, "ibp_decompress")
+    return out
+
+
+def ibp_decompress_gather(meta: ibp_meta_t, stream_buf: torch.Tensor, offsets: torch.Tensor, S: int,
+                          ids: torch.Tensor, out: torch.Tensor | None = None, err: torch.Tensor | None = None,
+                          stream=None, n_segments: int | None = None) -> torch.Tensor:
+    """Row j of out (S chunks) = segment ids[j]; stream_buf may be pinned host memory."""
+    if n_segments is None:
+        n_segments = offsets.numel() - 1
+    if out is None:
+        out = torch.empty(ids.numel() * S * (meta.W // 8), dtype=torch.uint8, device=_device(ids, offsets))
+    rc = load_library().ibp_decompress_gather(ctypes.byref(meta), _ptr(stream_buf), _nbytes(stream_buf),
+                                              _ptr(offsets), n_segments, S, _ptr(ids), ids.numel(), _ptr(out),
+                                              _ptr(err), _stream(stream))
+    _check(rc, "ibp_decompress_gather")
+    return out
+
+
+def ibp_gather_raw(src: torch.Tensor, row_bytes: int, ids: torch.Tensor, out: torch.Tensor | None = None,
+                   err: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Uncompressed zero-copy gather: row j of out = row ids[j] of src (rows of row_bytes bytes)."""
+    n_rows = _nbytes(src) // row_bytes
+    if out is None:
+        out = torch.empty(ids.numel() * row_bytes, dtype=torch.uint8, device=_device(ids))
+    rc = load_library().ibp_gather_raw(_ptr(src), row_bytes, n_rows, _ptr(ids), ids.numel(), _ptr(out),
+                                       _ptr(err), _stream(stream))
+    _check(rc, "ibp_gather_raw")
+    return out

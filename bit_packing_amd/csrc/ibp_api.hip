@@ -1,0 +1,319 @@
+// ibp_api.hip -- the extern "C" entry points declared in include/ibp.h.
+//
+// Every argument is checked here, on the host, before any HIP call; then the
+// launch geometry and the workspace layout are derived and the kernels in
+// ibp_kernels.hip are enqueued on the caller's stream.
+#include <string.h>
+
+#include "ibp.h"
+#include "ibp_internal.h"
+
+namespace {
+
+using namespace ibp;
+
+uint64_t full_bits(uint32_t W) { return W >= 64 ? ~0ull : ((1ull << W) - 1ull); }
+
+bool width_ok(uint32_t W) { return W == 32 || W == 64; }
+
+uint32_t log2_if_pow2(uint32_t S) {
+  if (S == 0 || (S & (S - 1u))) return kNotPow2;
+  uint32_t l = 0;
+  while ((1u << l) != S) ++l;
+  return l;
+}
+
+bool aligned(const void *p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Mask/Bitval -> kernel parameters: popcount and the runs of free positions.
+bool make_params(const ibp_meta_t *m, CodecParams *p) {
+  if (!m || !width_ok(m->W) || m->reserved != 0) return false;
+  const uint64_t full = full_bits(m->W);
+  if ((m->mask & ~full) || (m->bitval & ~m->mask)) return false;
+  memset(p, 0, sizeof(*p));
+  p->mask = m->mask;
+  p->bitval = m->bitval;
+  p->W = m->W;
+  p->pc = (uint32_t)__builtin_popcountll(m->mask);
+  const uint64_t F = ~m->mask & full;
+  uint32_t n = 0, cum = 0;
+  for (uint32_t b = 0; b < m->W;) {
+    if (!((F >> b) & 1ull)) {
+      ++b;
+      continue;
+    }
+    const uint32_t start = b;
+    while (b < m->W && ((F >> b) & 1ull)) ++b;
+    const uint32_t len = b - start;
+    p->runs.pmask[n] = full_bits(len) << cum;
+    p->runs.shift[n] = start - cum;
+    cum += len;
+    ++n;
+  }
+  p->runs.n = n;
+  return true;
+}
+
+// Bits per segment can never exceed S * (W + 1); total bits must fit the 62-bit
+// look-back value field.
+bool total_fits(uint64_t n_chunks, uint32_t W) {
+  return n_chunks < (1ull << 55) && n_chunks * (uint64_t)(W + 1) < (1ull << 62);
+}
+
+uint32_t meta_blocks(uint64_t n) {
+  const uint64_t want = (n + (uint64_t)kBlock * 16 - 1) / ((uint64_t)kBlock * 16);
+  return (uint32_t)(want < 1 ? 1 : (want > kMetaMaxBlocks ? kMetaMaxBlocks : want));
+}
+
+uint32_t enc_segs_per_tile(uint32_t S) { return S >= kEncTileChunks ? 1u : kEncTileChunks / S; }
+
+uint64_t enc_tiles(uint64_t n_chunks, uint32_t S) {
+  const uint64_t nseg = (n_chunks + S - 1) / S;
+  const uint32_t G = enc_segs_per_tile(S);
+  return (nseg + G - 1) / G;
+}
+
+uint32_t dec_units_per_tile(uint32_t S) {
+  uint32_t G = S >= kDecTileChunks ? 1u : kDecTileChunks / S;
+  return G > kDecMaxUnits ? kDecMaxUnits : G;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? IBP_OK : IBP_ERR_DEVICE; }
+
+// Device-visible address of the byte range [p, p + bytes), or nullptr when the
+// range does not lie inside one device allocation or one pinned host allocation.
+// Pageable host memory and stray pointers are refused here instead of being
+// handed to a kernel, where they would fault the GPU.  Pinned host memory is
+// returned through its device mapping (the zero-copy path).
+const void *device_range(const void *p, uint64_t bytes) {
+  if (bytes == 0) return p;
+  if (!p) return nullptr;
+  hipPointerAttribute_t at;
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  const char *dev;
+  if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
+    dev = static_cast<const char *>(p);
+  } else if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    const char *hp = at.hostPointer ? static_cast<const char *>(at.hostPointer) : static_cast<const char *>(p);
+    dev = static_cast<const char *>(at.devicePointer) + (static_cast<const char *>(p) - hp);
+  } else {
+    return nullptr;
+  }
+  hipDeviceptr_t base = nullptr;
+  size_t size = 0;
+  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)dev) == hipSuccess) {
+    if ((uintptr_t)dev < (uintptr_t)base || (uintptr_t)dev + bytes > (uintptr_t)base + size) return nullptr;
+  } else {
+    (void)hipGetLastError();
+    if (at.type != hipMemoryTypeHost) return nullptr;
+  }
+  return dev;
+}
+
+template <typename P> bool view(P *&p, uint64_t bytes) {
+  const void *d = device_range(p, bytes);
+  if (bytes && !d) return false;
+  p = const_cast<P *>(static_cast<const P *>(d));
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+IBP_API const char *ibp_status_str(int status) {
+  switch (status) {
+    case IBP_OK: return "IBP_OK";
+    case IBP_ERR_INVALID_ARG: return "IBP_ERR_INVALID_ARG";
+    case IBP_ERR_SIZE: return "IBP_ERR_SIZE";
+    case IBP_ERR_CAPACITY: return "IBP_ERR_CAPACITY";
+    case IBP_ERR_DEVICE: return "IBP_ERR_DEVICE";
+    default: return "IBP_ERR_UNKNOWN";
+  }
+}
+
+IBP_API uint64_t ibp_num_segments(uint64_t n_chunks, uint32_t S) {
+  return S ? (n_chunks + S - 1) / S : 0;
+}
+
+IBP_API uint64_t ibp_max_stream_bytes(uint64_t n_chunks, uint32_t W) {
+  const uint64_t bytes = (n_chunks * (uint64_t)(W + 1) + 7) / 8;
+  return (bytes + 15) & ~15ull;
+}
+
+IBP_API uint64_t ibp_stream_bytes(uint64_t total_bits) { return (((total_bits + 7) / 8) + 15) & ~15ull; }
+
+IBP_API uint64_t ibp_metadata_workspace_bytes(uint64_t n_sample_chunks, uint32_t W) {
+  const uint64_t w = width_ok(W) ? W : 64;
+  return ((uint64_t)meta_blocks(n_sample_chunks) * w + 66) * 8;
+}
+
+IBP_API uint64_t ibp_compress_workspace_bytes(uint64_t n_chunks, uint32_t S) {
+  if (S == 0) return 0;
+  return 8 + 16 * enc_tiles(n_chunks, S);
+}
+
+IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, uint32_t W, double T,
+                               ibp_meta_t *meta_out, uint64_t *counts_out, void *d_workspace,
+                               uint64_t workspace_bytes, void *hip_stream) {
+  if (!width_ok(W) || !meta_out || !d_workspace || !(T > 0.5 && T <= 1.0)) return IBP_ERR_INVALID_ARG;
+  if (n_sample_chunks == 0 || !d_samples || !aligned(d_samples, W / 8) || !aligned(d_workspace, 8))
+    return IBP_ERR_INVALID_ARG;
+  if (n_sample_chunks >= (1ull << 40)) return IBP_ERR_SIZE;
+  if (workspace_bytes < ibp_metadata_workspace_bytes(n_sample_chunks, W)) return IBP_ERR_CAPACITY;
+  if (!view(d_samples, n_sample_chunks * (W / 8)) || !view(d_workspace, ibp_metadata_workspace_bytes(n_sample_chunks, W)))
+    return IBP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  MetaArgs a;
+  a.in = d_samples;
+  a.n = n_sample_chunks;
+  a.W = W;
+  a.blocks = meta_blocks(n_sample_chunks);
+  a.partial = static_cast<uint64_t *>(d_workspace);
+  a.result = a.partial + (uint64_t)a.blocks * W;
+  // k = ceil(round(T * 10^6) * n / 10^6), exactly, in 128-bit integers
+  const uint64_t tppm = (uint64_t)(T * 1e6 + 0.5);
+  const unsigned __int128 num = (unsigned __int128)tppm * n_sample_chunks;
+  a.k = (uint64_t)((num + 999999u) / 1000000u);
+  hipError_t e = launch_meta(a, s);
+  if (e != hipSuccess) return IBP_ERR_DEVICE;
+  uint64_t host[66];
+  e = hipMemcpyAsync(host, a.result, sizeof(host), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return IBP_ERR_DEVICE;
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return IBP_ERR_DEVICE;
+  meta_out->W = W;
+  meta_out->reserved = 0;
+  meta_out->mask = host[64];
+  meta_out->bitval = host[65];
+  if (counts_out)
+    for (uint32_t b = 0; b < W; ++b) counts_out[b] = host[b];
+  return IBP_OK;
+}
+
+IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_bytes, uint32_t S,
+                         void *d_stream, uint64_t stream_capacity, uint64_t *d_offsets,
+                         void *d_workspace, uint64_t workspace_bytes, uint32_t *d_err_word,
+                         void *hip_stream) {
+  CodecParams p;
+  if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
+  if (S == 0 || S > IBP_MAX_S || !d_offsets) return IBP_ERR_INVALID_ARG;
+  const uint32_t cb = p.W / 8;
+  if (n_bytes % cb) return IBP_ERR_SIZE;
+  const uint64_t n = n_bytes / cb;
+  if (n && (!d_in || !d_stream || !d_workspace)) return IBP_ERR_INVALID_ARG;
+  if (!aligned(d_in, cb) || !aligned(d_stream, 16) || !aligned(d_offsets, 8) || !aligned(d_workspace, 8))
+    return IBP_ERR_INVALID_ARG;
+  if (!total_fits(n, p.W)) return IBP_ERR_SIZE;
+  if (stream_capacity < ibp_max_stream_bytes(n, p.W)) return IBP_ERR_CAPACITY;
+  if (workspace_bytes < ibp_compress_workspace_bytes(n, S)) return IBP_ERR_CAPACITY;
+  const uint64_t nseg = (n + S - 1) / S;
+  if (!view(d_in, n_bytes) || !view(d_stream, ibp_max_stream_bytes(n, p.W)) || !view(d_offsets, 8 * (nseg + 1)) ||
+      !view(d_workspace, n ? ibp_compress_workspace_bytes(n, S) : 0) || !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (n == 0) return status_of(launch_zero(d_offsets, 1, s));  // offset table = {0}
+  EncodeArgs a;
+  a.in = d_in;
+  a.stream = static_cast<uint32_t *>(d_stream);
+  a.off = d_offsets;
+  a.control = static_cast<uint32_t *>(d_workspace);
+  a.status = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(d_workspace) + 8);
+  a.ntiles = enc_tiles(n, S);
+  a.tails = a.status + a.ntiles;
+  a.err = d_err_word;
+  a.n_chunks = n;
+  a.nseg = nseg;
+  a.S = S;
+  a.s_log2 = log2_if_pow2(S);
+  a.G = enc_segs_per_tile(S);
+  a.tile_chunks = a.G * S;
+  a.obuf_dw = ((31 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;
+  return status_of(launch_encode(a, p, s));
+}
+
+static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                         const uint64_t *d_offsets, uint64_t nseg, uint32_t S, const int64_t *d_ids,
+                         uint64_t n_units, uint64_t n_chunks, void *d_out, uint32_t *d_err_word,
+                         void *hip_stream, bool gather) {
+  CodecParams p;
+  if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
+  if (S == 0 || S > IBP_MAX_S || !d_offsets) return IBP_ERR_INVALID_ARG;
+  const uint32_t cb = p.W / 8;
+  if (n_chunks && (!d_out || !stream_in)) return IBP_ERR_INVALID_ARG;
+  if (gather && n_units && !d_ids) return IBP_ERR_INVALID_ARG;
+  if (!aligned(stream_in, 16) || !aligned(d_out, cb) || !aligned(d_offsets, 8) || !aligned(d_ids, 8))
+    return IBP_ERR_INVALID_ARG;
+  if (!total_fits(n_chunks, p.W) || (gather && !total_fits(nseg * (uint64_t)S, p.W))) return IBP_ERR_SIZE;
+  if (n_units == 0) return IBP_OK;
+  if (!view(stream_in, stream_bytes) || !view(d_offsets, 8 * (nseg + 1)) || !view(d_ids, gather ? 8 * n_units : 0) ||
+      !view(d_out, n_chunks * cb) || !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  DecodeArgs a;
+  a.stream = static_cast<const uint8_t *>(stream_in);
+  a.stream_bytes = stream_bytes;
+  a.off = d_offsets;
+  a.ids = d_ids;
+  a.out = d_out;
+  a.err = d_err_word;
+  a.n_chunks = n_chunks;
+  a.n_units = n_units;
+  a.nseg = nseg;
+  a.S = S;
+  a.s_log2 = log2_if_pow2(S);
+  a.G = dec_units_per_tile(S);
+  const uint32_t tile_chunks = a.G * S;
+  if (gather) {
+    a.slot_dw = ((S * (p.W + 1) + 127) / 128 + 1) * 4;
+    a.stage_dw = a.G * a.slot_dw + 4;
+  } else {
+    a.slot_dw = 0;
+    a.stage_dw = 4 * ((tile_chunks * (p.W + 1) + 254) / 128) + 8;
+  }
+  uint32_t per_unit = 3 * a.G;
+  if (gather) per_unit += (a.G & 1u) + 3 * a.G;  // 8-byte aligned first-block table + block counts
+  a.wave_dw = (a.stage_dw + per_unit + 3) & ~3u;
+  return status_of(launch_decode(a, p, gather, static_cast<hipStream_t>(hip_stream)));
+}
+
+IBP_API int ibp_decompress(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                           const uint64_t *d_offsets, uint64_t n_chunks, uint32_t S, void *d_out,
+                           uint32_t *d_err_word, void *hip_stream) {
+  const uint64_t nseg = ibp_num_segments(n_chunks, S);
+  return decode_common(meta, stream_in, stream_bytes, d_offsets, nseg, S, nullptr, nseg, n_chunks, d_out,
+                       d_err_word, hip_stream, false);
+}
+
+IBP_API int ibp_decompress_gather(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                                  const uint64_t *d_offsets, uint64_t n_segments, uint32_t S,
+                                  const int64_t *d_ids, uint64_t n_ids, void *d_out,
+                                  uint32_t *d_err_word, void *hip_stream) {
+  if (S != 0 && n_ids > (1ull << 55) / S) return IBP_ERR_SIZE;
+  return decode_common(meta, stream_in, stream_bytes, d_offsets, n_segments, S, d_ids, n_ids,
+                       n_ids * (uint64_t)S, d_out, d_err_word, hip_stream, true);
+}
+
+IBP_API int ibp_gather_raw(const void *src, uint64_t row_bytes, uint64_t n_rows, const int64_t *d_ids,
+                           uint64_t n_ids, void *d_out, uint32_t *d_err_word, void *hip_stream) {
+  if (row_bytes == 0 || row_bytes % 16) return IBP_ERR_SIZE;
+  if (n_ids && (!src || !d_ids || !d_out)) return IBP_ERR_INVALID_ARG;
+  if (!aligned(src, 16) || !aligned(d_out, 16) || !aligned(d_ids, 8)) return IBP_ERR_INVALID_ARG;
+  if (n_ids == 0) return IBP_OK;
+  if (!view(src, row_bytes * n_rows) || !view(d_ids, 8 * n_ids) || !view(d_out, row_bytes * n_ids) ||
+      !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  RawGatherArgs a;
+  a.src = static_cast<const uint8_t *>(src);
+  a.ids = d_ids;
+  a.out = static_cast<uint8_t *>(d_out);
+  a.err = d_err_word;
+  a.row_blocks = row_bytes / 16;
+  a.n_rows = n_rows;
+  a.n_ids = n_ids;
+  return status_of(launch_raw_gather(a, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

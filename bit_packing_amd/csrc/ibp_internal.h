@@ -1,0 +1,115 @@
+// ibp_internal.h -- definitions shared by the host launch code and the gfx950
+// kernels of the IBP codec.  Not part of the public ABI (that is include/ibp.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ibp {
+
+constexpr uint32_t kWave = 64;          // CDNA4 wavefront width
+constexpr uint32_t kBlock = 256;        // threads per workgroup for every kernel
+constexpr uint32_t kWavesPerBlock = kBlock / kWave;
+constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-bit chunk
+
+// Compression tile: a workgroup sizes, offsets and packs about this many chunks.
+constexpr uint32_t kEncTileChunks = 1024;
+// Decompression tile: a wavefront decodes about this many chunks at a time,
+// with at most this many segments (rows) per tile.
+constexpr uint32_t kDecTileChunks = 512;
+constexpr uint32_t kDecMaxUnits = 128;
+// Metadata count kernel: at most this many workgroups write partial counts.
+constexpr uint32_t kMetaMaxBlocks = 1024;
+
+// Status words of the compression look-back: 2-bit flag above a 62-bit value.
+constexpr uint64_t kFlagAggregate = 1ull << 62;
+constexpr uint64_t kFlagPrefix = 2ull << 62;
+constexpr uint64_t kValueMask = (1ull << 62) - 1;
+constexpr uint64_t kTailReady = 1ull << 63;
+
+// The free (non-Mask) positions of a chunk split into maximal runs of
+// consecutive bits.  Run r sits at chunk bits [pos_r, pos_r + len_r) and at
+// payload bits [cum_r, cum_r + len_r), cum_r = total length of the runs below it.
+// Stored as the payload-side mask lowbits(len_r) << cum_r and the shift
+// pos_r - cum_r (never negative), so extract and deposit are one shift, one AND
+// and one OR per run.
+struct Runs {
+  uint64_t pmask[kMaxRuns];
+  uint32_t shift[kMaxRuns];
+  uint32_t n;
+};
+
+struct CodecParams {
+  uint64_t mask;
+  uint64_t bitval;
+  uint32_t W;   // 32 or 64
+  uint32_t pc;  // popcount(mask)
+  Runs runs;
+};
+
+struct MetaArgs {
+  const void *in;
+  uint64_t n;          // sample chunks
+  uint64_t *partial;   // [blocks][W] partial counts
+  uint64_t *result;    // [64 counts][mask][bitval]
+  uint64_t k;          // majority count needed for an invariant bit
+  uint32_t W;
+  uint32_t blocks;
+};
+
+struct EncodeArgs {
+  const void *in;
+  uint32_t *stream;    // dword view of the output stream
+  uint64_t *off;       // nseg + 1 bit offsets
+  uint64_t *status;    // ntiles look-back words
+  uint64_t *tails;     // ntiles hand-over words (last partial dword of a tile)
+  uint32_t *control;   // [0] tile ticket, [1] abort flag
+  uint32_t *err;       // optional
+  uint64_t n_chunks;
+  uint64_t nseg;
+  uint64_t ntiles;
+  uint32_t S;
+  uint32_t s_log2;     // log2(S) when S is a power of two, else kNotPow2
+  uint32_t G;          // segments per tile
+  uint32_t tile_chunks;
+  uint32_t obuf_dw;    // LDS dwords for the packed tile
+};
+
+struct DecodeArgs {
+  const uint8_t *stream;
+  uint64_t stream_bytes;
+  const uint64_t *off;
+  const int64_t *ids;  // gather: segment id of each output row
+  void *out;
+  uint32_t *err;       // optional
+  uint64_t n_chunks;   // chunks written in total
+  uint64_t n_units;    // contiguous: segments; gather: rows
+  uint64_t nseg;       // segments in the stream
+  uint32_t S;
+  uint32_t s_log2;
+  uint32_t G;          // units per wave tile
+  uint32_t stage_dw;   // LDS staging dwords per wave
+  uint32_t slot_dw;    // gather: staging dwords per row
+  uint32_t wave_dw;    // LDS dwords per wave in total
+};
+
+struct RawGatherArgs {
+  const uint8_t *src;
+  const int64_t *ids;
+  uint8_t *out;
+  uint32_t *err;
+  uint64_t row_blocks; // row size in 16-byte blocks
+  uint64_t n_rows;
+  uint64_t n_ids;
+};
+
+constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;
+
+// Launchers (ibp_kernels.hip).  Each returns the hipError_t of its launch(es).
+hipError_t launch_meta(const MetaArgs &a, hipStream_t s);
+hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather, hipStream_t s);
+hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s);
+hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s);
+
+}  // namespace ibp

@@ -1,0 +1,183 @@
+/*
+ * ibp.h -- C ABI of the MI355X (gfx950) Invariant Bit Packing (IBP) codec.
+ *
+ * The method is the one summarised in "Riduzione del Collo di Bottiglia della
+ * Memoria GPU con la Compressione Lossless per il ML" (gist.science, paper
+ * 2605.30728), section "Algoritmo Core":
+ *   1. Preprocessing: find the bit positions of a W-bit chunk that keep one value
+ *      over at least a fraction T of a sample batch -> Mask, and their values ->
+ *      Bitval (ibp_build_metadata);
+ *   2. Compression: a chunk whose Mask bits equal Bitval loses those bits; every
+ *      chunk carries a participation bit (ibp_compress);
+ *   3. Decompression: a wavefront stages a contiguous compressed segment in LDS,
+ *      finds each lane's bit offset with a wave-wide prefix count and re-inserts
+ *      the Bitval bits (ibp_decompress; ibp_decompress_gather for rows read
+ *      straight from pinned host memory, the "PCIe Transfer Compression" mode of
+ *      section "Integrazione del Sistema").
+ *
+ * Compressed format (shared with nothing else; every call below produces or
+ * consumes exactly this):
+ *   - chunk i is the little-endian word at bytes [i*W/8, (i+1)*W/8) of the input;
+ *   - chunks are grouped into segments of S consecutive chunks (the last segment
+ *     may be shorter);
+ *   - a segment of m chunks is: m participation bits (1 = compressed), in chunk
+ *     order, then the m payloads back to back in chunk order; a compressed
+ *     chunk's payload is its W - popcount(Mask) non-Mask bits in increasing
+ *     position order, a raw chunk's payload is all W bits;
+ *   - stream bit q is bit (q % 8) of byte q / 8; fields are written low bit first;
+ *   - segments are bit-contiguous (no padding); segment k starts at bit
+ *     offsets[k]; offsets[nseg] is the total bit count; bits of the last byte
+ *     above the total are 0.
+ *   So the total is the sum over chunks of 1 + (compressed ? W - popcount(Mask) : W).
+ *
+ * Conventions for every call:
+ *   - "d_" pointers are device memory (hipMalloc / torch CUDA tensors).  Stream
+ *     inputs of the decoders may instead point to pinned host memory allocated
+ *     with hipHostMalloc (read zero-copy over PCIe by the kernel).
+ *   - hip_stream is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns, except ibp_build_metadata, which waits for
+ *     its stream.
+ *   - The caller allocates and frees every buffer; the library allocates no
+ *     memory.  Workspaces are caller-provided, sized by the *_workspace_bytes
+ *     queries; their contents on entry do not matter.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns an error code and enqueues nothing.  Calls never throw.
+ *   - d_err_word (optional, may be NULL): a device uint32 that kernels OR error
+ *     bits into (IBP_DEVERR_*).  The library never clears it.
+ *   - All calls are stateless and may run concurrently on different streams.
+ */
+#ifndef IBP_H
+#define IBP_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define IBP_API __attribute__((visibility("default")))
+#else
+#define IBP_API
+#endif
+
+typedef enum {
+  IBP_OK = 0,
+  IBP_ERR_INVALID_ARG = 1, /* NULL pointer; W not 32 or 64; S == 0 or S > IBP_MAX_S;
+                              T not in (0.5, 1]; misaligned pointer; Bitval outside Mask */
+  IBP_ERR_SIZE = 2,        /* byte count not a whole number of chunks; too many chunks */
+  IBP_ERR_CAPACITY = 3,    /* stream capacity or workspace below the required size */
+  IBP_ERR_DEVICE = 4       /* a HIP runtime call failed (kernel launch, copy, sync) */
+} ibp_status_t;
+
+/* Bits OR-ed into *d_err_word by the kernels. */
+#define IBP_DEVERR_CORRUPT 1u   /* a segment's decoded length differs from its offset span,
+                                   or its offsets are not monotone / exceed the stream */
+#define IBP_DEVERR_BAD_ID 2u    /* a gather id is negative or >= n_segments; its row is skipped */
+#define IBP_DEVERR_TIMEOUT 4u   /* compression: a wait on a neighbouring tile timed out */
+
+/* Largest segment length (chunks per segment). */
+#define IBP_MAX_S 1024u
+
+/* Invariant-bit metadata of one dataset ("Algoritmo Core", step 1).  Only the low
+ * W bits of mask and bitval are used; bitval must be 0 outside mask. */
+typedef struct {
+  uint32_t W;        /* chunk width in bits: 32 or 64 */
+  uint32_t reserved; /* must be 0 */
+  uint64_t mask;     /* 1 = invariant position */
+  uint64_t bitval;   /* value of each invariant position, 0 elsewhere */
+} ibp_meta_t;
+
+/* Human-readable name of a status code (static string). */
+IBP_API const char *ibp_status_str(int status);
+
+/* ceil(n_chunks / S); 0 when S == 0. */
+IBP_API uint64_t ibp_num_segments(uint64_t n_chunks, uint32_t S);
+
+/* Capacity a compressed stream of n_chunks W-bit chunks may need: the worst case
+ * (every chunk raw, n*(W+1) bits) in bytes, rounded up to 16.  ibp_compress
+ * requires stream_capacity >= this. */
+IBP_API uint64_t ibp_max_stream_bytes(uint64_t n_chunks, uint32_t W);
+
+/* Bytes of a stream of total_bits bits that the decoders may read:
+ * ceil(total_bits / 8) rounded up to 16.  Pass at least the true length of the
+ * buffer as stream_bytes; the kernels read nothing beyond stream_bytes. */
+IBP_API uint64_t ibp_stream_bytes(uint64_t total_bits);
+
+/* Workspace for ibp_build_metadata and ibp_compress. */
+IBP_API uint64_t ibp_metadata_workspace_bytes(uint64_t n_sample_chunks, uint32_t W);
+IBP_API uint64_t ibp_compress_workspace_bytes(uint64_t n_chunks, uint32_t S);
+
+/*
+ * Step 1 -- metadata ("Algoritmo Core", Preprocessing).
+ *   d_samples: n_sample_chunks contiguous W-bit chunks (device, aligned to W/8).
+ *   Position b is invariant when its majority value occurs in at least
+ *   k = ceil(round(T * 10^6) * n / 10^6) samples; 0.5 < T <= 1.
+ *   meta_out (host): W, mask, bitval.  counts_out (host, optional): W uint64, the
+ *   number of samples with bit b set.
+ *   Waits for hip_stream (the result is copied back to the host).
+ */
+IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, uint32_t W, double T,
+                               ibp_meta_t *meta_out, uint64_t *counts_out, void *d_workspace,
+                               uint64_t workspace_bytes, void *hip_stream);
+
+/*
+ * Step 2 -- compression ("Algoritmo Core", Compressione).  One fused pass: each
+ * tile of segments sizes itself, takes its bit offset from its predecessors by a
+ * decoupled look-back, and packs.
+ *   meta (host): as returned by ibp_build_metadata (or any valid Mask/Bitval).
+ *   d_in: n_bytes of input (device, aligned to W/8); n_bytes % (W/8) == 0.
+ *   S: chunks per segment, 1..IBP_MAX_S.
+ *   d_stream: output, stream_capacity >= ibp_max_stream_bytes(n, W) bytes,
+ *     aligned to 16.  Bytes past ceil(total/8) rounded up to 4 are not written.
+ *   d_offsets: output, nseg + 1 uint64 bit offsets (device).
+ *   d_workspace: ibp_compress_workspace_bytes(n, S) bytes (device).
+ *   The total size is d_offsets[nseg] bits; copy it back when needed.
+ */
+IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_bytes, uint32_t S,
+                         void *d_stream, uint64_t stream_capacity, uint64_t *d_offsets,
+                         void *d_workspace, uint64_t workspace_bytes, uint32_t *d_err_word,
+                         void *hip_stream);
+
+/*
+ * Step 3 -- decompression, device-resident ("Algoritmo Core", Decompressione).
+ *   stream_in: compressed stream (device, or pinned host memory), aligned to 16,
+ *     readable for stream_bytes bytes.
+ *   d_offsets: nseg + 1 bit offsets (device), nseg = ceil(n_chunks / S).
+ *   d_out: n_chunks * W/8 bytes (device, aligned to W/8).
+ *   A segment whose offsets are inconsistent is not decoded and sets
+ *   IBP_DEVERR_CORRUPT; no read goes outside [stream_in, stream_in + stream_bytes).
+ */
+IBP_API int ibp_decompress(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                           const uint64_t *d_offsets, uint64_t n_chunks, uint32_t S, void *d_out,
+                           uint32_t *d_err_word, void *hip_stream);
+
+/*
+ * Step 3 on a gather ("Integrazione del Sistema", PCIe Transfer Compression):
+ * row j of d_out (S chunks) = segment d_ids[j] of a stream of n_segments full
+ * segments of S chunks.  stream_in is normally pinned host memory, read by the
+ * kernel over PCIe without a staging copy; device memory works too.
+ *   d_ids: n_ids int64 segment ids (device).  Duplicates are decoded again.
+ *   d_out: n_ids * S * W/8 bytes (device).  A row whose id is out of range is
+ *   left untouched and sets IBP_DEVERR_BAD_ID.
+ */
+IBP_API int ibp_decompress_gather(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                                  const uint64_t *d_offsets, uint64_t n_segments, uint32_t S,
+                                  const int64_t *d_ids, uint64_t n_ids, void *d_out,
+                                  uint32_t *d_err_word, void *hip_stream);
+
+/*
+ * Baseline for the measurements, not part of the codec: the uncompressed
+ * transfer that IBP replaces (the page's "Risultati" compare against it).
+ * Row j of d_out = row d_ids[j] of a table of n_rows rows of row_bytes bytes at
+ * src (pinned host memory or device memory, aligned to 16); row_bytes % 16 == 0.
+ * Out-of-range ids leave the row untouched and set IBP_DEVERR_BAD_ID.
+ */
+IBP_API int ibp_gather_raw(const void *src, uint64_t row_bytes, uint64_t n_rows, const int64_t *d_ids,
+                           uint64_t n_ids, void *d_out, uint32_t *d_err_word, void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IBP_H */

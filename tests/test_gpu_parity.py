@@ -1,0 +1,217 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, bit-exact.
+
+Tolerance is 0 everywhere: the codec is lossless, so counts, Mask, Bitval, the
+offset table, every stream byte below ceil(total/8) and the round trip must
+agree exactly.  Sizes span several compression tiles (1024 chunks) and
+decompression tiles (512 chunks per wavefront) plus ragged tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DT = {32: np.uint32, 64: np.uint64}
+
+
+@pytest.fixture(scope="module")
+def ibp():
+    import bit_packing_amd
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bit_packing_amd.load_library()
+    return bit_packing_amd
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _data(rng, n, W, mask, bitval, p_match):
+    """n W-bit chunks: random free bits; invariant bits equal Bitval with probability p_match."""
+    if W == 32:
+        v = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
+    else:
+        v = rng.integers(0, 1 << 63, size=n, dtype=np.uint64) * np.uint64(2) + \
+            rng.integers(0, 2, size=n, dtype=np.uint64)
+    t = DT[W]
+    keep = rng.random(n) < p_match
+    v[keep] = (v[keep] & t(~mask & ((1 << W) - 1))) | t(bitval)
+    return v
+
+
+def _masks(rng, W):
+    full = (1 << W) - 1
+    exp = 0x78000000 if W == 32 else 0x7C007C007C007C00
+    m = int(rng.integers(0, 1 << 62)) & full
+    return [
+        ("zero", 0, 0),
+        ("full", full, int(rng.integers(0, 1 << 62)) & full),
+        ("exponent", exp, exp & 0x3838383838383838),
+        ("random", m, int(rng.integers(0, 1 << 62)) & m),
+    ]
+
+
+def _run_case(ibp, dev, v, W, S, mask, bitval, tag):
+    n = v.size
+    say(f"case {tag}: W={W} S={S} n={n} mask={mask:#x}")
+    meta = ibp.make_meta(W, mask, bitval)
+    x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    comp = ibp.ibp_compress(meta, x, S, err=err)
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    off = comp.offsets.cpu().numpy().view(np.uint64)
+    assert np.array_equal(off, ref_off), f"{tag}: offsets differ"
+    nb = (int(ref_off[-1]) + 7) // 8
+    got = comp.stream[:nb].cpu().numpy()
+    if not np.array_equal(got, ref_stream):
+        bad = int(np.nonzero(got != ref_stream)[0][0])
+        raise AssertionError(f"{tag}: stream differs first at byte {bad} of {nb}")
+    # decode the GPU stream
+    out = ibp.ibp_decompress(meta, comp.stream, comp.offsets, n, S, err=err)
+    assert torch.equal(out, x), f"{tag}: round trip differs"
+    # decode the oracle stream from an exactly sized buffer (tail block read byte-wise)
+    if nb:
+        s2 = torch.from_numpy(ref_stream.copy()).to(dev)
+        out2 = ibp.ibp_decompress(meta, s2, torch.from_numpy(ref_off.view(np.int64)).to(dev), n, S, err=err)
+        assert torch.equal(out2, x), f"{tag}: decode of the oracle stream differs"
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0, f"{tag}: device error word {int(err.item())}"
+
+
+@pytest.mark.parametrize("W", [32, 64])
+@pytest.mark.parametrize("S", [1, 3, 32, 100, 128, 256, 1000, 1024])
+def test_compress_decompress_parity(ibp, W, S):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(W * 10007 + S)
+    sizes = sorted({0, 1, 63, 64, 65, max(S - 1, 1), S, S + 1, 3 * S + 7, 5000, 70_001})
+    for name, mask, bitval in _masks(rng, W):
+        for n in sizes:
+            p = 0.9 if name != "zero" else 1.0
+            _run_case(ibp, dev, _data(rng, n, W, mask, bitval, p), W, S, mask, bitval, f"{name}-{n}")
+
+
+@pytest.mark.parametrize("W", [32, 64])
+def test_all_invariant_and_raw_streams(ibp, W):
+    """Minimum size (all chunks equal Bitval on a full Mask) and +1 bit per chunk (Mask = 0)."""
+    dev = torch.device("cuda:0")
+    full = (1 << W) - 1
+    v = np.zeros(40_000, DT[W])
+    _run_case(ibp, dev, v, W, 256, full, 0, "all-invariant")
+    rng = np.random.default_rng(9)
+    _run_case(ibp, dev, _data(rng, 40_000, W, 0, 0, 0.0), W, 256, 0, 0, "raw")
+
+
+@pytest.mark.parametrize("W", [32, 64])
+@pytest.mark.parametrize("T", [0.51, 0.9, 0.99, 1.0])
+def test_metadata_parity(ibp, W, T):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(int(T * 1000) + W)
+    for n in (1, 2, 255, 4096, 100_003, 1_500_000):
+        base = _data(rng, n, W, 0, 0, 0.0)
+        # bias the bits so that several positions sit near the threshold
+        bias = DT[W](rng.integers(0, 1 << 31)) if W == 32 else DT[W](rng.integers(0, 1 << 62))
+        v = np.where(rng.random(n) < T, base & bias, base)
+        say(f"metadata W={W} T={T} n={n}")
+        meta, counts = ibp.ibp_build_metadata(torch.from_numpy(v.view(np.uint8).copy()).to(dev), W, T)
+        mask, bitval, c1 = oracle.build_meta(v, W, T)
+        assert counts == c1.tolist()
+        assert (meta.mask, meta.bitval, meta.W) == (mask, bitval, W)
+
+
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (64, 1), (32, 1000)])
+@pytest.mark.parametrize("where", ["device", "pinned"])
+def test_gather_parity(ibp, W, S, where):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(S + W)
+    nseg = 3000
+    mask = 0xC0000000 if W == 32 else 0x7800000078000000
+    bitval = 0 if W == 32 else 0x3800000038000000
+    v = _data(rng, nseg * S, W, mask, bitval, 0.95)
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    meta = ibp.make_meta(W, mask, bitval)
+    if where == "device":
+        src = torch.from_numpy(ref_stream.copy()).to(dev)
+    else:
+        src = torch.empty(ref_stream.size, dtype=torch.uint8, pin_memory=True)
+        src.copy_(torch.from_numpy(ref_stream))
+    off = torch.from_numpy(ref_off.view(np.int64)).to(dev)
+    ids_np = rng.integers(0, nseg, size=4099).astype(np.int64)
+    ids_np[:3] = [0, nseg - 1, 0]  # first, last, duplicate
+    ids = torch.from_numpy(ids_np).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    say(f"gather W={W} S={S} from {where}")
+    rows = ibp.ibp_decompress_gather(meta, src, off, S, ids, err=err)
+    ref = oracle.decode_gather(ref_stream, ref_off, S, ids_np, W, mask, bitval, np.uint8)
+    assert np.array_equal(rows.cpu().numpy(), ref)
+    assert np.array_equal(ref.view(DT[W]).reshape(len(ids_np), S), v.reshape(nseg, S)[ids_np])
+    assert int(err.item()) == 0
+
+
+def test_raw_gather(ibp):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(1)
+    table = rng.integers(0, 255, size=(1000, 512), dtype=np.uint8)
+    src = torch.empty(table.size, dtype=torch.uint8, pin_memory=True)
+    src.copy_(torch.from_numpy(table.reshape(-1)))
+    ids_np = rng.integers(0, 1000, size=777).astype(np.int64)
+    say("raw gather from pinned memory")
+    out = ibp.ibp_gather_raw(src, 512, torch.from_numpy(ids_np).to(dev))
+    assert np.array_equal(out.cpu().numpy().reshape(777, 512), table[ids_np])
+
+
+def test_device_error_reporting(ibp):
+    """Corrupt offsets and bad ids are reported in the error word; nothing is read
+    outside the stream and rows with bad ids are left untouched."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(2)
+    W, S, mask, bitval = 32, 128, 0xC0000000, 0
+    v = _data(rng, 100 * S, W, mask, bitval, 0.9)
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    meta = ibp.make_meta(W, mask, bitval)
+    stream = torch.from_numpy(ref_stream.copy()).to(dev)
+    say("error paths: corrupt offset")
+    bad_off = ref_off.copy().view(np.int64)
+    bad_off[7] += 3
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ibp.ibp_decompress(meta, stream, torch.from_numpy(bad_off).to(dev), v.size, S, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & ibp.IBP_DEVERR_CORRUPT
+    say("error paths: offset past the stream end")
+    bad_off = ref_off.copy().view(np.int64)
+    bad_off[-1] = (ref_stream.size + 64) * 8
+    err.zero_()
+    ibp.ibp_decompress(meta, stream, torch.from_numpy(bad_off).to(dev), v.size, S, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & ibp.IBP_DEVERR_CORRUPT
+    say("error paths: bad gather ids")
+    err.zero_()
+    ids = torch.tensor([5, -1, 100, 99], dtype=torch.int64, device=dev)
+    out = torch.full((4 * S * 4,), 0xAB, dtype=torch.uint8, device=dev)
+    ibp.ibp_decompress_gather(meta, stream, torch.from_numpy(ref_off.view(np.int64)).to(dev), S, ids, out=out,
+                              err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & ibp.IBP_DEVERR_BAD_ID
+    o = out.cpu().numpy().reshape(4, -1)
+    assert (o[1] == 0xAB).all() and (o[2] == 0xAB).all()
+    assert np.array_equal(o[0].view(np.uint32), v.reshape(100, S)[5])
+    assert np.array_equal(o[3].view(np.uint32), v.reshape(100, S)[99])
+
+
+def test_host_argument_checks(ibp):
+    """Pointers the kernels cannot reach are refused before any launch."""
+    dev = torch.device("cuda:0")
+    meta = ibp.make_meta(32, 0xC0000000, 0)
+    pageable = torch.zeros(4096, dtype=torch.uint8)  # ordinary host memory
+    off = torch.zeros(2, dtype=torch.int64, device=dev)
+    with pytest.raises(ibp.IBPError) as e:
+        ibp.ibp_decompress(meta, pageable, off, 128, 128)
+    assert e.value.status == ibp.IBP_ERR_INVALID_ARG
+    stream = torch.zeros(4096, dtype=torch.uint8, device=dev)
+    lib = ibp.load_library()
+    # a stream length far beyond the allocation
+    rc = lib.ibp_decompress(ibp.ctypes.byref(meta), stream.data_ptr(), 1 << 40, off.data_ptr(), 128, 128,
+                            torch.empty(512, dtype=torch.uint8, device=dev).data_ptr(), None, None)
+    assert rc == ibp.IBP_ERR_INVALID_ARG
