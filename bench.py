@@ -1,0 +1,342 @@
+"""Benchmark of the IBP codec on one MI355X; prints one JSON line.
+
+A step is one pass of the hot path over one batch of the workload:
+
+* gnn (default) and dlrm: a gather of 65,536 uniform (gnn) or 32,768 Zipf(1.05)
+  (dlrm) row ids, each row one compressed segment, decoded into HBM.  ``value``
+  is measured with the compressed table resident in HBM; the same gathers read
+  zero-copy from pinned host memory over PCIe are measured in the same run and
+  reported under ``pcie_sourced``, beside the measured PCIe ceilings and the
+  uncompressed zero-copy gather they replace.
+* tiny, llm, ids: a device-resident decompression of the whole tensor.
+
+Metadata (step 1) and compression (step 2) run first on the same data and are
+timed and reported too, and the decoded output is compared against the input.
+``cpu_baseline`` is the CPU oracle (one thread) on a bounded sample of the same
+work.  ``roofline`` is for the kernel of the timed step: its algorithmic bytes
+per launch over its mean launch time (HIP events on its stream).  ``traffic``
+comes from the committed rocprofv3 counter summary of that kernel, and is null
+when the kernel source has changed since the counters were taken.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "IBP decompress effective GB/s (HBM- and PCIe-sourced) + compression ratio"
+HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD published
+PCIE_PEAK_GBPS = 64.0      # PCIe 5.0 x16, one direction, published link rate
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in ("ibp_kernels.hip", "ibp_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from profiles/<kernel>_<workload>_traffic.txt, if that summary
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+class Timer:
+    """Per-launch HIP event pairs on the launching (current) stream, plus wall time."""
+
+    def __init__(self, torch, n):
+        self.torch = torch
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def run(self, fn, n):
+        torch = self.torch
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            a, b = self.ev[i]
+            a.record()
+            fn(i)
+            b.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        kern = [a.elapsed_time(b) for a, b in self.ev[:n]]
+        return wall, sum(kern) / len(kern)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gnn", choices=["gnn", "dlrm", "tiny", "llm", "ids"])
+    ap.add_argument("--scale", type=float, default=1.0, help="shrink the workload (testing only)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the IBP hot path has no "
+              "cross-GPU step; the sharding plan is described in the design notes.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import bit_packing_amd as ibp
+    import workloads
+
+    ibp.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    inst = workloads.generate(args.workload, args.scale)
+    W, T, S = w.W, w.T, w.S
+    n_chunks = inst.n_chunks
+    U = inst.data.nbytes
+    gather = w.gather > 0
+    extra = {}
+
+    x = torch.from_numpy(inst.data.reshape(-1).view(np.uint8)).to(dev)
+    sample = torch.from_numpy(inst.sample.reshape(-1).view(np.uint8)).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    timer = Timer(torch, max(args.steps, 20) + args.warmup)
+
+    # ---- step 1: metadata (synchronous by definition; wall time)
+    meta, _ = ibp.ibp_build_metadata(sample, W, T)
+    t0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        meta, _ = ibp.ibp_build_metadata(sample, W, T)
+    extra["metadata"] = {"ms": (time.perf_counter() - t0) / reps * 1e3, "sample_chunks": int(inst.sample.nbytes * 8 // W),
+                         "mask": hex(meta.mask), "bitval": hex(meta.bitval)}
+
+    # ---- step 2: compression, HBM -> HBM
+    cap = ibp.ibp_max_stream_bytes(n_chunks, W)
+    stream_d = torch.empty(cap, dtype=torch.uint8, device=dev)
+    nseg = ibp.ibp_num_segments(n_chunks, S)
+    off_d = torch.empty(nseg + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(ibp.ibp_compress_workspace_bytes(n_chunks, S), dtype=torch.uint8, device=dev)
+
+    def compress(_i):
+        ibp.ibp_compress(meta, x, S, err=err, out_stream=stream_d, out_offsets=off_d, workspace=ws)
+
+    compress(0)
+    creps = 10 if U > (64 << 20) else 20
+    _, c_ms = timer.run(compress, creps)
+    total_bits = int(off_d[-1].item())
+    C = (total_bits + 7) // 8
+    r_stream = U / C
+    r_total = U / (C + 8 * (nseg + 1) + 24)
+    extra["compress"] = {"kernel_ms": c_ms, "effective_GBps": U / c_ms / 1e6,
+                         "algorithmic_GBps": (U + C + 8 * (nseg + 1)) / c_ms / 1e6}
+    extra["ratio"] = {"r_stream": r_stream, "r_total": r_total, "stream_bytes": C, "input_bytes": U,
+                      "segments": nseg, "S": S}
+    stream_bytes = ibp.ibp_stream_bytes(total_bits)
+    stream_d = stream_d[:stream_bytes]
+
+    # ---- step 3: device-resident decompression of the whole tensor
+    out_full = torch.empty_like(x)
+
+    def decompress(_i):
+        ibp.ibp_decompress(meta, stream_d, off_d, n_chunks, S, out=out_full, err=err)
+
+    decompress(0)
+    dreps = 10 if U > (64 << 20) else 20
+    _, d_ms = timer.run(decompress, dreps)
+    d_alg = C + 8 * (nseg + 1) + U
+    extra["decompress_device"] = {"kernel_ms": d_ms, "effective_GBps": U / d_ms / 1e6,
+                                  "algorithmic_GBps": d_alg / d_ms / 1e6,
+                                  "hbm_fraction": d_alg / d_ms / 1e6 / HBM_PEAK_GBPS}
+    torch.cuda.synchronize()
+    roundtrip_ok = bool(torch.equal(out_full, x))
+    del out_full
+
+    off_h = off_d.cpu().numpy().view(np.uint64)
+    if gather:
+        n_rows = inst.data.shape[0]
+        row_bytes = inst.row_bytes
+        ids_all = workloads.gather_ids(args.workload, n_rows, args.warmup + args.steps)
+        ids_d = torch.from_numpy(ids_all).to(dev)
+        m = ids_all.shape[1]
+        out_rows = torch.empty(m * row_bytes, dtype=torch.uint8, device=dev)
+        spans = (off_h[1:] - off_h[:-1])
+        # algorithmic bytes per gather: the rows' compressed spans, two offsets and an id per row, the output
+        alg_hbm = [int(((spans[ids] + 7) // 8).sum()) + 24 * m + m * row_bytes for ids in ids_all]
+        pcie_bytes = [int(((spans[ids] + 7) // 8).sum()) for ids in ids_all]
+
+        def gather_from(src):
+            def fn(i):
+                ibp.ibp_decompress_gather(meta, src, off_d, S, ids_d[i], out=out_rows, err=err)
+            return fn
+
+        # timed step: gather from the HBM-resident compressed table
+        step = gather_from(stream_d)
+        for i in range(args.warmup):
+            step(i)
+        wall, k_ms = timer.run(lambda i: step(args.warmup + i), args.steps)
+        last = ids_all[-1]
+        ref_rows = torch.from_numpy(inst.data.reshape(n_rows, -1)[last].reshape(-1).view(np.uint8).copy()).to(dev)
+        gather_ok = bool(torch.equal(out_rows, ref_rows))
+        step_bytes = m * row_bytes
+        value = step_bytes * args.steps / wall / 1e9
+        ms_per_step = wall / args.steps * 1e3
+        achieved = (sum(alg_hbm[args.warmup:]) / args.steps) / k_ms / 1e6
+        kernel_name, kernel_label = "decode_kernel_gather", "ibp_decompress_gather (HBM-resident table)"
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(kernel_name, args.workload),
+                    "kernel": kernel_label, "kernel_ms": k_ms,
+                    "algorithmic_bytes_per_launch": sum(alg_hbm[args.warmup:]) / args.steps}
+
+        # the same gathers with the compressed table in pinned host memory (zero-copy PCIe)
+        host_stream = torch.empty(stream_bytes, dtype=torch.uint8, pin_memory=True)
+        host_stream.copy_(stream_d)
+        hstep = gather_from(host_stream)
+        for i in range(args.warmup):
+            hstep(i)
+        h_wall, h_ms = timer.run(lambda i: hstep(args.warmup + i), args.steps)
+        h_ok = bool(torch.equal(out_rows, ref_rows))
+        # PCIe ceilings measured in this run: hipMemcpyAsync H2D, and a zero-copy streaming read
+        probe = torch.empty(256 << 20, dtype=torch.uint8, pin_memory=True)
+        probe_d = torch.empty_like(probe, device=dev)
+        _, cp_ms = timer.run(lambda i: probe_d.copy_(probe, non_blocking=True), 5)
+        seq = torch.arange((256 << 20) // 4096, dtype=torch.int64, device=dev)
+        _, zc_ms = timer.run(lambda i: ibp.ibp_gather_raw(probe, 4096, seq, out=probe_d), 5)
+        pcie_meas = max(probe.numel() / cp_ms / 1e6, probe.numel() / zc_ms / 1e6)
+        # uncompressed zero-copy gather of the same rows (the transfer IBP replaces)
+        raw_host = torch.empty(U, dtype=torch.uint8, pin_memory=True)
+        raw_host.copy_(torch.from_numpy(inst.data.reshape(-1).view(np.uint8)))
+        _, raw_ms = timer.run(lambda i: ibp.ibp_gather_raw(raw_host, row_bytes, ids_d[args.warmup + i],
+                                                           out=out_rows), args.steps)
+        del probe, probe_d, raw_host
+        pb = sum(pcie_bytes[args.warmup:]) / args.steps
+        extra["pcie_sourced"] = {
+            "effective_GBps": step_bytes / h_ms / 1e6, "kernel_ms": h_ms, "wall_ms_per_step": h_wall / args.steps * 1e3,
+            "pcie_read_GBps_algorithmic": pb / h_ms / 1e6,
+            "pcie_measured_GBps": pcie_meas, "memcpy_h2d_GBps": (256 << 20) / cp_ms / 1e6,
+            "zero_copy_stream_GBps": (256 << 20) / zc_ms / 1e6,
+            "fraction_of_measured_pcie": step_bytes / h_ms / 1e6 / pcie_meas,
+            "uncompressed_zero_copy_gather_GBps": step_bytes / raw_ms / 1e6,
+            "speedup_vs_uncompressed": raw_ms / h_ms,
+            "roofline": {"bound": "pcie", "achieved": pb / h_ms / 1e6, "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                         "frac": pb / h_ms / 1e6 / PCIE_PEAK_GBPS},
+            "parity_ok": h_ok}
+        del host_stream
+        checks = {"roundtrip_equal": roundtrip_ok, "gather_equal": gather_ok}
+        config = {"workload": f"{args.workload}: {w.description}", "rows": n_rows, "row_bytes": row_bytes,
+                  "W": W, "T": T, "S": S, "ids_per_step": m,
+                  "ids": "uniform" if args.workload == "gnn" else "Zipf(1.05)",
+                  "source": "compressed table resident in HBM"}
+        cpu_work = ("gather", ids_all[args.warmup:].reshape(-1), row_bytes)
+    else:
+        out_full = torch.empty_like(x)
+
+        def step(i):
+            ibp.ibp_decompress(meta, stream_d, off_d, n_chunks, S, out=out_full, err=err)
+
+        for i in range(args.warmup):
+            step(i)
+        wall, k_ms = timer.run(step, args.steps)
+        value = U * args.steps / wall / 1e9
+        ms_per_step = wall / args.steps * 1e3
+        achieved = d_alg / k_ms / 1e6
+        kernel_name = "decode_kernel"
+        roofline = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": committed_traffic(kernel_name, args.workload),
+                    "kernel": "ibp_decompress", "kernel_ms": k_ms, "algorithmic_bytes_per_launch": d_alg}
+        torch.cuda.synchronize()
+        checks = {"roundtrip_equal": bool(torch.equal(out_full, x)) and roundtrip_ok}
+        config = {"workload": f"{args.workload}: {w.description}", "elements": int(inst.data.size),
+                  "W": W, "T": T, "S": S, "source": "compressed stream resident in HBM"}
+        cpu_work = ("decode", None, None)
+    torch.cuda.synchronize()
+    errword = int(err.item())
+
+    # a plain device copy of known size: its counter readings calibrate FETCH_SIZE / WRITE_SIZE
+    cal = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+    del cal, cal2
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inst, meta, stream_d, off_h, S, cpu_work, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": f"u{W}", "data": "synthetic (seeded SplitMix64 generators)",
+        "config": config, "compression_ratio": r_stream, "roofline": roofline, "cpu_baseline": cpu,
+        "checks": {**checks, "device_error_word": errword}, "extra": extra,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(res), flush=True)
+    return 0 if all(checks.values()) and errword == 0 else 1
+
+
+def cpu_baseline(inst, meta, stream_d, off_h, S, work, budget_s):
+    """The oracle, one thread, on a bounded sample of the same work."""
+    import numpy as np
+
+    import oracle
+
+    stream_h = stream_d.cpu().numpy()
+    W = inst.w.W
+    kind, ids, row_bytes = work
+    t0 = time.perf_counter()
+    done = 0
+    if kind == "gather":
+        for start in range(0, len(ids), 1024):
+            oracle.decode_gather(stream_h, off_h, S, ids[start:start + 1024], W, meta.mask, meta.bitval, np.uint8)
+            done += min(1024, len(ids) - start)
+            if time.perf_counter() - t0 > budget_s:
+                break
+        el = time.perf_counter() - t0
+        nbytes = done * row_bytes
+        sample = f"oracle gather of the first {done} row ids of the timed steps ({nbytes} bytes out)"
+    else:
+        nseg = len(off_h) - 1
+        seg_bytes = S * W // 8
+        k = 0
+        while k < nseg and time.perf_counter() - t0 < budget_s:
+            kk = min(nseg, k + 256)
+            last_chunks = min(kk * S, inst.n_chunks) - k * S
+            sub_off = (off_h[k:kk + 1] - off_h[k]).astype(np.uint64)
+            b0 = int(off_h[k]) // 8
+            shift = int(off_h[k]) % 8
+            # re-base the segment range to a byte boundary for the oracle
+            seg = np.unpackbits(stream_h[b0:(int(off_h[kk]) + 7) // 8 + 1], bitorder="little")[shift:]
+            sub_stream = np.packbits(seg, bitorder="little")
+            oracle.decode(sub_stream, sub_off, last_chunks, W, meta.mask, meta.bitval, S, np.uint8)
+            done += last_chunks
+            k = kk
+        el = time.perf_counter() - t0
+        nbytes = done * W // 8
+        sample = f"oracle decode of the first {k} segments ({nbytes} bytes out)"
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle", "sample": sample,
+            "seconds": el}
+
+
+if __name__ == "__main__":
+    sys.exit(main())
