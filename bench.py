@@ -33,7 +33,8 @@ sys.path.insert(0, ROOT)
 METRIC = "IBP decompress effective GB/s (HBM- and PCIe-sourced) + compression ratio"
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD published
 PCIE_PEAK_GBPS = 64.0      # PCIe 5.0 x16, one direction, published link rate
-KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in ("ibp_kernels.hip", "ibp_internal.h")]
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in
+                  ("ibp_device.h", "ibp_internal.h", "ibp_meta.hip", "ibp_encode.hip", "ibp_decode.hip")]
 
 
 def kernel_source_hash() -> str:

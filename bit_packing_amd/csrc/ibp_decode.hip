@@ -1,0 +1,357 @@
+// ibp_decode.hip -- step 3 of the IBP codec on gfx950: decompression of a
+// contiguous stream held in HBM, and of a gather of rows read straight from
+// pinned host memory ("Riduzione del Collo di Bottiglia della Memoria GPU con la
+// Compressione Lossless per il ML", section "Algoritmo Core", Decompressione, and
+// section "Integrazione del Sistema", PCIe Transfer Compression).
+//
+// Each wavefront decodes one tile of G units (segments for the contiguous decode,
+// rows for the gather):
+//  a. read the units' bit ranges from the offset table and check them, so that
+//     no read leaves the stream and no LDS write leaves the tile's staging area;
+//  b. stage the compressed bits in LDS with 16-byte loads, all issued before any
+//     LDS write (the contiguous tile is one range; a gather stages each row in
+//     its own slot);
+//  c. per pass of 64 chunks, find each lane's payload offset from the
+//     participation bits: every chunk before it in its segment costs W bits,
+//     minus popcount(Mask) for each compressed one, so the offset is a prefix
+//     count of the participation bits (v_mbcnt over a 64-bit mask); read the
+//     payload from LDS, deposit it into the free positions and OR in Bitval, or
+//     take it raw; store 64 consecutive chunks.
+// The prefix count has three forms, chosen by the host from S:
+//  - S a multiple of 64: a pass lies inside one segment, whose 64 participation
+//    bits are one broadcast 64-bit LDS read;
+//  - S dividing 64: a pass holds 64/S whole segments; a ballot of the
+//    participation bits, masked to the lane's segment;
+//  - any other S: a ballot plus a per-segment carry kept in LDS.
+#include "ibp_device.h"
+
+namespace ibp {
+namespace {
+
+using namespace dev;
+
+constexpr uint32_t kBad = 0xFFFFFFFFu;
+
+enum : uint32_t {
+  kModeGeneral = 0,  // any S
+  kModeSmallS = 1,   // 64 % S == 0: each pass holds 64/S whole segments
+  kModeLargeS = 2,   // S % 64 == 0: each pass lies inside one segment
+};
+
+// Stage the 16-byte blocks [blk0, blk0 + nb) of src into LDS at dst.  Whole
+// blocks are loaded four per lane before any is written (up to 256 loads in
+// flight per wavefront); the block holding the end of a source whose length is
+// not a multiple of 16 is read byte by byte afterwards.
+__device__ __forceinline__ void stage_range(const uint8_t *src, uint64_t nbytes, uint64_t blk0, uint32_t nb,
+                                            uint32_t *dst, uint32_t lane) {
+  const uint64_t whole = nbytes >> 4;
+  const uint32_t nf = blk0 >= whole ? 0u : (uint32_t)min((uint64_t)nb, whole - blk0);
+  for (uint32_t j0 = 0; j0 < nf; j0 += 4 * kWave) {
+    uint4 t[4];
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const uint32_t j = j0 + u * kWave + lane;
+      if (j < nf) t[u] = load16(src, blk0 + j);
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const uint32_t j = j0 + u * kWave + lane;
+      if (j < nf) *reinterpret_cast<uint4 *>(dst + 4 * j) = t[u];
+    }
+  }
+  for (uint32_t j = nf + lane; j < nb; j += kWave)
+    *reinterpret_cast<uint4 *>(dst + 4 * j) = load16_tail(src, nbytes, blk0 + j);
+}
+
+// S a multiple of 64: the segments of the tile one after another, 64 chunks per pass.
+template <typename T, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
+                                                   const uint32_t *lbeg, const uint32_t *lend, uint32_t nu,
+                                                   uint32_t nch, T *out, uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  const uint32_t pc = p.pc;
+  const T bitval = (T)p.bitval;
+  uint32_t err = 0;
+  for (uint32_t r = 0; r < nu; ++r) {
+    const uint32_t lb = uniform(lbeg[r]);
+    if (lb == kBad) continue;
+    const uint32_t c0 = r * a.S;
+    const uint32_t m = min(a.S, nch - c0);
+    const uint32_t pay0 = lb + m;  // first payload bit of the segment
+    uint32_t run = 0;              // compressed chunks of the segment before this pass
+    T *o = out + c0;
+    for (uint32_t q = 0; q < m; q += kWave) {
+      uint64_t H = uniform64(lds_field<uint64_t>(stg, lb + q));  // this pass's participation bits
+      if (m - q < kWave) H &= low_lanes(m - q);
+      const uint32_t i = q + lane;
+      const bool h = (H >> lane) & 1ull;
+      const uint32_t pos = pay0 + i * W - pc * (run + count_below(H));
+      const T x = lds_field<T>(stg, pos);
+      const T v = h ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
+      if (i < m) o[i] = v;
+      run += popc(H);
+    }
+    if (pay0 + m * W - pc * run != uniform(lend[r])) err |= IBP_DEVERR_CORRUPT;
+  }
+  return err;
+}
+
+// S dividing 64: each pass holds 64/S whole segments.
+template <typename T, bool kGather, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_small_s(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
+                                                   const uint32_t *lbeg, const uint32_t *lend, uint32_t nch,
+                                                   T *out, uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  const uint32_t pc = p.pc;
+  const T bitval = (T)p.bitval;
+  const uint32_t i = lane & (a.S - 1u);
+  const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));  // lanes of earlier segments in the pass
+  uint32_t err = 0;
+  for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
+    const uint32_t cl = p0 + lane;
+    const bool valid = cl < nch;
+    const uint32_t r = cl >> a.s_log2;
+    const uint32_t lb = valid ? lbeg[r] : kBad;
+    const bool ok = lb != kBad;
+    uint32_t m = a.S;
+    if constexpr (!kGather) m = valid ? min(a.S, nch - (r << a.s_log2)) : a.S;
+    const bool h = ok && lds_bit(stg, lb + i);
+    const uint64_t H = ballot(h);
+    const uint32_t cnt = count_below(H) - popc(H & seg_below);
+    const uint32_t pos = ok ? lb + m + i * W - pc * cnt : 0u;
+    const T x = lds_field<T>(stg, pos);
+    const T v = h ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
+    if (ok) {
+      out[cl] = v;
+      if (i == m - 1 && pos + (h ? W - pc : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
+    }
+  }
+  return err;
+}
+
+// Any S: a segment may start anywhere in a pass and span passes; the number of
+// compressed chunks before each segment start is kept in gseg.
+template <typename T, bool kGather>
+__device__ __forceinline__ uint32_t decode_general(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
+                                                   const uint32_t *lbeg, const uint32_t *lend, uint32_t *gseg,
+                                                   uint32_t nch, T *out, uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  const uint32_t pc = p.pc;
+  const T bitval = (T)p.bitval;
+  uint32_t err = 0;
+  uint32_t running = 0;  // compressed chunks among tile chunks [0, p0)
+  for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
+    const uint32_t cl = p0 + lane;
+    const bool valid = cl < nch;
+    const uint32_t r = cl / a.S;
+    const uint32_t i = cl - r * a.S;
+    const uint32_t lb = valid ? lbeg[r] : kBad;
+    const bool ok = lb != kBad;
+    uint32_t m = a.S;
+    if constexpr (!kGather) m = valid ? min(a.S, nch - r * a.S) : a.S;
+    const bool h = ok && lds_bit(stg, lb + i);
+    const uint64_t H = ballot(h);
+    const uint32_t g_cl = running + count_below(H);
+    const uint32_t s0 = r * a.S;
+    uint32_t g_start;
+    if (s0 >= p0)
+      g_start = running + popc(H & low_lanes(s0 - p0));
+    else
+      g_start = valid ? gseg[r] : 0u;
+    if (valid && i == 0) gseg[r] = g_cl;
+    const uint32_t pos = ok ? lb + m + i * W - pc * (g_cl - g_start) : 0u;
+    const T x = lds_field<T>(stg, pos);
+    const T v = h ? (deposit_free<T, 0>(x, p.runs) | bitval) : x;
+    if (ok) {
+      out[cl] = v;
+      if (i == m - 1 && pos + (h ? W - pc : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
+    }
+    running += popc(H);
+    wave_lds_sync();
+  }
+  return err;
+}
+
+template <typename T, bool kGather, uint32_t kMode, uint32_t NR>
+__global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParams p) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWave);
+  const uint64_t u0 = ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * a.G;
+  if (u0 >= a.n_units) return;
+  const uint32_t nu = (uint32_t)min((uint64_t)a.G, a.n_units - u0);
+  uint32_t *stg = smem + (uint64_t)wave * a.wave_dw;
+  uint32_t *lbeg = stg + a.stage_dw;
+  uint32_t *lend = lbeg + a.G;
+  uint32_t *gseg = lend + a.G;
+  const uint64_t chunk0 = u0 * a.S;
+  const uint32_t nch = (uint32_t)min((uint64_t)nu * a.S, a.n_chunks - chunk0);
+  uint32_t err = 0;
+
+  if constexpr (!kGather) {
+    // a. the tile's range [A, B) and its segments
+    const uint64_t A = a.off[u0], B = a.off[u0 + nu];
+    const bool tile_ok = A <= B && B - A <= (uint64_t)nch * (W + 1) && B <= a.stream_bytes * 8u;
+    if (!tile_ok) {
+      if (lane == 0 && a.err) atomicOr(a.err, IBP_DEVERR_CORRUPT);
+      return;
+    }
+    const uint64_t base = A & ~127ull;
+    for (uint32_t r = lane; r < nu; r += kWave) {
+      const uint64_t x = a.off[u0 + r], y = a.off[u0 + r + 1];
+      const uint64_t m = min((uint64_t)a.S, a.n_chunks - (u0 + r) * a.S);
+      const bool good = A <= x && x <= y && y <= B && y - x >= m && y - x <= m * (W + 1);
+      lbeg[r] = good ? (uint32_t)(x - base) : kBad;
+      lend[r] = good ? (uint32_t)(y - base) : kBad;
+      if (!good) err |= IBP_DEVERR_CORRUPT;
+    }
+    // b. stage
+    stage_range(a.stream, a.stream_bytes, A >> 7, (uint32_t)(((B + 127u) >> 7) - (A >> 7)), stg, lane);
+  } else {
+    uint64_t *ufirst = reinterpret_cast<uint64_t *>(gseg + a.G + (a.G & 1u));
+    uint32_t *unb = reinterpret_cast<uint32_t *>(ufirst + a.G);
+    const uint64_t whole = a.stream_bytes >> 4;
+    // a. rows
+    bool tail_row = false;
+    for (uint32_t r = lane; r < nu; r += kWave) {
+      const int64_t id = a.ids[u0 + r];
+      bool good = id >= 0 && (uint64_t)id < a.nseg;
+      if (!good) err |= IBP_DEVERR_BAD_ID;
+      uint64_t x = 0, y = 0;
+      if (good) {
+        x = a.off[id];
+        y = a.off[id + 1];
+        const bool sane = x <= y && y <= a.stream_bytes * 8u && y - x >= a.S && y - x <= (uint64_t)a.S * (W + 1);
+        if (!sane) {
+          good = false;
+          err |= IBP_DEVERR_CORRUPT;
+        }
+      }
+      const uint32_t slot = r * a.slot_dw * 32u;
+      lbeg[r] = good ? slot + (uint32_t)(x & 127u) : kBad;
+      lend[r] = good ? slot + (uint32_t)(y - (x & ~127ull)) : kBad;
+      ufirst[r] = x >> 7;
+      unb[r] = good ? (uint32_t)(((y + 127u) >> 7) - (x >> 7)) : 0u;
+      tail_row |= good && ((y + 127u) >> 7) > whole;
+    }
+    wave_lds_sync();
+    // b. stage every row into its slot: whole blocks first, all loads in flight
+    const uint32_t sb = a.slot_dw / 4u;
+    const uint32_t total = nu * sb;
+    for (uint32_t f0 = 0; f0 < total; f0 += 4 * kWave) {
+      uint4 tmp[4];
+      uint32_t dst[4];
+#pragma unroll
+      for (uint32_t u = 0; u < 4; ++u) {
+        const uint32_t f = f0 + u * kWave + lane;
+        const uint32_t r = f / sb, j = f - r * sb;
+        dst[u] = kBad;
+        if (f < total && j < unb[r] && ufirst[r] + j < whole) {
+          tmp[u] = load16(a.stream, ufirst[r] + j);
+          dst[u] = r * a.slot_dw + 4u * j;
+        }
+      }
+#pragma unroll
+      for (uint32_t u = 0; u < 4; ++u)
+        if (dst[u] != kBad) *reinterpret_cast<uint4 *>(stg + dst[u]) = tmp[u];
+    }
+    // the row that ends in the stream's last, partial block
+    if (ballot(tail_row)) {
+      for (uint32_t r = 0; r < nu; ++r) {
+        const uint32_t n_r = uniform(unb[r]);
+        const uint64_t f_r = uniform64(ufirst[r]);
+        if (n_r == 0 || f_r + n_r <= whole) continue;
+        for (uint32_t j = lane; j < n_r; j += kWave)
+          if (f_r + j >= whole)
+            *reinterpret_cast<uint4 *>(stg + r * a.slot_dw + 4u * j) = load16_tail(a.stream, a.stream_bytes, f_r + j);
+      }
+    }
+  }
+  wave_lds_sync();
+
+  // c. decode
+  T *out = static_cast<T *>(a.out) + chunk0;
+  if constexpr (kMode == kModeLargeS)
+    err |= decode_large_s<T, NR>(a, p, stg, lbeg, lend, nu, nch, out, lane);
+  else if constexpr (kMode == kModeSmallS)
+    err |= decode_small_s<T, kGather, NR>(a, p, stg, lbeg, lend, nch, out, lane);
+  else
+    err |= decode_general<T, kGather>(a, p, stg, lbeg, lend, gseg, nch, out, lane);
+  if (err && a.err) atomicOr(a.err, err);
+}
+
+// Uncompressed gather baseline: row j = row ids[j], 16 bytes per lane.
+__global__ void __launch_bounds__(kBlock) raw_gather_kernel(RawGatherArgs a) {
+  const uint64_t total = a.n_ids * a.row_blocks;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t f = (uint64_t)blockIdx.x * kBlock + threadIdx.x; f < total; f += stride) {
+    const uint64_t j = f / a.row_blocks, b = f - j * a.row_blocks;
+    const int64_t id = a.ids[j];
+    if (id < 0 || (uint64_t)id >= a.n_rows) {
+      if (b == 0 && a.err) atomicOr(a.err, IBP_DEVERR_BAD_ID);
+      continue;
+    }
+    const uint4 x = reinterpret_cast<const uint4 *>(a.src)[(uint64_t)id * a.row_blocks + b];
+    reinterpret_cast<uint4 *>(a.out)[f] = x;
+  }
+}
+
+// ------------------------------------------------------------------ launch
+
+struct Launch {
+  dim3 grid;
+  size_t shmem;
+  hipStream_t s;
+};
+
+template <typename T, bool G, uint32_t M, uint32_t NR>
+hipError_t go(const DecodeArgs &a, const CodecParams &p, const Launch &l) {
+  hipLaunchKernelGGL((decode_kernel<T, G, M, NR>), l.grid, dim3(kBlock), l.shmem, l.s, a, p);
+  return hipGetLastError();
+}
+
+template <typename T, bool G, uint32_t M>
+hipError_t go_runs(const DecodeArgs &a, const CodecParams &p, const Launch &l) {
+  switch (runs_bucket(p.runs.n)) {
+    case 1: return go<T, G, M, 1>(a, p, l);
+    case 2: return go<T, G, M, 2>(a, p, l);
+    case 3: return go<T, G, M, 3>(a, p, l);
+    case 4: return go<T, G, M, 4>(a, p, l);
+    case 5: return go<T, G, M, 5>(a, p, l);
+    case 6: return go<T, G, M, 6>(a, p, l);
+    case 7: return go<T, G, M, 7>(a, p, l);
+    case 8: return go<T, G, M, 8>(a, p, l);
+    default: return go<T, G, M, 0>(a, p, l);
+  }
+}
+
+template <typename T, bool G>
+hipError_t go_mode(const DecodeArgs &a, const CodecParams &p, const Launch &l) {
+  if (a.S % kWave == 0) return go_runs<T, G, kModeLargeS>(a, p, l);
+  if (kWave % a.S == 0) return go_runs<T, G, kModeSmallS>(a, p, l);
+  return go<T, G, kModeGeneral, 0>(a, p, l);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather, hipStream_t s) {
+  if (a.n_units == 0) return hipSuccess;
+  const uint64_t tiles = (a.n_units + a.G - 1) / a.G;
+  const uint64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
+  if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  if (a.S % kWave != 0 && kWave % a.S == 0 && a.s_log2 == kNotPow2) return hipErrorInvalidValue;
+  const Launch l{dim3((uint32_t)blocks), (size_t)a.wave_dw * 4 * kWavesPerBlock, s};
+  if (p.W == 32) return gather ? go_mode<uint32_t, true>(a, p, l) : go_mode<uint32_t, false>(a, p, l);
+  return gather ? go_mode<uint64_t, true>(a, p, l) : go_mode<uint64_t, false>(a, p, l);
+}
+
+hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s) {
+  const uint64_t total = a.n_ids * a.row_blocks;
+  if (total == 0) return hipSuccess;
+  const uint64_t want = (total + kBlock - 1) / kBlock;
+  const uint32_t blocks = (uint32_t)(want < 65536 ? want : 65536);
+  hipLaunchKernelGGL(raw_gather_kernel, dim3(blocks), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ibp

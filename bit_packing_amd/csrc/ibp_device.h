@@ -1,0 +1,164 @@
+// ibp_device.h -- device helpers shared by the gfx950 kernels of the IBP codec:
+// 64-lane wave primitives, run-decomposed bit extract/deposit, LDS bit fields,
+// 16-byte loads and agent-scope atomics.
+#pragma once
+
+#include "ibp.h"
+#include "ibp_internal.h"
+
+namespace ibp {
+namespace dev {
+
+// ------------------------------------------------------------------ wave helpers
+
+__device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Number of set bits of m in the lanes below this one (v_mbcnt).
+__device__ __forceinline__ uint32_t count_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+__device__ __forceinline__ uint32_t popc(uint64_t m) { return (uint32_t)__builtin_popcountll(m); }
+
+__device__ __forceinline__ uint64_t low_lanes(uint32_t k) {  // bits [0, k), k <= 64
+  return k >= 64 ? ~0ull : ((1ull << k) - 1ull);
+}
+
+// readfirstlane returns int: convert through uint32_t so nothing is sign-extended.
+__device__ __forceinline__ uint32_t uniform(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// Orders this wavefront's LDS accesses around the call.  LDS instructions of one
+// wavefront execute in program order, so only the compiler needs fencing.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint64_t wave_sum64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_sum32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// ------------------------------------------------------------------ bit moves
+
+// Parallel bit extract / deposit over the free (non-Mask) positions, one shift,
+// AND and OR per run.  NR = number of runs when known at compile time (1..8),
+// NR = 0 for a loop over the runtime count.
+template <typename T, uint32_t NR> __device__ __forceinline__ T extract_free(T v, const Runs &rr) {
+  T out = 0;
+  if constexpr (NR == 0) {
+    for (uint32_t r = 0; r < rr.n; ++r) out |= (v >> rr.shift[r]) & (T)rr.pmask[r];
+  } else {
+#pragma unroll
+    for (uint32_t r = 0; r < NR; ++r) out |= (v >> rr.shift[r]) & (T)rr.pmask[r];
+  }
+  return out;
+}
+
+template <typename T, uint32_t NR> __device__ __forceinline__ T deposit_free(T x, const Runs &rr) {
+  T out = 0;
+  if constexpr (NR == 0) {
+    for (uint32_t r = 0; r < rr.n; ++r) out |= (x & (T)rr.pmask[r]) << rr.shift[r];
+  } else {
+#pragma unroll
+    for (uint32_t r = 0; r < NR; ++r) out |= (x & (T)rr.pmask[r]) << rr.shift[r];
+  }
+  return out;
+}
+
+// ------------------------------------------------------------------ LDS bit fields
+
+__device__ __forceinline__ uint32_t lds_bit(const uint32_t *s, uint32_t q) {
+  return (s[q >> 5] >> (q & 31u)) & 1u;
+}
+
+// sizeof(T)*8 bits starting at local bit q (stream order, low bit first).
+template <typename T> __device__ __forceinline__ T lds_field(const uint32_t *s, uint32_t q);
+
+template <> __device__ __forceinline__ uint32_t lds_field<uint32_t>(const uint32_t *s, uint32_t q) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  return __builtin_amdgcn_alignbit(s[d + 1], s[d], sh);
+}
+
+template <> __device__ __forceinline__ uint64_t lds_field<uint64_t>(const uint32_t *s, uint32_t q) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  const uint32_t w0 = s[d], w1 = s[d + 1], w2 = s[d + 2];
+  const uint32_t lo = __builtin_amdgcn_alignbit(w1, w0, sh);
+  const uint32_t hi = __builtin_amdgcn_alignbit(w2, w1, sh);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// OR a field whose bits above its length are 0 into LDS at bit q.
+__device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint32_t x) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  const uint32_t lo = x << sh;
+  const uint32_t hi = sh ? (x >> (32u - sh)) : 0u;
+  if (lo) atomicOr(&s[d], lo);
+  if (hi) atomicOr(&s[d + 1], hi);
+}
+
+__device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint64_t x) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  const uint32_t x0 = (uint32_t)x, x1 = (uint32_t)(x >> 32);
+  const uint32_t w0 = x0 << sh;
+  const uint32_t w1 = sh ? ((x1 << sh) | (x0 >> (32u - sh))) : x1;
+  const uint32_t w2 = sh ? (x1 >> (32u - sh)) : 0u;
+  if (w0) atomicOr(&s[d], w0);
+  if (w1) atomicOr(&s[d + 1], w1);
+  if (w2) atomicOr(&s[d + 2], w2);
+}
+
+// ------------------------------------------------------------------ global memory
+
+__device__ __forceinline__ uint4 load16(const uint8_t *src, uint64_t blk) {
+  return *reinterpret_cast<const uint4 *>(src + blk * 16u);
+}
+
+// The 16-byte block that holds the last bytes of a buffer of nbytes bytes whose
+// length is not a multiple of 16: read byte by byte, bytes past the end are 0.
+__device__ __noinline__ uint4 load16_tail(const uint8_t *src, uint64_t nbytes, uint64_t blk) {
+  const uint64_t b0 = blk * 16u;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  for (uint32_t j = 0; j < 16u; ++j)
+    if (b0 + j < nbytes) w[j >> 2] |= (uint32_t)src[b0 + j] << (8u * (j & 3u));
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint64_t atomic_load_agent(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_store_agent(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t atomic_load_agent32(const uint32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace dev
+
+// Compile-time run count for a runtime one: 1..8 exactly, 0 = loop.
+inline uint32_t runs_bucket(uint32_t n) { return (n >= 1 && n <= 8) ? n : 0u; }
+
+}  // namespace ibp

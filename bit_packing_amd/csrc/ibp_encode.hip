@@ -1,0 +1,251 @@
+// ibp_encode.hip -- step 2 of the IBP codec on gfx950: compression in one pass
+// ("Riduzione del Collo di Bottiglia della Memoria GPU con la Compressione
+// Lossless per il ML", section "Algoritmo Core", Compressione).
+//
+// A chunk whose Mask bits equal Bitval loses them (the remaining bits close up
+// towards bit 0); every chunk gets a participation bit.  The participation bits
+// of a segment are written first, as its header, then the payloads.  Each
+// workgroup sizes its tile, obtains the tile's starting bit through a decoupled
+// look-back over its predecessors (Merrill & Garland, "Single-pass Parallel
+// Prefix Scan with Decoupled Look-back", 2016), and packs the tile in LDS.
+#include "ibp_device.h"
+
+namespace ibp {
+namespace {
+
+using namespace dev;
+
+// One workgroup per tile of G consecutive segments (about kEncTileChunks chunks).
+//  1. take a tile ticket (tiles are numbered in start order, so every tile a
+//     tile waits for is already running);
+//  2. load the chunks, test the invariant bits, ballot the participation bits;
+//  3. the tile's bit count follows from the number of matching chunks; publish
+//     it, then wavefront 0 walks back over the predecessors' status words 64 at
+//     a time (decoupled look-back) to get the tile's starting bit;
+//  4. write the segment offsets, assemble the tile's bits in LDS with atomic ORs
+//     (headers, then payloads = parallel bit extract or the raw chunk);
+//  5. store the whole dwords; the dword shared with the previous tile is written
+//     by this tile after OR-ing in the bits the previous tile handed over, and the
+//     dword shared with the next tile is handed over instead of written.
+template <typename T, uint32_t NR>
+__global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParams p) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+  uint32_t *obuf = smem;
+  uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // 16 words
+  uint32_t *pref = reinterpret_cast<uint32_t *>(bal + 16);          // 17 words
+  __shared__ uint64_t s_excl;
+  __shared__ uint32_t s_tile;
+  __shared__ uint32_t s_failed;
+
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
+  if (tid == 0) s_tile = atomicAdd(&a.control[0], 1u);
+  for (uint32_t d = tid; d < a.obuf_dw; d += kBlock) obuf[d] = 0u;
+  __syncthreads();
+  const uint64_t t = s_tile;
+  if (t >= a.ntiles) return;  // more workgroups than tiles: cannot happen, grid == ntiles
+
+  const uint64_t k0 = t * a.G;
+  const uint64_t c0 = k0 * a.S;
+  const uint32_t nsegt = (uint32_t)min((uint64_t)a.G, a.nseg - k0);
+  const uint32_t nch = (uint32_t)min((uint64_t)a.tile_chunks, a.n_chunks - c0);
+  const T *in = static_cast<const T *>(a.in) + c0;
+  const T mask = (T)p.mask, bitval = (T)p.bitval;
+
+  // 2. chunks and participation bits
+  constexpr uint32_t kQ = kEncTileChunks / kBlock;  // passes of 256 chunks
+  T v[kQ];
+  uint32_t hbits = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < kQ; ++q) {
+    const uint32_t cl = q * kBlock + tid;
+    v[q] = cl < nch ? in[cl] : (T)0;
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < kQ; ++q) {
+    const uint32_t cl = q * kBlock + tid;
+    const bool h = cl < nch && ((v[q] ^ bitval) & mask) == 0;
+    hbits |= (uint32_t)h << q;
+    const uint64_t B = ballot(h);
+    if (lane == 0) bal[q * kWavesPerBlock + wave] = B;
+  }
+  __syncthreads();
+  if (tid <= 16) {
+    uint32_t s = 0;
+    for (uint32_t j = 0; j < tid; ++j) s += popc(bal[j]);
+    pref[tid] = s;
+  }
+  __syncthreads();
+  // matching chunks among tile chunks [0, x)
+  auto g = [&](uint32_t x) -> uint32_t {
+    const uint32_t b = x >> 6, o = x & 63u;
+    return pref[b] + (o ? popc(bal[b] & low_lanes(o)) : 0u);
+  };
+  const uint64_t agg = (uint64_t)nch * (W + 1) - (uint64_t)p.pc * pref[16];
+
+  // 3. decoupled look-back
+  if (wave == 0) {
+    uint64_t excl = 0;
+    bool timed_out = false;
+    if (t == 0) {
+      if (lane == 0) atomic_store_agent(&a.status[0], kFlagPrefix | agg);
+    } else {
+      if (lane == 0) atomic_store_agent(&a.status[t], kFlagAggregate | agg);
+      int64_t base = (int64_t)t - 1;
+      uint32_t spins = 0;
+      while (true) {
+        const int64_t j = base - (int64_t)lane;
+        const uint64_t s = j >= 0 ? atomic_load_agent(&a.status[j]) : kFlagPrefix;
+        const uint64_t flag = s & ~kValueMask;
+        const uint64_t pm = ballot(flag == kFlagPrefix);
+        const uint64_t zm = ballot(flag == 0);
+        const uint32_t first_p = pm ? (uint32_t)__builtin_ctzll(pm) : 64u;
+        const uint64_t needed = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
+        if ((zm & needed) && !timed_out) {
+          // bounded wait: give up when another tile has aborted or after ~2^20 polls
+          bool give_up = false;
+          if ((++spins & 1023u) == 0u) give_up = atomic_load_agent32(&a.control[1]) != 0u;
+          if (spins > (1u << 20)) {
+            give_up = true;
+            if (lane == 0) {
+              atomic_store_agent32(&a.control[1], 1u);
+              if (a.err) atomicOr(a.err, IBP_DEVERR_TIMEOUT);
+            }
+          }
+          timed_out = ballot(give_up) != 0;
+          if (!timed_out) __builtin_amdgcn_s_sleep(1);
+          continue;
+        }
+        excl += wave_sum64(lane <= first_p ? (s & kValueMask) : 0ull);
+        if (first_p < 64) break;
+        base -= 64;
+      }
+      if (lane == 0) atomic_store_agent(&a.status[t], kFlagPrefix | ((excl + agg) & kValueMask));
+    }
+    if (lane == 0) {
+      s_excl = excl;
+      s_failed = timed_out ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint64_t excl = s_excl;
+  // a tile that gave up waiting has no valid start bit: it must not store anything
+  // that depends on it (its neighbours see the abort flag and give up as well)
+  const bool failed = s_failed != 0u;
+
+  // 4a. segment offsets
+  if (failed) {
+    if (tid == 0) atomic_store_agent(&a.tails[t], kTailReady);
+    return;
+  }
+  for (uint32_t r = tid; r < nsegt; r += kBlock)
+    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)p.pc * g(r * a.S);
+  if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
+
+  // 4b. pack into LDS; bit 0 of obuf is stream bit (excl & ~31)
+  const uint32_t lb0 = (uint32_t)(excl & 31u);
+#pragma unroll
+  for (uint32_t q = 0; q < kQ; ++q) {
+    const uint32_t cl = q * kBlock + tid;
+    if (cl < nch) {
+      uint32_t r, i;
+      if (a.s_log2 != kNotPow2) {
+        r = cl >> a.s_log2;
+        i = cl & (a.S - 1u);
+      } else {
+        r = cl / a.S;
+        i = cl - r * a.S;
+      }
+      const uint32_t s0 = r * a.S;
+      const uint32_t m = min(a.S, nch - s0);
+      const uint32_t gs = g(s0);
+      const uint32_t segbase = lb0 + s0 * (W + 1) - p.pc * gs;
+      const bool h = (hbits >> q) & 1u;
+      if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
+      const uint32_t pos = segbase + m + i * W - p.pc * (g(cl) - gs);
+      const T payload = h ? extract_free<T, NR>(v[q], p.runs) : v[q];
+      lds_or_field(obuf, pos, payload);
+    }
+  }
+  __syncthreads();
+
+  // 5. store; hand over the shared last dword, complete the shared first dword
+  const uint32_t nd = (uint32_t)((lb0 + agg + 31u) >> 5);
+  const bool has_head = lb0 != 0u;
+  const bool has_tail = ((lb0 + agg) & 31u) != 0u;
+  const bool last = t == a.ntiles - 1;
+  uint32_t *gdst = a.stream + (excl >> 5);
+  for (uint32_t d = tid; d < nd; d += kBlock) {
+    const bool skip = (d == 0 && has_head) || (d == nd - 1 && has_tail && !last);
+    if (!skip) gdst[d] = obuf[d];
+  }
+  if (tid == 0) {
+    if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | obuf[nd - 1]);
+    if (has_head) {
+      uint64_t prev = 0;
+      uint32_t spins = 0;
+      while (true) {
+        prev = atomic_load_agent(&a.tails[t - 1]);
+        if (prev & kTailReady) break;
+        if ((++spins & 1023u) == 0u && atomic_load_agent32(&a.control[1]) != 0u) break;
+        if (spins > (1u << 20)) {
+          atomic_store_agent32(&a.control[1], 1u);
+          if (a.err) atomicOr(a.err, IBP_DEVERR_TIMEOUT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      gdst[0] = obuf[0] | (uint32_t)prev;
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) zero_kernel(uint64_t *p, uint64_t n) {
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < n; i += stride) p[i] = 0;
+}
+
+}  // namespace
+
+static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; }
+
+template <typename T, uint32_t NR>
+static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
+  hipLaunchKernelGGL((encode_kernel<T, NR>), dim3((uint32_t)a.ntiles), dim3(kBlock), shmem, s, a, p);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_encode_w(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
+  switch (runs_bucket(p.runs.n)) {
+    case 1: return launch_encode_t<T, 1>(a, p, shmem, s);
+    case 2: return launch_encode_t<T, 2>(a, p, shmem, s);
+    case 3: return launch_encode_t<T, 3>(a, p, shmem, s);
+    case 4: return launch_encode_t<T, 4>(a, p, shmem, s);
+    case 5: return launch_encode_t<T, 5>(a, p, shmem, s);
+    case 6: return launch_encode_t<T, 6>(a, p, shmem, s);
+    case 7: return launch_encode_t<T, 7>(a, p, shmem, s);
+    case 8: return launch_encode_t<T, 8>(a, p, shmem, s);
+    default: return launch_encode_t<T, 0>(a, p, shmem, s);
+  }
+}
+
+hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const uint32_t blocks = (uint32_t)host_min((n + kBlock - 1) / kBlock, 4096);
+  hipLaunchKernelGGL(zero_kernel, dim3(blocks), dim3(kBlock), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s) {
+  if (a.ntiles == 0) return hipSuccess;
+  if (a.ntiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  // clear the ticket, abort flag, status and hand-over words (a kernel, not a
+  // memset node, so the sequence stays valid inside a captured graph)
+  hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
+  if (e != hipSuccess) return e;
+  const size_t shmem = (size_t)a.obuf_dw * 4 + 16 * 8 + 17 * 4;
+  return p.W == 32 ? launch_encode_w<uint32_t>(a, p, shmem, s) : launch_encode_w<uint64_t>(a, p, shmem, s);
+}
+
+}  // namespace ibp

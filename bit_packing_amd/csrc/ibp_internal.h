@@ -105,7 +105,7 @@ struct RawGatherArgs {
 
 constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;
 
-// Launchers (ibp_kernels.hip).  Each returns the hipError_t of its launch(es).
+// Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip).  Each returns the hipError_t of its launch(es).
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather, hipStream_t s);

@@ -1,0 +1,79 @@
+// ibp_meta.hip -- step 1 of the IBP codec on gfx950: Mask and Bitval from a
+// sample batch ("Riduzione del Collo di Bottiglia della Memoria GPU con la
+// Compressione Lossless per il ML", section "Algoritmo Core", Preprocessing).
+//
+// A bit position is invariant when its majority value holds in at least k of the
+// n samples; k arrives precomputed from T.  Counting is integer-only, so the GPU
+// and any other exact implementation agree on every count.
+#include "ibp_device.h"
+
+namespace ibp {
+namespace {
+
+using namespace dev;
+
+// Per-position one-counts: every thread keeps W register counters over a
+// grid-stride range of samples; a workgroup sums them into one row of partials.
+template <typename T>
+__global__ void __launch_bounds__(kBlock) count_ones_kernel(MetaArgs a) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  __shared__ uint32_t red[kWavesPerBlock][W];
+  const T *in = static_cast<const T *>(a.in);
+  uint32_t c[W];
+#pragma unroll
+  for (uint32_t b = 0; b < W; ++b) c[b] = 0;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t i = (uint64_t)blockIdx.x * kBlock + threadIdx.x; i < a.n; i += stride) {
+    const T v = in[i];
+#pragma unroll
+    for (uint32_t b = 0; b < W; ++b) c[b] += (uint32_t)((v >> b) & 1u);
+  }
+  const uint32_t lane = lane_id(), wave = threadIdx.x / kWave;
+#pragma unroll
+  for (uint32_t b = 0; b < W; ++b) {
+    const uint32_t s = wave_sum32(c[b]);
+    if (lane == 0) red[wave][b] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x < W) {
+    uint64_t s = 0;
+    for (uint32_t w = 0; w < kWavesPerBlock; ++w) s += red[w][threadIdx.x];
+    a.partial[(uint64_t)blockIdx.x * W + threadIdx.x] = s;
+  }
+}
+
+// One wavefront: lane b sums the partial counts of position b and applies the
+// threshold; the ballots of the per-lane verdicts are Mask and Bitval.
+__global__ void __launch_bounds__(kWave) meta_finish_kernel(MetaArgs a) {
+  const uint32_t b = threadIdx.x;
+  uint64_t c1 = 0;
+  if (b < a.W)
+    for (uint32_t j = 0; j < a.blocks; ++j) c1 += a.partial[(uint64_t)j * a.W + b];
+  const uint64_t c0 = a.n - c1;
+  const uint64_t majority = c1 > c0 ? c1 : c0;
+  const bool invariant = b < a.W && majority >= a.k;
+  const uint64_t mask = ballot(invariant);
+  const uint64_t bitval = ballot(invariant && c1 > c0);
+  a.result[b] = b < a.W ? c1 : 0;
+  if (b == 0) {
+    a.result[64] = mask;
+    a.result[65] = bitval;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_meta(const MetaArgs &a, hipStream_t s) {
+  if (a.n) {
+    if (a.W == 32)
+      hipLaunchKernelGGL(count_ones_kernel<uint32_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL(count_ones_kernel<uint64_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(meta_finish_kernel, dim3(1), dim3(kWave), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ibp
