@@ -231,7 +231,7 @@ IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_by
   a.s_log2 = log2_if_pow2(S);
   a.G = enc_segs_per_tile(S);
   a.tile_chunks = a.G * S;
-  a.obuf_dw = ((31 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;
+  a.obuf_dw = ((127 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;  // image from the 16-byte block of the first bit
   return status_of(launch_encode(a, p, s));
 }
 

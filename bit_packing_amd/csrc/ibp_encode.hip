@@ -15,35 +15,50 @@ namespace {
 
 using namespace dev;
 
+enum : uint32_t {
+  kModeGeneral = 0,  // any S
+  kModeSmallS = 1,   // 64 % S == 0: each 64-chunk block holds 64/S whole segments
+  kModeLargeS = 2,   // S % 64 == 0: each 64-chunk block lies inside one segment
+};
+
 // One workgroup per tile of G consecutive segments (about kEncTileChunks chunks).
 //  1. take a tile ticket (tiles are numbered in start order, so every tile a
 //     tile waits for is already running);
-//  2. load the chunks, test the invariant bits, ballot the participation bits;
-//  3. the tile's bit count follows from the number of matching chunks; publish
-//     it, then wavefront 0 walks back over the predecessors' status words 64 at
-//     a time (decoupled look-back) to get the tile's starting bit;
-//  4. write the segment offsets, assemble the tile's bits in LDS with atomic ORs
-//     (headers, then payloads = parallel bit extract or the raw chunk);
+//  2. load the chunks (16 per thread, 64 consecutive per wavefront per pass),
+//     test the invariant bits and ballot the participation bits; clear the LDS
+//     image while the loads are in flight;
+//  3. a wave-wide scan of the ballot popcounts gives the number of compressed
+//     chunks before every 64-chunk block, hence every segment's size and the
+//     tile's; publish it, then wavefront 0 walks back over the predecessors'
+//     status words 64 at a time (decoupled look-back) to get the tile's first bit;
+//  4. write the segment offsets; assemble the tile's bits in LDS with atomic ORs
+//     (headers as whole ballot fields, payloads = parallel bit extract or the raw
+//     chunk); bit 0 of the image is the first bit of the 16-byte block holding the
+//     tile's first bit, so interior stores are 16-byte aligned;
 //  5. store the whole dwords; the dword shared with the previous tile is written
 //     by this tile after OR-ing in the bits the previous tile handed over, and the
 //     dword shared with the next tile is handed over instead of written.
-template <typename T, uint32_t NR>
+// The per-chunk prefix count has the decoder's three forms (S a multiple of 64,
+// S dividing 64, any S).
+template <typename T, uint32_t kMode, uint32_t NR>
 __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
+  constexpr uint32_t kQ = kEncTileChunks / kBlock;   // passes of 256 chunks
+  constexpr uint32_t kBal = kEncTileChunks / kWave;  // 64-chunk blocks per tile
+  static_assert(kBal == kWave, "one ballot word per lane of the prefix scan");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   uint32_t *obuf = smem;
-  uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // 16 words
-  uint32_t *pref = reinterpret_cast<uint32_t *>(bal + 16);          // 17 words
+  uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // kBal words
+  uint32_t *pref = reinterpret_cast<uint32_t *>(bal + kBal);        // kBal + 1 words
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_tile;
   __shared__ uint32_t s_failed;
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
   if (tid == 0) s_tile = atomicAdd(&a.control[0], 1u);
-  for (uint32_t d = tid; d < a.obuf_dw; d += kBlock) obuf[d] = 0u;
   __syncthreads();
   const uint64_t t = s_tile;
-  if (t >= a.ntiles) return;  // more workgroups than tiles: cannot happen, grid == ntiles
+  if (t >= a.ntiles) return;  // grid == ntiles, so every ticket is a tile
 
   const uint64_t k0 = t * a.G;
   const uint64_t c0 = k0 * a.S;
@@ -51,39 +66,46 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   const uint32_t nch = (uint32_t)min((uint64_t)a.tile_chunks, a.n_chunks - c0);
   const T *in = static_cast<const T *>(a.in) + c0;
   const T mask = (T)p.mask, bitval = (T)p.bitval;
+  const uint32_t pc = p.pc;
 
-  // 2. chunks and participation bits
-  constexpr uint32_t kQ = kEncTileChunks / kBlock;  // passes of 256 chunks
+  // 2. chunks, participation bits; clear the image meanwhile
   T v[kQ];
-  uint32_t hbits = 0;
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
     const uint32_t cl = q * kBlock + tid;
     v[q] = cl < nch ? in[cl] : (T)0;
   }
+  for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kBlock)
+    *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
+  uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
     const uint32_t cl = q * kBlock + tid;
-    const bool h = cl < nch && ((v[q] ^ bitval) & mask) == 0;
-    hbits |= (uint32_t)h << q;
-    const uint64_t B = ballot(h);
-    if (lane == 0) bal[q * kWavesPerBlock + wave] = B;
+    B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
+    if (lane == 0) bal[q * kWavesPerBlock + wave] = B[q];
   }
   __syncthreads();
-  if (tid <= 16) {
-    uint32_t s = 0;
-    for (uint32_t j = 0; j < tid; ++j) s += popc(bal[j]);
-    pref[tid] = s;
+  // 3. compressed chunks before each 64-chunk block
+  if (wave == 0) {
+    const uint32_t c = popc(bal[lane]);
+    uint32_t x = c;
+#pragma unroll
+    for (uint32_t o = 1; o < kWave; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o, kWave);
+      if (lane >= o) x += y;
+    }
+    pref[lane] = x - c;
+    if (lane == kWave - 1) pref[kBal] = x;
   }
   __syncthreads();
-  // matching chunks among tile chunks [0, x)
+  // compressed chunks among tile chunks [0, x), any x <= tile size
   auto g = [&](uint32_t x) -> uint32_t {
     const uint32_t b = x >> 6, o = x & 63u;
     return pref[b] + (o ? popc(bal[b] & low_lanes(o)) : 0u);
   };
-  const uint64_t agg = (uint64_t)nch * (W + 1) - (uint64_t)p.pc * pref[16];
+  const uint64_t agg = (uint64_t)nch * (W + 1) - (uint64_t)pc * pref[kBal];
 
-  // 3. decoupled look-back
+  // decoupled look-back
   if (wave == 0) {
     uint64_t excl = 0;
     bool timed_out = false;
@@ -129,58 +151,82 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   }
   __syncthreads();
   const uint64_t excl = s_excl;
-  // a tile that gave up waiting has no valid start bit: it must not store anything
-  // that depends on it (its neighbours see the abort flag and give up as well)
-  const bool failed = s_failed != 0u;
-
-  // 4a. segment offsets
-  if (failed) {
+  // a tile that gave up waiting has no valid start bit: it stores nothing that
+  // depends on it (its neighbours see the abort flag and give up as well)
+  if (s_failed != 0u) {
     if (tid == 0) atomic_store_agent(&a.tails[t], kTailReady);
     return;
   }
+
+  // 4a. segment offsets
   for (uint32_t r = tid; r < nsegt; r += kBlock)
-    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)p.pc * g(r * a.S);
+    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)pc * g(r * a.S);
   if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
 
-  // 4b. pack into LDS; bit 0 of obuf is stream bit (excl & ~31)
-  const uint32_t lb0 = (uint32_t)(excl & 31u);
+  // 4b. pack into LDS
+  const uint32_t lb0 = (uint32_t)(excl & 127u);
+  const uint32_t i_lane = lane & (a.S - 1u);                   // small-S: index in segment
+  const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
-    const uint32_t cl = q * kBlock + tid;
-    if (cl < nch) {
-      uint32_t r, i;
-      if (a.s_log2 != kNotPow2) {
-        r = cl >> a.s_log2;
-        i = cl & (a.S - 1u);
-      } else {
-        r = cl / a.S;
-        i = cl - r * a.S;
-      }
-      const uint32_t s0 = r * a.S;
+    const uint32_t blk = q * kWavesPerBlock + wave;  // this wavefront's 64-chunk block
+    const uint32_t cb = blk * kWave;                 // its first tile chunk
+    if (cb >= nch) continue;                         // uniform
+    const uint32_t cl = cb + lane;
+    const bool valid = cl < nch;
+    const bool h = (B[q] >> lane) & 1ull;
+    const uint32_t g_cl = uniform(pref[blk]) + count_below(B[q]);
+    uint32_t i, s0, gs;
+    if constexpr (kMode == kModeLargeS) {
+      s0 = (cb / a.S) * a.S;  // uniform: the block lies in one segment
+      i = cl - s0;
+      gs = uniform(pref[s0 >> 6]);
       const uint32_t m = min(a.S, nch - s0);
-      const uint32_t gs = g(s0);
-      const uint32_t segbase = lb0 + s0 * (W + 1) - p.pc * gs;
-      const bool h = (hbits >> q) & 1u;
-      if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
-      const uint32_t pos = segbase + m + i * W - p.pc * (g(cl) - gs);
-      const T payload = h ? extract_free<T, NR>(v[q], p.runs) : v[q];
-      lds_or_field(obuf, pos, payload);
+      const uint32_t segbase = lb0 + s0 * (W + 1) - pc * gs;
+      if (lane == 0) lds_or_field(obuf, segbase + (cb - s0), B[q]);  // 64 header bits
+      const uint32_t pos = segbase + m + i * W - pc * (g_cl - gs);
+      if (valid) lds_or_field(obuf, pos, h ? extract_free<T, NR>(v[q], p.runs) : v[q]);
+    } else if constexpr (kMode == kModeSmallS) {
+      s0 = cb + (lane & ~(a.S - 1u));
+      i = i_lane;
+      gs = uniform(pref[blk]) + popc(B[q] & seg_below);
+      const uint32_t m = min(a.S, nch - min(s0, nch));
+      const uint32_t segbase = lb0 + s0 * (W + 1) - pc * gs;
+      if (valid && i == 0) lds_or_field(obuf, segbase, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
+      const uint32_t pos = segbase + m + i * W - pc * (g_cl - gs);
+      if (valid) lds_or_field(obuf, pos, h ? extract_free<T, NR>(v[q], p.runs) : v[q]);
+    } else {
+      const uint32_t r = cl / a.S;
+      s0 = r * a.S;
+      i = cl - s0;
+      if (valid) {
+        gs = g(s0);
+        const uint32_t m = min(a.S, nch - s0);
+        const uint32_t segbase = lb0 + s0 * (W + 1) - pc * gs;
+        if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
+        const uint32_t pos = segbase + m + i * W - pc * (g_cl - gs);
+        lds_or_field(obuf, pos, h ? extract_free<T, NR>(v[q], p.runs) : v[q]);
+      }
     }
   }
   __syncthreads();
 
-  // 5. store; hand over the shared last dword, complete the shared first dword
-  const uint32_t nd = (uint32_t)((lb0 + agg + 31u) >> 5);
-  const bool has_head = lb0 != 0u;
-  const bool has_tail = ((lb0 + agg) & 31u) != 0u;
+  // 5. store: obuf dword d is stream dword (excl >> 7) * 4 + d
   const bool last = t == a.ntiles - 1;
-  uint32_t *gdst = a.stream + (excl >> 5);
-  for (uint32_t d = tid; d < nd; d += kBlock) {
-    const bool skip = (d == 0 && has_head) || (d == nd - 1 && has_tail && !last);
-    if (!skip) gdst[d] = obuf[d];
-  }
+  const uint32_t first_d = lb0 >> 5;                         // dword holding the first bit
+  const uint32_t last_d = (uint32_t)((lb0 + agg - 1) >> 5);  // dword holding the last bit
+  const bool has_head = (lb0 & 31u) != 0u;
+  const bool has_tail = ((lb0 + agg) & 31u) != 0u;
+  const uint32_t lo = first_d + (has_head ? 1u : 0u);
+  const uint32_t hi = last_d + 1u - ((has_tail && !last) ? 1u : 0u);  // [lo, hi) stored directly
+  uint32_t *gdst = a.stream + ((excl >> 7) << 2);
+  const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
+  for (uint32_t d = lo + tid; d < a4; d += kBlock) gdst[d] = obuf[d];
+  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kBlock)
+    *reinterpret_cast<uint4 *>(gdst + d) = *reinterpret_cast<const uint4 *>(obuf + d);
+  for (uint32_t d = e4 + tid; d < hi; d += kBlock) gdst[d] = obuf[d];
   if (tid == 0) {
-    if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | obuf[nd - 1]);
+    if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | obuf[last_d]);
     if (has_head) {
       uint64_t prev = 0;
       uint32_t spins = 0;
@@ -195,7 +241,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      gdst[0] = obuf[0] | (uint32_t)prev;
+      gdst[first_d] = obuf[first_d] | (uint32_t)prev;
     }
   }
 }
@@ -209,25 +255,32 @@ __global__ void __launch_bounds__(kBlock) zero_kernel(uint64_t *p, uint64_t n) {
 
 static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; }
 
-template <typename T, uint32_t NR>
+template <typename T, uint32_t M, uint32_t NR>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  hipLaunchKernelGGL((encode_kernel<T, NR>), dim3((uint32_t)a.ntiles), dim3(kBlock), shmem, s, a, p);
+  hipLaunchKernelGGL((encode_kernel<T, M, NR>), dim3((uint32_t)a.ntiles), dim3(kBlock), shmem, s, a, p);
   return hipGetLastError();
+}
+
+template <typename T, uint32_t M>
+static hipError_t launch_encode_runs(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
+  switch (runs_bucket(p.runs.n)) {
+    case 1: return launch_encode_t<T, M, 1>(a, p, shmem, s);
+    case 2: return launch_encode_t<T, M, 2>(a, p, shmem, s);
+    case 3: return launch_encode_t<T, M, 3>(a, p, shmem, s);
+    case 4: return launch_encode_t<T, M, 4>(a, p, shmem, s);
+    case 5: return launch_encode_t<T, M, 5>(a, p, shmem, s);
+    case 6: return launch_encode_t<T, M, 6>(a, p, shmem, s);
+    case 7: return launch_encode_t<T, M, 7>(a, p, shmem, s);
+    case 8: return launch_encode_t<T, M, 8>(a, p, shmem, s);
+    default: return launch_encode_t<T, M, 0>(a, p, shmem, s);
+  }
 }
 
 template <typename T>
 static hipError_t launch_encode_w(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  switch (runs_bucket(p.runs.n)) {
-    case 1: return launch_encode_t<T, 1>(a, p, shmem, s);
-    case 2: return launch_encode_t<T, 2>(a, p, shmem, s);
-    case 3: return launch_encode_t<T, 3>(a, p, shmem, s);
-    case 4: return launch_encode_t<T, 4>(a, p, shmem, s);
-    case 5: return launch_encode_t<T, 5>(a, p, shmem, s);
-    case 6: return launch_encode_t<T, 6>(a, p, shmem, s);
-    case 7: return launch_encode_t<T, 7>(a, p, shmem, s);
-    case 8: return launch_encode_t<T, 8>(a, p, shmem, s);
-    default: return launch_encode_t<T, 0>(a, p, shmem, s);
-  }
+  if (a.S % kWave == 0) return launch_encode_runs<T, kModeLargeS>(a, p, shmem, s);
+  if (kWave % a.S == 0) return launch_encode_runs<T, kModeSmallS>(a, p, shmem, s);
+  return launch_encode_t<T, kModeGeneral, 0>(a, p, shmem, s);
 }
 
 hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s) {
@@ -244,7 +297,8 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   // memset node, so the sequence stays valid inside a captured graph)
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
-  const size_t shmem = (size_t)a.obuf_dw * 4 + 16 * 8 + 17 * 4;
+  const size_t shmem = (size_t)a.obuf_dw * 4 + (kEncTileChunks / kWave) * 12 + 4;
+  if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   return p.W == 32 ? launch_encode_w<uint32_t>(a, p, shmem, s) : launch_encode_w<uint64_t>(a, p, shmem, s);
 }
 

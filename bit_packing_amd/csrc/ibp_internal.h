@@ -13,7 +13,7 @@ constexpr uint32_t kWavesPerBlock = kBlock / kWave;
 constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-bit chunk
 
 // Compression tile: a workgroup sizes, offsets and packs about this many chunks.
-constexpr uint32_t kEncTileChunks = 1024;
+constexpr uint32_t kEncTileChunks = 4096;
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;

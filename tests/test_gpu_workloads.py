@@ -1,0 +1,84 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py
+times (same W, T, S, same calls).
+
+At these sizes the oracle cannot encode everything in seconds, so it checks:
+the metadata (all counts), the whole offset table (the oracle's size pass is
+cheap), sampled segments bit for bit (the oracle encodes single segments), and
+the round trip and the gathers against the input itself.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _bits(buf: np.ndarray, a: int, b: int) -> np.ndarray:
+    """Stream bits [a, b) of a byte buffer."""
+    chunk = buf[a // 8:(b + 7) // 8]
+    return np.unpackbits(chunk, bitorder="little")[a % 8:a % 8 + (b - a)]
+
+
+@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids"])
+def test_workload_full_size(name):
+    import bit_packing_amd as ibp
+
+    dev = torch.device("cuda:0")
+    say(f"workload {name}: generating")
+    inst = workloads.generate(name)
+    w = inst.w
+    W, T, S = w.W, w.T, w.S
+    flat = inst.data.reshape(-1)
+    x = torch.from_numpy(flat.view(np.uint8)).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    say(f"workload {name}: metadata")
+    meta, counts = ibp.ibp_build_metadata(torch.from_numpy(inst.sample.reshape(-1).view(np.uint8)).to(dev), W, T)
+    mask, bitval, c1 = oracle.build_meta(inst.sample.reshape(-1), W, T)
+    assert counts == c1.tolist() and (meta.mask, meta.bitval) == (mask, bitval)
+
+    say(f"workload {name}: compress {x.numel()} bytes")
+    comp = ibp.ibp_compress(meta, x, S, err=err)
+    off = comp.offsets.cpu().numpy().view(np.uint64)
+    ref_off = oracle.offsets(flat, W, mask, bitval, S)
+    assert np.array_equal(off, ref_off), "offset table differs"
+    total = int(off[-1])
+    stream_h = comp.stream[: (total + 7) // 8].cpu().numpy()
+    nseg = off.size - 1
+    rng = np.random.default_rng(7)
+    ks = sorted(set([0, 1, nseg // 2, nseg - 2, nseg - 1] + rng.integers(0, nseg, 60).tolist()) - {-1})
+    for k in ks:
+        seg, nbits = oracle.encode_segment(flat, W, mask, bitval, S, k)
+        assert nbits == int(off[k + 1] - off[k])
+        want = np.unpackbits(seg, bitorder="little")[:nbits]
+        assert np.array_equal(_bits(stream_h, int(off[k]), int(off[k + 1])), want), f"segment {k} differs"
+    # bits of the last byte above the total are zero
+    if total % 8:
+        assert stream_h[-1] >> (total % 8) == 0
+
+    say(f"workload {name}: decompress")
+    out = ibp.ibp_decompress(meta, comp.stream, comp.offsets, comp.n_chunks, S, err=err)
+    assert torch.equal(out, x), "round trip differs"
+    del out
+
+    if w.gather:
+        say(f"workload {name}: gather from pinned host memory")
+        n_rows = inst.data.shape[0]
+        ids_np = workloads.gather_ids(name, n_rows, 1)[0]
+        host = torch.empty((total + 7) // 8 + 16, dtype=torch.uint8, pin_memory=True)
+        host[: stream_h.size].copy_(torch.from_numpy(stream_h))
+        ids = torch.from_numpy(ids_np).to(dev)
+        rows = ibp.ibp_decompress_gather(meta, host, comp.offsets, S, ids, err=err)
+        got = rows.cpu().numpy().view(inst.data.dtype).reshape(len(ids_np), -1)
+        assert np.array_equal(got, inst.data[ids_np])
+        ref = oracle.decode_gather(stream_h, off, S, ids_np[:512], W, mask, bitval, inst.data.dtype)
+        assert np.array_equal(got[:512].reshape(-1), ref)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
