@@ -199,6 +199,12 @@ def main() -> int:
         last = ids_all[-1]
         ref_rows = torch.from_numpy(inst.data.reshape(n_rows, -1)[last].reshape(-1).view(np.uint8).copy()).to(dev)
         gather_ok = bool(torch.equal(out_rows, ref_rows))
+        # the same rows gathered uncompressed from the HBM copy of the table (context for the roofline)
+        raw_rows = torch.empty_like(out_rows)
+        _, rawd_ms = timer.run(lambda i: ibp.ibp_gather_raw(x, row_bytes, ids_d[args.warmup + i], out=raw_rows), args.steps)
+        extra["uncompressed_hbm_gather"] = {"kernel_ms": rawd_ms, "effective_GBps": m * row_bytes / rawd_ms / 1e6,
+                                            "algorithmic_GBps": (2 * m * row_bytes + 8 * m) / rawd_ms / 1e6}
+        del raw_rows
         step_bytes = m * row_bytes
         value = step_bytes * args.steps / wall / 1e9
         ms_per_step = wall / args.steps * 1e3

@@ -85,7 +85,8 @@ int status_of(hipError_t e) { return e == hipSuccess ? IBP_OK : IBP_ERR_DEVICE; 
 // Pageable host memory and stray pointers are refused here instead of being
 // handed to a kernel, where they would fault the GPU.  Pinned host memory is
 // returned through its device mapping (the zero-copy path).
-const void *device_range(const void *p, uint64_t bytes) {
+const void *device_range(const void *p, uint64_t bytes, bool *is_host = nullptr) {
+  if (is_host) *is_host = false;
   if (bytes == 0) return p;
   if (!p) return nullptr;
   hipPointerAttribute_t at;
@@ -97,6 +98,7 @@ const void *device_range(const void *p, uint64_t bytes) {
   if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) {
     dev = static_cast<const char *>(p);
   } else if (at.type == hipMemoryTypeHost && at.devicePointer) {
+    if (is_host) *is_host = true;
     const char *hp = at.hostPointer ? static_cast<const char *>(at.hostPointer) : static_cast<const char *>(p);
     dev = static_cast<const char *>(at.devicePointer) + (static_cast<const char *>(p) - hp);
   } else {
@@ -113,8 +115,8 @@ const void *device_range(const void *p, uint64_t bytes) {
   return dev;
 }
 
-template <typename P> bool view(P *&p, uint64_t bytes) {
-  const void *d = device_range(p, bytes);
+template <typename P> bool view(P *&p, uint64_t bytes, bool *is_host = nullptr) {
+  const void *d = device_range(p, bytes, is_host);
   if (bytes && !d) return false;
   p = const_cast<P *>(static_cast<const P *>(d));
   return true;
@@ -249,7 +251,8 @@ static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t
     return IBP_ERR_INVALID_ARG;
   if (!total_fits(n_chunks, p.W) || (gather && !total_fits(nseg * (uint64_t)S, p.W))) return IBP_ERR_SIZE;
   if (n_units == 0) return IBP_OK;
-  if (!view(stream_in, stream_bytes) || !view(d_offsets, 8 * (nseg + 1)) || !view(d_ids, gather ? 8 * n_units : 0) ||
+  bool host_stream = false;
+  if (!view(stream_in, stream_bytes, &host_stream) || !view(d_offsets, 8 * (nseg + 1)) || !view(d_ids, gather ? 8 * n_units : 0) ||
       !view(d_out, n_chunks * cb) || !view(d_err_word, d_err_word ? 4 : 0))
     return IBP_ERR_INVALID_ARG;
   DecodeArgs a;
@@ -264,7 +267,9 @@ static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t
   a.nseg = nseg;
   a.S = S;
   a.s_log2 = log2_if_pow2(S);
-  a.G = dec_units_per_tile(S);
+  // Rows read over PCIe go one per wavefront: more independent read streams keep
+  // more host reads in flight.  From HBM a wavefront takes about 512 chunks.
+  a.G = (gather && host_stream) ? 1u : dec_units_per_tile(S);
   const uint32_t tile_chunks = a.G * S;
   if (gather) {
     a.slot_dw = ((S * (p.W + 1) + 127) / 128 + 1) * 4;
