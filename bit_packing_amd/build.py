@@ -1,9 +1,11 @@
 """Build libibp.so for gfx950 in-tree with hipcc (no JIT cache, so the library
-travels with the source tree)."""
+travels with the source tree).  Each source compiles in its own hipcc process
+(in parallel), then one link."""
 from __future__ import annotations
 
 import os
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -11,26 +13,40 @@ SOURCES = [os.path.join(HERE, "csrc", f) for f in ("ibp_meta.hip", "ibp_encode.h
 LIB = os.path.join(HERE, "libibp.so")
 
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wall",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
     # packed-FP32 instructions stay off in every HIP build of this project
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fvisibility=hidden",
 ]
+_NOISE = "is not a recognized feature for this target"
+
+
+def _run(procs):
+    errs = []
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        msg = "\n".join(l for l in out.splitlines() if _NOISE not in l)
+        if p.returncode != 0:
+            errs.append(f"{' '.join(cmd)}\n{msg}")
+    if errs:
+        raise RuntimeError("hipcc failed:\n" + "\n\n".join(errs))
 
 
 def build_library(verbose: bool = False) -> str:
     """Compile csrc/*.hip into bit_packing_amd/libibp.so (always recompiles)."""
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    tmp = LIB + ".tmp"
-    cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           *SOURCES, "-o", tmp]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    msg = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{' '.join(cmd)}\n{msg}")
-    if verbose and msg.strip():
-        print(msg)
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    with tempfile.TemporaryDirectory(prefix="ibp_build_") as tmpd:
+        objs, procs = [], []
+        for src in SOURCES:
+            obj = os.path.join(tmpd, os.path.basename(src) + ".o")
+            cmd = [hipcc, *HIPCC_FLAGS, *inc, "-c", src, "-o", obj]
+            procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+            objs.append(obj)
+        _run(procs)
+        tmp = LIB + ".tmp"
+        cmd = [hipcc, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        _run([(cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True))])
     os.replace(tmp, LIB)
     return LIB
 

@@ -18,8 +18,8 @@ constexpr uint32_t kEncTileChunks = 4096;
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
 constexpr uint32_t kDecMaxUnits = 128;
-// Metadata count kernel: at most this many workgroups write partial counts.
-constexpr uint32_t kMetaMaxBlocks = 1024;
+// Metadata count kernel: at most this many workgroups (one per CU) write partial counts.
+constexpr uint32_t kMetaMaxBlocks = 256;
 
 // Status words of the compression look-back: 2-bit flag above a 62-bit value.
 constexpr uint64_t kFlagAggregate = 1ull << 62;

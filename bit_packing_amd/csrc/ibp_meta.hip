@@ -42,13 +42,22 @@ __global__ void __launch_bounds__(kBlock) count_ones_kernel(MetaArgs a) {
   }
 }
 
-// One wavefront: lane b sums the partial counts of position b and applies the
-// threshold; the ballots of the per-lane verdicts are Mask and Bitval.
-__global__ void __launch_bounds__(kWave) meta_finish_kernel(MetaArgs a) {
-  const uint32_t b = threadIdx.x;
+// One workgroup: wavefront w sums every fourth row of partial counts (lane b =
+// position b), the four sums meet in LDS, and wavefront 0 applies the threshold;
+// the ballots of its per-lane verdicts are Mask and Bitval.
+__global__ void __launch_bounds__(kBlock) meta_finish_kernel(MetaArgs a) {
+  __shared__ uint64_t red[kWavesPerBlock][kWave];
+  const uint32_t b = lane_id(), part = uniform(threadIdx.x / kWave);
   uint64_t c1 = 0;
-  if (b < a.W)
-    for (uint32_t j = 0; j < a.blocks; ++j) c1 += a.partial[(uint64_t)j * a.W + b];
+  if (b < a.W) {
+#pragma unroll 8
+    for (uint32_t j = part; j < a.blocks; j += kWavesPerBlock) c1 += a.partial[(uint64_t)j * a.W + b];
+  }
+  red[part][b] = c1;
+  __syncthreads();
+  if (part != 0) return;
+  c1 = 0;
+  for (uint32_t w = 0; w < kWavesPerBlock; ++w) c1 += red[w][b];
   const uint64_t c0 = a.n - c1;
   const uint64_t majority = c1 > c0 ? c1 : c0;
   const bool invariant = b < a.W && majority >= a.k;
@@ -72,7 +81,7 @@ hipError_t launch_meta(const MetaArgs &a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(meta_finish_kernel, dim3(1), dim3(kWave), 0, s, a);
+  hipLaunchKernelGGL(meta_finish_kernel, dim3(1), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 
