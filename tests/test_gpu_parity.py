@@ -215,3 +215,29 @@ def test_host_argument_checks(ibp):
     rc = lib.ibp_decompress(ibp.ctypes.byref(meta), stream.data_ptr(), 1 << 40, off.data_ptr(), 128, 128,
                             torch.empty(512, dtype=torch.uint8, device=dev).data_ptr(), None, None)
     assert rc == ibp.IBP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("src,dst", [("pinned", "device"), ("device", "pinned"), ("pinned", "pinned")])
+def test_zero_copy_compress(ibp, src, dst):
+    """Compression reading its input from, or writing its stream into, pinned host
+    memory through the device mapping (no staging copy): same bytes as the oracle."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(12)
+    W, S, mask, bitval = 32, 128, 0x78000000, 0x38000000
+    v = _data(rng, 3000 * S + 17, W, mask, bitval, 0.97)
+    meta = ibp.make_meta(W, mask, bitval)
+    xb = torch.from_numpy(v.view(np.uint8).copy())
+    x = xb.to(dev) if src == "device" else xb.pin_memory()
+    cap = ibp.ibp_max_stream_bytes(v.size, W)
+    out = torch.empty(cap, dtype=torch.uint8, device=dev) if dst == "device" else \
+        torch.empty(cap, dtype=torch.uint8, pin_memory=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    say(f"zero-copy compress {src} -> {dst}")
+    comp = ibp.ibp_compress(meta, x, S, err=err, out_stream=out)
+    torch.cuda.synchronize()
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off)
+    assert np.array_equal(out[: ref_stream.size].cpu().numpy(), ref_stream)
+    back = ibp.ibp_decompress(meta, out, comp.offsets, v.size, S, err=err)
+    assert np.array_equal(back.cpu().numpy(), v.view(np.uint8))
+    assert int(err.item()) == 0

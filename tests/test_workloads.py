@@ -54,12 +54,15 @@ EXPECTED = {
     "dlrm": (0x7800000078000000, 0x3800000038000000, 1.1226),
     "llm": (0x7C007C007C007C00, 0x3800380038003800, 1.3634),
     "ids": (0xFFFFFFFFFF000000, 0x0, 2.3705),
+    # 95% exact zeros: every bit keeps the value 0 in >= 90% of the samples, so a zero
+    # chunk costs its participation bit only: 32 / (0.95 * 1 + 0.05 * 33) = 12.31
+    "sparse": (0xFFFFFFFF, 0x0, 12.31),
 }
 
 
 @pytest.mark.parametrize("name", list(EXPECTED))
 def test_expected_metadata_and_ratio(name):
-    inst = workloads.generate(name, {"tiny": 1, "gnn": 0.02, "dlrm": 0.002, "llm": 0.002, "ids": 0.002}[name])
+    inst = workloads.generate(name, {"tiny": 1, "gnn": 0.02, "dlrm": 0.002, "llm": 0.002, "ids": 0.002, "sparse": 0.02}[name])
     W = inst.w.W
     mask, bitval, _ = oracle.build_meta(inst.sample, W, inst.w.T)
     em, eb, er = EXPECTED[name]

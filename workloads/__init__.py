@@ -13,9 +13,12 @@ dlrm   10,000,000 x 64 fp32 ~ U(-0.05, 0.05)       64    0.98   32    100,000 di
 llm    2^30 bf16 ~ N(0,1e-3), 0.1% N(0,1) outliers 64    0.97   256   first 2^20 elements
 ids    500,000,000 int64 ~ U[0,2^24), 5% U[0,2^40)  64    0.999  256   first 1,000,000 (before
                                                                       the 5% replacement)
+sparse 1,000,000 x 128 fp32, 95% +0, rest |N(0,1)|   32    0.9    128   10,000 distinct rows
 =====  ==========================================  ====  =====  ====  =========================
 
-gnn and dlrm rows are one segment each (S = one row) and are read back by gathers:
+The first five are the measured configurations; "sparse" is the sparse-feature
+regime of the IBP page's "Risultati" section (a GNN cache whose features are
+mostly exact zeros).  gnn, dlrm and sparse rows are one segment each (S = one row) and are read back by gathers:
 65,536 uniform row ids per step (gnn) and 32,768 Zipf(1.05) row ids per step (dlrm).
 ``scale`` shrinks the row/element counts (same distributions) for CPU-sized tests.
 All randomness comes from ``gen.c`` (counter-based SplitMix64), keyed by
@@ -62,6 +65,7 @@ def _load():
         L.gen_normal_f32.argtypes = [u64, u64, dbl, vp]
         L.gen_relu_normal_f32.argtypes = [u64, u64, vp]
         L.gen_uniform_f32.argtypes = [u64, u64, dbl, dbl, vp]
+        L.gen_sparse_abs_normal_f32.argtypes = [u64, u64, dbl, vp]
         L.gen_bf16_grad.argtypes = [u64, u64, dbl, dbl, vp]
         L.gen_ids.argtypes = [u64, u64, uint, vp]
         L.gen_replace_ids.argtypes = [u64, u64, dbl, uint, vp]
@@ -107,10 +111,13 @@ WORKLOADS = {
                     "uint16", 0, 0),
     "ids": Workload(5, "ids", "Integer id stream: 500,000,000 int64 ~ U[0, 2^24), 5% U[0, 2^40)", 64, 0.999, 256,
                     "int64", 0, 0),
+    "sparse": Workload(6, "sparse", "Sparse GNN feature cache: 1,000,000 nodes x 128 fp32, 95% zeros, rest |N(0,1)|",
+                       32, 0.9, 128, "float32", 128, 65536),
 }
 
-FULL_SIZE = {"tiny": 262_144, "gnn": 1_000_000, "dlrm": 10_000_000, "llm": 1 << 30, "ids": 500_000_000}
-SAMPLE_SIZE = {"tiny": 4096, "gnn": 10_000, "dlrm": 100_000, "llm": 1 << 20, "ids": 1_000_000}
+FULL_SIZE = {"tiny": 262_144, "gnn": 1_000_000, "dlrm": 10_000_000, "llm": 1 << 30, "ids": 500_000_000,
+             "sparse": 1_000_000}
+SAMPLE_SIZE = {"tiny": 4096, "gnn": 10_000, "dlrm": 100_000, "llm": 1 << 20, "ids": 1_000_000, "sparse": 10_000}
 
 
 @dataclass
@@ -136,7 +143,7 @@ def size_at(name: str, scale: float) -> int:
     n = int(FULL_SIZE[name] * scale)
     if name == "llm":
         n -= n % 4  # whole 64-bit chunks of bf16
-    return max(n, 1 if name in ("gnn", "dlrm") else 64)
+    return max(n, 1 if name in ("gnn", "dlrm", "sparse") else 64)
 
 
 def generate(name: str, scale: float = 1.0) -> Instance:
@@ -156,6 +163,9 @@ def generate(name: str, scale: float = 1.0) -> Instance:
     elif name == "dlrm":
         data = np.empty((n, w.row_elems), np.float32)
         L.gen_uniform_f32(k_data, data.size, -0.05, 0.05, data.ctypes.data)
+    elif name == "sparse":
+        data = np.empty((n, w.row_elems), np.float32)
+        L.gen_sparse_abs_normal_f32(k_data, data.size, 0.05, data.ctypes.data)
     elif name == "llm":
         data = np.empty(n, np.uint16)
         L.gen_bf16_grad(k_data, n, 1e-3, 1e-3, data.ctypes.data)
@@ -181,13 +191,13 @@ def generate(name: str, scale: float = 1.0) -> Instance:
 
 
 def gather_ids(name: str, n_rows: int, steps: int, per_step: int | None = None) -> np.ndarray:
-    """Row ids of `steps` gather steps, shape (steps, per_step): uniform for gnn,
-    Zipf(1.05) over ranks with a seeded rank -> row permutation for dlrm."""
+    """Row ids of `steps` gather steps, shape (steps, per_step): uniform for gnn and
+    sparse, Zipf(1.05) over ranks with a seeded rank -> row permutation for dlrm."""
     w = WORKLOADS[name]
     per_step = per_step or w.gather
     L = _load()
     out = np.empty((steps, per_step), np.int64)
-    if name == "gnn":
+    if name in ("gnn", "sparse"):
         for s in range(steps):
             L.gen_uniform_ids(key(w.seed * 1_000_000 + s, 4), n_rows, per_step, out[s].ctypes.data)
     elif name == "dlrm":

@@ -63,6 +63,14 @@ void gen_relu_normal_f32(uint64_t key, uint64_t n, float *out) {
   }
 }
 
+/* Sparse features: out[i] = |N(0,1)| with probability p_nonzero, else +0.0. */
+void gen_sparse_abs_normal_f32(uint64_t key, uint64_t n, double p_nonzero, float *out) {
+  const uint64_t k_sel = gen_key(key, 1);
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < (int64_t)n; ++i)
+    out[i] = u01(k_sel, (uint64_t)i) < p_nonzero ? (float)fabs(normal(key, (uint64_t)i)) : 0.0f;
+}
+
 /* out[i] = fp32(lo + (hi - lo) * U[0,1)) */
 void gen_uniform_f32(uint64_t key, uint64_t n, double lo, double hi, float *out) {
 #pragma omp parallel for schedule(static)
