@@ -75,8 +75,13 @@ def _load():
         lib.ibpo_decode.argtypes = [_vp, _u64, _vp, _u64, _uint, _u64, _u64, _u64, _vp, _int]
         lib.ibpo_decode_gather.argtypes = [_vp, _u64, _vp, _u64, _u64, _vp, _u64, _uint, _u64,
                                            _u64, _vp, _int]
+        lib.ibpo_encode_slots.argtypes = [_vp, _u64, _uint, _u64, _u64, _u64, _vp, _vp]
+        lib.ibpo_slot_bits.argtypes = [_vp, _u64, _uint, _u64, _u64, _vp]
+        lib.ibpo_slot_bits.restype = _u64
+        lib.ibpo_decode_slots_gather.argtypes = [_vp, _u64, _uint, _u64, _u64, _u64, _vp, _vp, _u64, _vp, _int]
         for f in ("ibpo_count_ones", "ibpo_meta_from_counts", "ibpo_build_meta", "ibpo_offsets",
-                  "ibpo_encode", "ibpo_encode_segment", "ibpo_decode", "ibpo_decode_gather"):
+                  "ibpo_encode", "ibpo_encode_segment", "ibpo_decode", "ibpo_decode_gather",
+                  "ibpo_encode_slots", "ibpo_decode_slots_gather"):
             getattr(lib, f).restype = _int
         _lib = lib
     return _lib
@@ -217,3 +222,37 @@ def decode_gather(stream: np.ndarray, off: np.ndarray, S: int, ids: np.ndarray, 
     if isb:
         return out[: m * S * (W // 8)].view(out_dtype)
     return out[: m * S]
+
+
+# ------------------------------------------------------------------ fixed-slot layout
+
+def encode_slots(x: np.ndarray, W: int, mask: int, bitval: int, S: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(slots bytes, 64-bit flag words, used bits per slot) of the rows of x (S chunks each)
+    in the fixed-slot layout: a row that compresses keeps its segment bits at the start
+    of its slot (flag 1), any other row is stored raw (flag 0)."""
+    p, isb, n, keep = _src(x, W)
+    if not isb or n % S:
+        raise ValueError("slots need byte input of whole rows")
+    R = n // S
+    slots = np.zeros(max(n * W // 8, 1), np.uint8)
+    flags = np.zeros(max((R + 63) // 64, 1), np.uint64)
+    rc = _load().ibpo_encode_slots(p, R, W, mask, bitval, S, _ptr(slots), _ptr(flags))
+    if rc:
+        raise OracleError(rc, "encode_slots")
+    used = np.array([_load().ibpo_slot_bits(_ptr(slots), r, W, mask, S, _ptr(flags)) for r in range(R)], np.uint64)
+    return slots[: n * W // 8], flags[: (R + 63) // 64], used
+
+
+def decode_slots_gather(slots: np.ndarray, flags: np.ndarray, S: int, ids: np.ndarray, W: int, mask: int,
+                        bitval: int, out_dtype=np.uint8) -> np.ndarray:
+    """Rows ids[j] of a fixed-slot table, decoded."""
+    slots = np.ascontiguousarray(slots, np.uint8)
+    flags = np.ascontiguousarray(flags, np.uint64)
+    ids = np.ascontiguousarray(ids, np.int64)
+    R = slots.size // (S * W // 8)
+    out = np.zeros(max(ids.size * S * W // 8, 1), np.uint8)
+    rc = _load().ibpo_decode_slots_gather(_ptr(slots), R, W, mask, bitval, S, _ptr(flags), _ptr(ids), ids.size,
+                                          _ptr(out), 1)
+    if rc:
+        raise OracleError(rc, "decode_slots_gather")
+    return out[: ids.size * S * W // 8].view(out_dtype)

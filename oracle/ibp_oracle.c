@@ -338,3 +338,76 @@ int ibpo_decode_gather(const uint8_t *stream, uint64_t stream_bytes, const uint6
   }
   return IBPO_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* fixed-slot layout (Integrazione del Sistema, PCIe transfer mode)    */
+/* ------------------------------------------------------------------ */
+/*
+ * The in-place layout of the IBP page's PCIe transfer compression: every row of
+ * S chunks keeps a fixed slot of row_bytes = S*W/8 bytes (its uncompressed size)
+ * and only the used part of a slot is read.  Readings:
+ *   R8  Row r's slot starts at byte r*row_bytes.  If the row's segment encoding
+ *       (header of S participation bits, then the payloads: the same bits as a
+ *       segment of the packed stream) is shorter than S*W bits, the slot holds
+ *       those bits from its bit 0 and flag r is 1; otherwise it holds the raw row
+ *       and flag r is 0.
+ *   R9  Flags are a bit vector in 64-bit words: bit r%64 of word r/64.
+ *   R10 The used length of a compressed slot is not stored: it follows from the
+ *       header, S + sum over chunks of (participating ? W - popcount(Mask) : W).
+ * This oracle zeroes the unused tail of every slot; a reader never looks at it.
+ */
+
+/* Slots and flags of n_rows rows of S chunks (byte input, W a multiple of 8). */
+int ibpo_encode_slots(const void *src, uint64_t n_rows, unsigned W, uint64_t mask, uint64_t bitval,
+                      uint64_t S, uint8_t *slots, uint64_t *flags) {
+  if (!width_ok(W, 1) || S == 0 || (n_rows && (!src || !slots || !flags)) || !meta_ok(W, mask, bitval))
+    return IBPO_EARG;
+  const uint64_t row_bytes = S * (W / 8), row_bits = S * W, n = n_rows * S;
+  for (uint64_t w = 0; w < (n_rows + 63) / 64; ++w) flags[w] = 0;
+  for (uint64_t r = 0; r < n_rows; ++r) {
+    uint8_t *slot = slots + r * row_bytes;
+    memset(slot, 0, row_bytes);
+    uint64_t bits = segment_bits(src, 1, n, W, mask, bitval, S, r);
+    if (bits < row_bits) {
+      write_segment(slot, 0, src, 1, n, W, mask, bitval, S, r);
+      flags[r / 64] |= 1ull << (r % 64);
+    } else {
+      for (uint64_t i = 0; i < S; ++i) chunk_put(slot, 1, W, i, chunk_at(src, 1, W, r * S + i));
+    }
+  }
+  return IBPO_OK;
+}
+
+/* Used bits of slot r: from its header when compressed, else the whole row. */
+uint64_t ibpo_slot_bits(const uint8_t *slots, uint64_t r, unsigned W, uint64_t mask, uint64_t S,
+                        const uint64_t *flags) {
+  const uint8_t *slot = slots + r * S * (W / 8);
+  if (!((flags[r / 64] >> (r % 64)) & 1ull)) return S * W;
+  unsigned pc = count_set(mask, W);
+  uint64_t bits = S;
+  for (uint64_t i = 0; i < S; ++i) bits += get_bits(slot, i, 1) ? (uint64_t)(W - pc) : W;
+  return bits;
+}
+
+/* Row j of dst = row ids[j] read from its slot. */
+int ibpo_decode_slots_gather(const uint8_t *slots, uint64_t n_rows, unsigned W, uint64_t mask,
+                             uint64_t bitval, uint64_t S, const uint64_t *flags, const int64_t *ids,
+                             uint64_t n_ids, void *dst, int is_bytes) {
+  if (!width_ok(W, 1) || S == 0 || (n_ids && (!slots || !flags || !ids || !dst)) || !meta_ok(W, mask, bitval))
+    return IBPO_EARG;
+  const uint64_t row_bytes = S * (W / 8);
+  for (uint64_t j = 0; j < n_ids; ++j) {
+    int64_t id = ids[j];
+    if (id < 0 || (uint64_t)id >= n_rows) return IBPO_ESIZE;
+    const uint8_t *slot = slots + (uint64_t)id * row_bytes;
+    if ((flags[id / 64] >> (id % 64)) & 1ull) {
+      uint64_t bits = ibpo_slot_bits(slots, (uint64_t)id, W, mask, S, flags);
+      if (bits >= S * W) return IBPO_ECORRUPT;
+      int rc = read_segment(slot, 0, bits, S, W, mask, bitval, dst, is_bytes, j * S);
+      if (rc) return rc;
+    } else {
+      for (uint64_t i = 0; i < S; ++i) chunk_put(dst, is_bytes, W, j * S + i, chunk_at(slot, 1, W, i));
+    }
+  }
+  return IBPO_OK;
+}

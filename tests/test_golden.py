@@ -50,3 +50,15 @@ def test_golden_meta():
         mask, bitval, counts = oracle.build_meta(x, W, g[tk][0])
         assert counts.tolist() == g["counts"]
         assert (mask, bitval) == (g[mk][0], g[bk][0]), tk
+
+
+def test_golden_slots():
+    g = _parse("slots_w8_s4.txt")
+    W, S, mask, bitval = g["W"][0], g["S"][0], g["mask"][0], g["bitval"][0]
+    x = np.array(g["bytes"], np.uint8)
+    slots, flags, used = oracle.encode_slots(x, W, mask, bitval, S)
+    assert slots.tolist() == g["slots"]
+    assert flags.tolist() == g["flags"]
+    assert used.tolist() == g["used_bits"]
+    back = oracle.decode_slots_gather(slots, flags, S, np.array([1, 0, 1], np.int64), W, mask, bitval)
+    assert back.tolist() == g["bytes"][4:] + g["bytes"][:4] + g["bytes"][4:]

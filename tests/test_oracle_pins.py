@@ -290,3 +290,48 @@ def test_error_paths():
     with pytest.raises(oracle.OracleError) as e:
         oracle.decode_gather(stream, off, 4, np.array([3], np.int64), 32, 0xFFFFFF00, 0)
     assert e.value.rc == oracle.ESIZE
+
+
+# ---------------------------------------------------------------- fixed-slot layout
+
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (8, 5), (16, 3)])
+def test_slots_layout(W, S):
+    """Flags follow the size formula, compressed slots start with the row's segment bits,
+    raw slots hold the row verbatim, and every row reads back."""
+    rng = np.random.default_rng(W + S)
+    R = 300
+    dt = {8: np.uint8, 16: np.uint16, 32: np.uint32, 64: np.uint64}[W]
+    full = (1 << W) - 1
+    mask = (0x7C007C007C007C00 if W == 64 else 0x78000000 if W == 32 else 0xF0 if W == 8 else 0x7C00) & full
+    bitval = mask & 0x3838383838383838
+    rows = []
+    for r in range(R):
+        p_match = 0.95 if r % 3 else 0.02  # every third row almost all raw chunks
+        v = rng.integers(0, 1 << min(W, 62), size=S, dtype=np.uint64).astype(dt) if W < 64 else \
+            rng.integers(0, 1 << 62, size=S, dtype=np.uint64) * np.uint64(4) + rng.integers(0, 4, size=S, dtype=np.uint64)
+        keep = rng.random(S) < p_match
+        v[keep] = (v[keep] & dt(~mask & full)) | dt(bitval)
+        rows.append(v)
+    x = np.concatenate(rows).astype(dt)
+    slots, flags, used = oracle.encode_slots(x, W, mask, bitval, S)
+    words = x.astype(np.uint64).reshape(R, S)
+    matched = ((words ^ np.uint64(bitval)) & np.uint64(mask)) == 0
+    pc = bin(mask).count("1")
+    seg_bits = S + np.where(matched, W - pc, W).sum(axis=1)
+    want_flags = seg_bits < S * W
+    got_flags = np.array([(int(flags[r // 64]) >> (r % 64)) & 1 for r in range(R)], bool)
+    assert np.array_equal(got_flags, want_flags) and 0 < want_flags.mean() < 1
+    rb = S * W // 8
+    sl = slots.reshape(R, rb)
+    for r in range(R):
+        if want_flags[r]:
+            seg, nbits = oracle.encode_segment(x, W, mask, bitval, S, r)
+            assert int(used[r]) == nbits == seg_bits[r]
+            assert np.array_equal(np.unpackbits(sl[r], bitorder="little")[:nbits],
+                                  np.unpackbits(seg, bitorder="little")[:nbits])
+        else:
+            assert int(used[r]) == S * W
+            assert np.array_equal(sl[r], x.view(np.uint8).reshape(R, rb)[r])
+    ids = rng.integers(0, R, size=500).astype(np.int64)
+    back = oracle.decode_slots_gather(slots, flags, S, ids, W, mask, bitval, dt).reshape(500, S)
+    assert np.array_equal(back, x.reshape(R, S)[ids])
