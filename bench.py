@@ -34,7 +34,8 @@ METRIC = "IBP decompress effective GB/s (HBM- and PCIe-sourced) + compression ra
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD published
 PCIE_PEAK_GBPS = 64.0      # PCIe 5.0 x16, one direction, published link rate
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in
-                  ("ibp_device.h", "ibp_internal.h", "ibp_meta.hip", "ibp_encode.hip", "ibp_decode.hip")]
+                  ("ibp_device.h", "ibp_decode_loops.h", "ibp_internal.h", "ibp_meta.hip", "ibp_encode.hip",
+                   "ibp_decode.hip", "ibp_slots.hip")]
 
 
 def kernel_source_hash() -> str:
@@ -248,6 +249,30 @@ def main() -> int:
         extra["compress_zero_copy_host"] = {"kernel_ms": zcc_ms, "effective_GBps": U / zcc_ms / 1e6,
                                             "pcie_read_GBps": U / zcc_ms / 1e6, "pcie_write_GBps": C / zcc_ms / 1e6,
                                             "parity_ok": zc_ok}
+        # fixed-slot (in-place) layout of the same table: compress into slots in HBM,
+        # copy them to pinned host memory, gather the same rows from there
+        slots_d, flags_d = ibp.ibp_compress_slots(meta, x, S, err=err)
+        _, sc_ms = timer.run(lambda i: ibp.ibp_compress_slots(meta, x, S, slots=slots_d, flags=flags_d, err=err), 5)
+        slots_h = torch.empty(U, dtype=torch.uint8, pin_memory=True)
+        slots_h.copy_(slots_d)
+        slot_rows = torch.empty_like(out_rows)
+        sstep = lambda i: ibp.ibp_decompress_gather_slots(meta, slots_h, flags_d, S, ids_d[args.warmup + i],
+                                                          out=slot_rows, err=err)
+        sstep(0)
+        _, sg_ms = timer.run(sstep, args.steps)
+        torch.cuda.synchronize()
+        slots_ok = bool(torch.equal(slot_rows, ref_rows))
+        n_comp = int(np.unpackbits(flags_d.cpu().numpy().view(np.uint8)).sum())
+        # a slot row is read up to its used length: the segment's bits when it compresses, else the raw row
+        used = np.where(spans < S * W, (spans + 7) // 8, row_bytes)
+        sb = sum(int(used[ids].sum()) for ids in ids_all[args.warmup:]) / args.steps
+        extra["slots_pinned"] = {"effective_GBps": step_bytes / sg_ms / 1e6, "kernel_ms": sg_ms,
+                                 "pcie_read_GBps_algorithmic": sb / sg_ms / 1e6,
+                                 "fraction_of_measured_pcie": step_bytes / sg_ms / 1e6 / pcie_meas,
+                                 "speedup_vs_uncompressed": raw_ms / sg_ms, "speedup_vs_packed": h_ms / sg_ms,
+                                 "compress_kernel_ms": sc_ms, "rows_compressed": n_comp, "rows": n_rows,
+                                 "parity_ok": slots_ok}
+        del slots_d, slots_h, slot_rows
         del probe, probe_d, raw_host, zc_stream, zc_off
         # cache-compression mode: rows an HBM cache of fixed size holds, compressed vs raw
         extra["cache_mode"] = {"capacity_gain": U / (C + 8 * (nseg + 1)),
@@ -267,7 +292,7 @@ def main() -> int:
             "parity_ok": h_ok}
         del host_stream
         checks = {"roundtrip_equal": roundtrip_ok, "gather_equal": gather_ok, "pcie_gather_equal": h_ok,
-                  "zero_copy_compress_equal": zc_ok}
+                  "zero_copy_compress_equal": zc_ok, "slots_gather_equal": slots_ok}
         config = {"workload": f"{args.workload}: {w.description}", "rows": n_rows, "row_bytes": row_bytes,
                   "W": W, "T": T, "S": S, "ids_per_step": m,
                   "ids": "Zipf(1.05)" if args.workload == "dlrm" else "uniform",

@@ -11,6 +11,9 @@ have the names of the C entry points:
 * ``ibp_decompress`` -- device-resident decompression (step 3);
 * ``ibp_decompress_gather`` -- rows decoded straight from pinned host memory
   over PCIe ("Integrazione del Sistema", PCIe transfer compression);
+* ``ibp_compress_slots`` / ``ibp_decompress_gather_slots`` -- the fixed-slot
+  (in-place) layout of the PCIe transfer mode: each row keeps a slot of its raw
+  size, only the used part is read, a bit vector marks compressed rows;
 * ``ibp_gather_raw`` -- the uncompressed zero-copy gather the codec is
   measured against.
 
@@ -36,6 +39,7 @@ EXPORTS = (
     "ibp_status_str", "ibp_num_segments", "ibp_max_stream_bytes", "ibp_stream_bytes",
     "ibp_metadata_workspace_bytes", "ibp_compress_workspace_bytes", "ibp_build_metadata",
     "ibp_compress", "ibp_decompress", "ibp_decompress_gather", "ibp_gather_raw",
+    "ibp_slot_flag_words", "ibp_compress_slots", "ibp_decompress_gather_slots",
 )
 
 
@@ -86,8 +90,12 @@ def load_library() -> ctypes.CDLL:
         lib.ibp_decompress.argtypes = [_metap, _vp, _u64, _vp, _u64, _u32, _vp, _vp, _vp]
         lib.ibp_decompress_gather.argtypes = [_metap, _vp, _u64, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]
         lib.ibp_gather_raw.argtypes = [_vp, _u64, _u64, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_slot_flag_words.argtypes = [_u64]
+        lib.ibp_slot_flag_words.restype = _u64
+        lib.ibp_compress_slots.argtypes = [_metap, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_decompress_gather_slots.argtypes = [_metap, _vp, _u64, _u64, _u32, _vp, _vp, _u64, _vp, _vp, _vp]
         for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",
-                  "ibp_gather_raw"):
+                  "ibp_gather_raw", "ibp_compress_slots", "ibp_decompress_gather_slots"):
             getattr(lib, f).restype = _int
         _lib = lib
     return _lib
@@ -232,4 +240,45 @@ def ibp_gather_raw(src: torch.Tensor, row_bytes: int, ids: torch.Tensor, out: to
     rc = load_library().ibp_gather_raw(_ptr(src), row_bytes, n_rows, _ptr(ids), ids.numel(), _ptr(out),
                                        _ptr(err), _stream(stream))
     _check(rc, "ibp_gather_raw")
+    return out
+
+
+# ------------------------------------------------------------------ fixed-slot layout
+
+def ibp_slot_flag_words(n_rows: int) -> int:
+    return int(load_library().ibp_slot_flag_words(n_rows))
+
+
+def ibp_compress_slots(meta: ibp_meta_t, x: torch.Tensor, S: int, slots: torch.Tensor | None = None,
+                       flags: torch.Tensor | None = None, err: torch.Tensor | None = None,
+                       stream=None) -> tuple[torch.Tensor, torch.Tensor]:
+    """Compress the rows of x (S chunks each) into fixed slots of their raw size.
+    ``slots`` may be pinned host memory (compression in place in CPU memory).
+    Returns (slots, flags): flags is one bit per row in int64 words (1 = compressed)."""
+    row_bytes = S * meta.W // 8
+    n_rows = _nbytes(x) // row_bytes if row_bytes else 0
+    dev = _device(x)
+    if slots is None:
+        slots = torch.empty(max(n_rows * row_bytes, 16), dtype=torch.uint8, device=dev)
+    if flags is None:
+        flags = torch.empty(max(ibp_slot_flag_words(n_rows), 1), dtype=torch.int64, device=dev)
+    rc = load_library().ibp_compress_slots(ctypes.byref(meta), _ptr(x), n_rows, S, _ptr(slots), _nbytes(slots),
+                                           _ptr(flags), _ptr(err), _stream(stream))
+    _check(rc, "ibp_compress_slots")
+    return slots, flags
+
+
+def ibp_decompress_gather_slots(meta: ibp_meta_t, slots: torch.Tensor, flags: torch.Tensor, S: int,
+                                ids: torch.Tensor, n_rows: int | None = None, out: torch.Tensor | None = None,
+                                err: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row j of out = row ids[j] of a slot table; slots may be pinned host memory."""
+    row_bytes = S * meta.W // 8
+    if n_rows is None:
+        n_rows = _nbytes(slots) // row_bytes
+    if out is None:
+        out = torch.empty(ids.numel() * row_bytes, dtype=torch.uint8, device=_device(ids, flags))
+    rc = load_library().ibp_decompress_gather_slots(ctypes.byref(meta), _ptr(slots), _nbytes(slots), n_rows, S,
+                                                    _ptr(flags), _ptr(ids), ids.numel(), _ptr(out), _ptr(err),
+                                                    _stream(stream))
+    _check(rc, "ibp_decompress_gather_slots")
     return out

@@ -322,3 +322,81 @@ IBP_API int ibp_gather_raw(const void *src, uint64_t row_bytes, uint64_t n_rows,
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ fixed-slot layout
+
+extern "C" {
+
+IBP_API uint64_t ibp_slot_flag_words(uint64_t n_rows) { return (n_rows + 63) / 64; }
+
+IBP_API int ibp_compress_slots(const ibp_meta_t *meta, const void *d_in, uint64_t n_rows, uint32_t S,
+                               void *slots, uint64_t slots_bytes, uint64_t *d_flags, uint32_t *d_err_word,
+                               void *hip_stream) {
+  CodecParams p;
+  if (!make_params(meta, &p) || S == 0 || S > IBP_MAX_S) return IBP_ERR_INVALID_ARG;
+  const uint64_t row_bytes = (uint64_t)S * (p.W / 8);
+  if (row_bytes % 16) return IBP_ERR_SIZE;
+  if (n_rows && (!d_in || !slots || !d_flags)) return IBP_ERR_INVALID_ARG;
+  if (!aligned(d_in, 16) || !aligned(slots, 16) || !aligned(d_flags, 8)) return IBP_ERR_INVALID_ARG;
+  if (n_rows >= (1ull << 40)) return IBP_ERR_SIZE;
+  if (slots_bytes < n_rows * row_bytes) return IBP_ERR_CAPACITY;
+  if (n_rows == 0) return IBP_OK;
+  bool flags_host = false;
+  if (!view(d_in, n_rows * row_bytes) || !view(slots, n_rows * row_bytes) ||
+      !view(d_flags, 8 * ibp_slot_flag_words(n_rows), &flags_host) || flags_host ||
+      !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  SlotArgs a{};
+  a.in = d_in;
+  a.slots = static_cast<uint8_t *>(slots);
+  a.flags = d_flags;
+  a.err = d_err_word;
+  a.n_rows = n_rows;
+  a.n_units = n_rows;
+  a.S = S;
+  a.s_log2 = log2_if_pow2(S);
+  a.G = dec_units_per_tile(S);
+  a.row_bytes = (uint32_t)row_bytes;
+  a.img_dw = ((S * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;
+  a.wave_dw = (a.G * a.img_dw + a.G + 1 + 3) & ~3u;
+  return status_of(launch_encode_slots(a, p, static_cast<hipStream_t>(hip_stream)));
+}
+
+IBP_API int ibp_decompress_gather_slots(const ibp_meta_t *meta, const void *slots, uint64_t slots_bytes,
+                                        uint64_t n_rows, uint32_t S, const uint64_t *d_flags, const int64_t *d_ids,
+                                        uint64_t n_ids, void *d_out, uint32_t *d_err_word, void *hip_stream) {
+  CodecParams p;
+  if (!make_params(meta, &p) || S == 0 || S > IBP_MAX_S) return IBP_ERR_INVALID_ARG;
+  const uint64_t row_bytes = (uint64_t)S * (p.W / 8);
+  if (row_bytes % 16) return IBP_ERR_SIZE;
+  if (n_ids && (!slots || !d_flags || !d_ids || !d_out)) return IBP_ERR_INVALID_ARG;
+  if (!aligned(slots, 16) || !aligned(d_out, 16) || !aligned(d_flags, 8) || !aligned(d_ids, 8))
+    return IBP_ERR_INVALID_ARG;
+  if (n_rows >= (1ull << 40) || n_ids >= (1ull << 40)) return IBP_ERR_SIZE;
+  if (slots_bytes < n_rows * row_bytes) return IBP_ERR_CAPACITY;
+  if (n_ids == 0) return IBP_OK;
+  bool slots_host = false, flags_host = false;
+  if (!view(slots, n_rows * row_bytes, &slots_host) || !view(d_flags, 8 * ibp_slot_flag_words(n_rows), &flags_host) ||
+      flags_host || !view(d_ids, 8 * n_ids) || !view(d_out, n_ids * row_bytes) ||
+      !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  SlotArgs a{};
+  a.slots = static_cast<uint8_t *>(const_cast<void *>(slots));
+  a.flags = const_cast<uint64_t *>(d_flags);
+  a.ids = d_ids;
+  a.out = d_out;
+  a.err = d_err_word;
+  a.n_rows = n_rows;
+  a.n_units = n_ids;
+  a.S = S;
+  a.s_log2 = log2_if_pow2(S);
+  a.G = slots_host ? 1u : dec_units_per_tile(S);  // one row per wavefront over PCIe, as for the packed gather
+  a.row_bytes = (uint32_t)row_bytes;
+  const uint32_t row_blocks = (uint32_t)(row_bytes / 16);
+  a.img_dw = row_blocks * 4 + 4;
+  a.head_blocks = (S + 127) / 128 > (row_blocks < 4 ? row_blocks : 4) ? (S + 127) / 128 : (row_blocks < 4 ? row_blocks : 4);
+  a.wave_dw = (a.G * a.img_dw + 8 * a.G + (a.G & 1u) + 3) & ~3u;
+  return status_of(launch_decode_slots(a, p, static_cast<hipStream_t>(hip_stream)));
+}
+
+}  // extern "C"

@@ -23,20 +23,12 @@
 //  - S dividing 64: a pass holds 64/S whole segments; a ballot of the
 //    participation bits, masked to the lane's segment;
 //  - any other S: a ballot plus a per-segment carry kept in LDS.
-#include "ibp_device.h"
+#include "ibp_decode_loops.h"
 
 namespace ibp {
 namespace {
 
 using namespace dev;
-
-constexpr uint32_t kBad = 0xFFFFFFFFu;
-
-enum : uint32_t {
-  kModeGeneral = 0,  // any S
-  kModeSmallS = 1,   // 64 % S == 0: each pass holds 64/S whole segments
-  kModeLargeS = 2,   // S % 64 == 0: each pass lies inside one segment
-};
 
 // Stage the 16-byte blocks [blk0, blk0 + nb) of src into LDS at dst.  Whole
 // blocks are loaded four per lane before any is written (up to 256 loads in
@@ -61,115 +53,6 @@ __device__ __forceinline__ void stage_range(const uint8_t *src, uint64_t nbytes,
   }
   for (uint32_t j = nf + lane; j < nb; j += kWave)
     *reinterpret_cast<uint4 *>(dst + 4 * j) = load16_tail(src, nbytes, blk0 + j);
-}
-
-// S a multiple of 64: the segments of the tile one after another, 64 chunks per pass.
-template <typename T, uint32_t NR>
-__device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
-                                                   const uint32_t *lbeg, const uint32_t *lend, uint32_t nu,
-                                                   uint32_t nch, T *out, uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  const uint32_t pc = p.pc;
-  const T bitval = (T)p.bitval;
-  uint32_t err = 0;
-  for (uint32_t r = 0; r < nu; ++r) {
-    const uint32_t lb = uniform(lbeg[r]);
-    if (lb == kBad) continue;
-    const uint32_t c0 = r * a.S;
-    const uint32_t m = min(a.S, nch - c0);
-    const uint32_t pay0 = lb + m;  // first payload bit of the segment
-    uint32_t run = 0;              // compressed chunks of the segment before this pass
-    T *o = out + c0;
-    for (uint32_t q = 0; q < m; q += kWave) {
-      uint64_t H = uniform64(lds_field<uint64_t>(stg, lb + q));  // this pass's participation bits
-      if (m - q < kWave) H &= low_lanes(m - q);
-      const uint32_t i = q + lane;
-      const bool h = (H >> lane) & 1ull;
-      const uint32_t pos = pay0 + i * W - pc * (run + count_below(H));
-      const T x = lds_field<T>(stg, pos);
-      const T v = h ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
-      if (i < m) o[i] = v;
-      run += popc(H);
-    }
-    if (pay0 + m * W - pc * run != uniform(lend[r])) err |= IBP_DEVERR_CORRUPT;
-  }
-  return err;
-}
-
-// S dividing 64: each pass holds 64/S whole segments.
-template <typename T, bool kGather, uint32_t NR>
-__device__ __forceinline__ uint32_t decode_small_s(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
-                                                   const uint32_t *lbeg, const uint32_t *lend, uint32_t nch,
-                                                   T *out, uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  const uint32_t pc = p.pc;
-  const T bitval = (T)p.bitval;
-  const uint32_t i = lane & (a.S - 1u);
-  const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));  // lanes of earlier segments in the pass
-  uint32_t err = 0;
-  for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
-    const uint32_t cl = p0 + lane;
-    const bool valid = cl < nch;
-    const uint32_t r = cl >> a.s_log2;
-    const uint32_t lb = valid ? lbeg[r] : kBad;
-    const bool ok = lb != kBad;
-    uint32_t m = a.S;
-    if constexpr (!kGather) m = valid ? min(a.S, nch - (r << a.s_log2)) : a.S;
-    const bool h = ok && lds_bit(stg, lb + i);
-    const uint64_t H = ballot(h);
-    const uint32_t cnt = count_below(H) - popc(H & seg_below);
-    const uint32_t pos = ok ? lb + m + i * W - pc * cnt : 0u;
-    const T x = lds_field<T>(stg, pos);
-    const T v = h ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
-    if (ok) {
-      out[cl] = v;
-      if (i == m - 1 && pos + (h ? W - pc : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
-    }
-  }
-  return err;
-}
-
-// Any S: a segment may start anywhere in a pass and span passes; the number of
-// compressed chunks before each segment start is kept in gseg.
-template <typename T, bool kGather>
-__device__ __forceinline__ uint32_t decode_general(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
-                                                   const uint32_t *lbeg, const uint32_t *lend, uint32_t *gseg,
-                                                   uint32_t nch, T *out, uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  const uint32_t pc = p.pc;
-  const T bitval = (T)p.bitval;
-  uint32_t err = 0;
-  uint32_t running = 0;  // compressed chunks among tile chunks [0, p0)
-  for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
-    const uint32_t cl = p0 + lane;
-    const bool valid = cl < nch;
-    const uint32_t r = cl / a.S;
-    const uint32_t i = cl - r * a.S;
-    const uint32_t lb = valid ? lbeg[r] : kBad;
-    const bool ok = lb != kBad;
-    uint32_t m = a.S;
-    if constexpr (!kGather) m = valid ? min(a.S, nch - r * a.S) : a.S;
-    const bool h = ok && lds_bit(stg, lb + i);
-    const uint64_t H = ballot(h);
-    const uint32_t g_cl = running + count_below(H);
-    const uint32_t s0 = r * a.S;
-    uint32_t g_start;
-    if (s0 >= p0)
-      g_start = running + popc(H & low_lanes(s0 - p0));
-    else
-      g_start = valid ? gseg[r] : 0u;
-    if (valid && i == 0) gseg[r] = g_cl;
-    const uint32_t pos = ok ? lb + m + i * W - pc * (g_cl - g_start) : 0u;
-    const T x = lds_field<T>(stg, pos);
-    const T v = h ? (deposit_free<T, 0>(x, p.runs) | bitval) : x;
-    if (ok) {
-      out[cl] = v;
-      if (i == m - 1 && pos + (h ? W - pc : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
-    }
-    running += popc(H);
-    wave_lds_sync();
-  }
-  return err;
 }
 
 template <typename T, bool kGather, uint32_t kMode, uint32_t NR>

@@ -103,13 +103,34 @@ struct RawGatherArgs {
   uint64_t n_ids;
 };
 
+// Fixed-slot layout: row r of the table owns row_bytes bytes at slots + r * row_bytes.
+struct SlotArgs {
+  const void *in;      // compress: the raw rows
+  uint8_t *slots;      // compress: written; decompress: read (device or pinned host memory)
+  uint64_t *flags;     // 1 bit per row in 64-bit words (device memory)
+  const int64_t *ids;  // decompress: row ids
+  void *out;           // decompress: output rows
+  uint32_t *err;       // optional
+  uint64_t n_rows;     // rows in the table
+  uint64_t n_units;    // compress: n_rows; decompress: n_ids
+  uint32_t S;
+  uint32_t s_log2;
+  uint32_t G;          // rows per wavefront tile
+  uint32_t row_bytes;  // S * W / 8, a multiple of 16
+  uint32_t img_dw;     // LDS dwords per row
+  uint32_t wave_dw;    // LDS dwords per wavefront
+  uint32_t head_blocks;  // decompress: 16-byte blocks read before the header is known
+};
+
 constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;
 
-// Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip).  Each returns the hipError_t of its launch(es).
+// Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip, ibp_slots.hip).  Each returns the hipError_t of its launch(es).
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather, hipStream_t s);
 hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s);
 hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s);
+hipError_t launch_encode_slots(const SlotArgs &a, const CodecParams &p, hipStream_t s);  // ibp_slots.hip
+hipError_t launch_decode_slots(const SlotArgs &a, const CodecParams &p, hipStream_t s);
 
 }  // namespace ibp

@@ -176,6 +176,39 @@ IBP_API int ibp_decompress_gather(const ibp_meta_t *meta, const void *stream_in,
 IBP_API int ibp_gather_raw(const void *src, uint64_t row_bytes, uint64_t n_rows, const int64_t *d_ids,
                            uint64_t n_ids, void *d_out, uint32_t *d_err_word, void *hip_stream);
 
+/*
+ * Fixed-slot layout ("Integrazione del Sistema", PCIe Transfer Compression: tensors
+ * compressed in place in fixed-size buffers of which only the compressed part is
+ * read, with a bit vector in GPU memory marking the compressed ones).
+ *   Row r (S chunks, row_bytes = S*W/8, which must be a multiple of 16) owns bytes
+ *   [r*row_bytes, (r+1)*row_bytes) of `slots`.  If the row's segment encoding
+ *   (S participation bits, then the payloads: the same bits as a segment of the
+ *   packed stream) is shorter than S*W bits, the slot holds those bits from its bit
+ *   0 and bit r%64 of d_flags[r/64] is 1; otherwise the slot holds the raw row and
+ *   the bit is 0.  The used length of a compressed slot follows from its header.
+ */
+
+/* 64-bit flag words for n_rows rows: ceil(n_rows / 64). */
+IBP_API uint64_t ibp_slot_flag_words(uint64_t n_rows);
+
+/* Compress n_rows rows of d_in (device or pinned host memory, aligned to 16) into
+ * their slots (device or pinned host memory, aligned to 16, slots_bytes >=
+ * n_rows*row_bytes).  d_flags (device memory, ibp_slot_flag_words(n_rows) words)
+ * is cleared and filled.  Slot bytes after a compressed row's last 16-byte block
+ * are not written.  Asynchronous. */
+IBP_API int ibp_compress_slots(const ibp_meta_t *meta, const void *d_in, uint64_t n_rows, uint32_t S,
+                               void *slots, uint64_t slots_bytes, uint64_t *d_flags, uint32_t *d_err_word,
+                               void *hip_stream);
+
+/* Row j of d_out = row d_ids[j] of a slot table of n_rows rows (slots in pinned
+ * host memory, read zero-copy, or device memory).  Only the used part of a
+ * compressed slot is read: its header first, then the rest.  Out-of-range ids
+ * leave the row untouched and set IBP_DEVERR_BAD_ID.  Asynchronous. */
+IBP_API int ibp_decompress_gather_slots(const ibp_meta_t *meta, const void *slots, uint64_t slots_bytes,
+                                        uint64_t n_rows, uint32_t S, const uint64_t *d_flags,
+                                        const int64_t *d_ids, uint64_t n_ids, void *d_out,
+                                        uint32_t *d_err_word, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -241,3 +241,40 @@ def test_zero_copy_compress(ibp, src, dst):
     back = ibp.ibp_decompress(meta, out, comp.offsets, v.size, S, err=err)
     assert np.array_equal(back.cpu().numpy(), v.view(np.uint8))
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1024), (32, 4)])
+@pytest.mark.parametrize("where", ["device", "pinned"])
+def test_slots_parity(ibp, W, S, where):
+    """Fixed-slot layout: flags and the used prefix of every slot equal the oracle's;
+    gathers from device or pinned host slots equal the input rows."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(W * 7 + S)
+    R = 1500 if S < 1024 else 300
+    mask = 0x78000000 if W == 32 else 0x7C007C007C007C00
+    bitval = mask & 0x3838383838383838
+    rows = [_data(rng, S, W, mask, bitval, 0.97 if r % 5 else 0.02) for r in range(R)]
+    v = np.concatenate(rows)
+    meta = ibp.make_meta(W, mask, bitval)
+    x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+    row_bytes = S * W // 8
+    slots = torch.zeros(R * row_bytes, dtype=torch.uint8, device=dev) if where == "device" else \
+        torch.zeros(R * row_bytes, dtype=torch.uint8, pin_memory=True)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    say(f"slots W={W} S={S} in {where}")
+    slots, flags = ibp.ibp_compress_slots(meta, x, S, slots=slots, err=err)
+    torch.cuda.synchronize()
+    ref_slots, ref_flags, used = oracle.encode_slots(v, W, mask, bitval, S)
+    got_flags = flags.cpu().numpy().view(np.uint64)
+    assert np.array_equal(got_flags, ref_flags)
+    got = slots.cpu().numpy().reshape(R, row_bytes)
+    ref = ref_slots.reshape(R, row_bytes)
+    for r in range(R):
+        nb = (int(used[r]) + 7) // 8
+        assert np.array_equal(got[r, :nb], ref[r, :nb]), f"slot {r} differs"
+    ids_np = rng.integers(0, R, size=2049).astype(np.int64)
+    ids_np[:2] = [0, R - 1]
+    out = ibp.ibp_decompress_gather_slots(meta, slots, flags, S, torch.from_numpy(ids_np).to(dev), err=err)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(DT[W]).reshape(len(ids_np), S), v.reshape(R, S)[ids_np])
+    assert int(err.item()) == 0
