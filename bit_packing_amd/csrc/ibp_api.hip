@@ -2,7 +2,7 @@
 //
 // Every argument is checked here, on the host, before any HIP call; then the
 // launch geometry and the workspace layout are derived and the kernels in
-// ibp_kernels.hip are enqueued on the caller's stream.
+// ibp_meta.hip, ibp_encode.hip, ibp_decode.hip and ibp_slots.hip are enqueued on the caller's stream.
 #include <string.h>
 
 #include "ibp.h"
@@ -273,9 +273,11 @@ static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t
   const uint32_t tile_chunks = a.G * S;
   if (gather) {
     a.slot_dw = ((S * (p.W + 1) + 127) / 128 + 1) * 4;
+    a.sb_magic = (uint32_t)(((1ull << 32) + a.slot_dw / 4 - 1) / (a.slot_dw / 4));
     a.stage_dw = a.G * a.slot_dw + 4;
   } else {
     a.slot_dw = 0;
+    a.sb_magic = 0;
     a.stage_dw = 4 * ((tile_chunks * (p.W + 1) + 254) / 128) + 8;
   }
   uint32_t per_unit = 3 * a.G;

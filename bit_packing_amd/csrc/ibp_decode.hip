@@ -94,8 +94,27 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
     uint64_t *ufirst = reinterpret_cast<uint64_t *>(gseg + a.G + (a.G & 1u));
     uint32_t *unb = reinterpret_cast<uint32_t *>(ufirst + a.G);
     const uint64_t whole = a.stream_bytes >> 4;
-    // a. rows
+    // a. rows; for S >= 64 (G <= 8) lane r also keeps row r's first block and its
+    //    count of whole blocks in registers
     bool tail_row = false;
+    uint64_t my_first = 0;
+    uint32_t my_whole = 0;
+    // checks and descriptors of row r from its id and bit range [x, y)
+    auto describe = [&](uint32_t r, uint64_t x, uint64_t y, bool &good) {
+      if (good && !(x <= y && y <= a.stream_bytes * 8u && y - x >= a.S && y - x <= (uint64_t)a.S * (W + 1))) {
+        good = false;
+        err |= IBP_DEVERR_CORRUPT;
+      }
+      const uint32_t slot = r * a.slot_dw * 32u;
+      const uint64_t first = good ? x >> 7 : 0u;
+      const uint32_t nb = good ? (uint32_t)(((y + 127u) >> 7) - first) : 0u;
+      lbeg[r] = good ? slot + (uint32_t)(x & 127u) : kBad;
+      lend[r] = good ? slot + (uint32_t)(y - (x & ~127ull)) : kBad;
+      ufirst[r] = first;
+      unb[r] = nb;
+      tail_row |= good && first + nb > whole;
+      return first;
+    };
     for (uint32_t r = lane; r < nu; r += kWave) {
       const int64_t id = a.ids[u0 + r];
       bool good = id >= 0 && (uint64_t)id < a.nseg;
@@ -104,39 +123,70 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
       if (good) {
         x = a.off[id];
         y = a.off[id + 1];
-        const bool sane = x <= y && y <= a.stream_bytes * 8u && y - x >= a.S && y - x <= (uint64_t)a.S * (W + 1);
-        if (!sane) {
-          good = false;
-          err |= IBP_DEVERR_CORRUPT;
-        }
       }
-      const uint32_t slot = r * a.slot_dw * 32u;
-      lbeg[r] = good ? slot + (uint32_t)(x & 127u) : kBad;
-      lend[r] = good ? slot + (uint32_t)(y - (x & ~127ull)) : kBad;
-      ufirst[r] = x >> 7;
-      unb[r] = good ? (uint32_t)(((y + 127u) >> 7) - (x >> 7)) : 0u;
-      tail_row |= good && ((y + 127u) >> 7) > whole;
+      my_first = describe(r, x, y, good);
+      my_whole = my_first >= whole ? 0u : (uint32_t)min((uint64_t)unb[r], whole - my_first);
     }
     wave_lds_sync();
-    // b. stage every row into its slot: whole blocks first, all loads in flight
-    const uint32_t sb = a.slot_dw / 4u;
-    const uint32_t total = nu * sb;
-    for (uint32_t f0 = 0; f0 < total; f0 += 4 * kWave) {
-      uint4 tmp[4];
-      uint32_t dst[4];
-#pragma unroll
-      for (uint32_t u = 0; u < 4; ++u) {
-        const uint32_t f = f0 + u * kWave + lane;
-        const uint32_t r = f / sb, j = f - r * sb;
-        dst[u] = kBad;
-        if (f < total && j < unb[r] && ufirst[r] + j < whole) {
-          tmp[u] = load16(a.stream, ufirst[r] + j);
-          dst[u] = r * a.slot_dw + 4u * j;
+    // b. stage every row into its slot: whole blocks first, four loads in flight per
+    //    lane before any LDS write
+    if (a.S >= kWave) {
+      // one load instruction per (row, 64 blocks): the row's base address is scalar
+      uint32_t r = 0, j0 = 0;
+      auto item = [&](uint4 &t, uint32_t &d) {
+        d = kBad;
+        if (r >= nu) return;
+        const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
+        const uint64_t f_r = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_first >> 32), (int)r) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_first, (int)r);
+        const uint32_t j = j0 + lane;
+        if (j < n_r) {
+          t = *reinterpret_cast<const uint4 *>(a.stream + f_r * 16u + (j << 4));
+          d = r * a.slot_dw + 4u * j;
         }
+        j0 += kWave;
+        if (j0 >= n_r) {
+          j0 = 0;
+          ++r;
+        }
+      };
+      auto put = [&](const uint4 &t, uint32_t d) {
+        if (d != kBad) *reinterpret_cast<uint4 *>(stg + d) = t;
+      };
+      while (r < nu) {
+        uint4 t0, t1, t2, t3;
+        uint32_t d0, d1, d2, d3;
+        item(t0, d0);
+        item(t1, d1);
+        item(t2, d2);
+        item(t3, d3);
+        put(t0, d0);
+        put(t1, d1);
+        put(t2, d2);
+        put(t3, d3);
       }
+    } else {
+      // flat over the rows' slot blocks; row = f / sb by a multiply-high with
+      // sb_magic = ceil(2^32 / sb), exact for f, sb < 2^16
+      const uint32_t sb = a.slot_dw / 4u;
+      const uint32_t total = nu * sb;
+      for (uint32_t f0 = 0; f0 < total; f0 += 4 * kWave) {
+        uint4 tmp[4];
+        uint32_t dst[4];
 #pragma unroll
-      for (uint32_t u = 0; u < 4; ++u)
-        if (dst[u] != kBad) *reinterpret_cast<uint4 *>(stg + dst[u]) = tmp[u];
+        for (uint32_t u = 0; u < 4; ++u) {
+          const uint32_t f = f0 + u * kWave + lane;
+          const uint32_t r = __umulhi(f, a.sb_magic), j = f - __umul24(r, sb);
+          dst[u] = kBad;
+          if (f < total && j < unb[r] && ufirst[r] + j < whole) {
+            tmp[u] = load16(a.stream, ufirst[r] + j);
+            dst[u] = r * a.slot_dw + 4u * j;
+          }
+        }
+#pragma unroll
+        for (uint32_t u = 0; u < 4; ++u)
+          if (dst[u] != kBad) *reinterpret_cast<uint4 *>(stg + dst[u]) = tmp[u];
+      }
     }
     // the row that ends in the stream's last, partial block
     if (ballot(tail_row)) {

@@ -31,27 +31,28 @@ __device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const Co
   constexpr uint32_t W = sizeof(T) * 8;
   const uint32_t pc = p.pc;
   const T bitval = (T)p.bitval;
+  const uint32_t lane_bits = lane * W;
   uint32_t err = 0;
   for (uint32_t r = 0; r < nu; ++r) {
     const uint32_t lb = uniform(lbeg[r]);
     if (lb == kBad) continue;
     const uint32_t c0 = r * a.S;
     const uint32_t m = min(a.S, nch - c0);
-    const uint32_t pay0 = lb + m;  // first payload bit of the segment
-    uint32_t run = 0;              // compressed chunks of the segment before this pass
+    uint32_t run = 0;  // compressed chunks of the segment before this pass
     T *o = out + c0;
     for (uint32_t q = 0; q < m; q += kWave) {
       uint64_t H = uniform64(lds_field<uint64_t>(stg, lb + q));  // this pass's participation bits
-      if (m - q < kWave) H &= low_lanes(m - q);
-      const uint32_t i = q + lane;
-      const bool h = (H >> lane) & 1ull;
-      const uint32_t pos = pay0 + i * W - pc * (run + count_below(H));
+      const bool full = m - q >= kWave;
+      if (!full) H &= low_lanes(m - q);
+      // payload bit of chunk q + lane: the chunks before it in the segment cost W bits
+      // each, pc fewer for every compressed one (the wave-uniform part is scalar)
+      const uint32_t pos = (lb + m + q * W - pc * run) + lane_bits - __umul24(pc, count_below(H));
       const T x = lds_field<T>(stg, pos);
-      const T v = h ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
-      if (i < m) o[i] = v;
+      const T v = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
+      if (full || lane < m - q) o[q + lane] = v;
       run += popc(H);
     }
-    if (pay0 + m * W - pc * run != uniform(lend[r])) err |= IBP_DEVERR_CORRUPT;
+    if (lb + m + m * W - pc * run != uniform(lend[r])) err |= IBP_DEVERR_CORRUPT;
   }
   return err;
 }

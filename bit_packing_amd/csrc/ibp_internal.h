@@ -90,6 +90,7 @@ struct DecodeArgs {
   uint32_t G;          // units per wave tile
   uint32_t stage_dw;   // LDS staging dwords per wave
   uint32_t slot_dw;    // gather: staging dwords per row
+  uint32_t sb_magic;   // gather: ceil(2^32 / (slot_dw / 4)), for a division by the slot's block count
   uint32_t wave_dw;    // LDS dwords per wave in total
 };
 

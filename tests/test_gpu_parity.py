@@ -2,7 +2,7 @@
 
 Tolerance is 0 everywhere: the codec is lossless, so counts, Mask, Bitval, the
 offset table, every stream byte below ceil(total/8) and the round trip must
-agree exactly.  Sizes span several compression tiles (1024 chunks) and
+agree exactly.  Sizes span several compression tiles (4096 chunks) and
 decompression tiles (512 chunks per wavefront) plus ragged tails.
 """
 import numpy as np
@@ -150,6 +150,34 @@ def test_gather_parity(ibp, W, S, where):
     assert int(err.item()) == 0
 
 
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1), (32, 256)])
+def test_gather_many_ids(ibp, W, S):
+    """A gather from HBM large enough that several rounds of wavefronts run (and,
+    for S >= 64, the per-row staging path); compared with the rows themselves and,
+    for a prefix, with the oracle's decode of the same stream."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(1000 + S + W)
+    nseg = 5000
+    mask = 0xC0000000 if W == 32 else 0x7800000078000000
+    bitval = 0 if W == 32 else 0x3800000038000000
+    v = _data(rng, nseg * S, W, mask, bitval, 0.9)
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    meta = ibp.make_meta(W, mask, bitval)
+    src = torch.from_numpy(ref_stream.copy()).to(dev)
+    off = torch.from_numpy(ref_off.view(np.int64)).to(dev)
+    n_ids = max(400_000 // S, 50_000) * 4 + 13
+    ids_np = rng.integers(0, nseg, size=n_ids).astype(np.int64)
+    ids = torch.from_numpy(ids_np).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    say(f"gather W={W} S={S} ids={n_ids}")
+    rows = ibp.ibp_decompress_gather(meta, src, off, S, ids, err=err)
+    got = rows.cpu().numpy().view(DT[W]).reshape(n_ids, S)
+    assert np.array_equal(got, v.reshape(nseg, S)[ids_np])
+    ref = oracle.decode_gather(ref_stream, ref_off, S, ids_np[:2048], W, mask, bitval, np.uint8)
+    assert np.array_equal(rows[:ref.size].cpu().numpy(), ref)
+    assert int(err.item()) == 0
+
+
 def test_raw_gather(ibp):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(1)
@@ -277,4 +305,58 @@ def test_slots_parity(ibp, W, S, where):
     out = ibp.ibp_decompress_gather_slots(meta, slots, flags, S, torch.from_numpy(ids_np).to(dev), err=err)
     torch.cuda.synchronize()
     assert np.array_equal(out.cpu().numpy().view(DT[W]).reshape(len(ids_np), S), v.reshape(R, S)[ids_np])
+    assert int(err.item()) == 0
+
+
+def test_graph_replay(ibp):
+    """Compress, decompress and three gathers captured in one HIP graph.  Each of
+    several replays, with eager work, fills and synchronisations between them, must
+    reproduce the oracle's stream, offsets, round trip and gathered rows."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(77)
+    W, S, nseg = 32, 128, 2000
+    mask, bitval = 0xC0000000, 0
+    v = _data(rng, nseg * S, W, mask, bitval, 0.95)
+    n = v.size
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    nb = ref_stream.size
+    meta = ibp.make_meta(W, mask, bitval)
+    x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream_g = torch.empty(ibp.ibp_max_stream_bytes(n, W), dtype=torch.uint8, device=dev)
+    off_g = torch.empty(nseg + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(ibp.ibp_compress_workspace_bytes(n, S), dtype=torch.uint8, device=dev)
+    out_full = torch.empty_like(x)
+    ids_np = [rng.integers(0, nseg, size=m).astype(np.int64) for m in (1000, 4096, 77)]
+    ids = [torch.from_numpy(i).to(dev) for i in ids_np]
+    rows = [torch.empty(i.size * S * 4, dtype=torch.uint8, device=dev) for i in ids_np]
+    ref_rows = [oracle.decode_gather(ref_stream, ref_off, S, i, W, mask, bitval, np.uint8) for i in ids_np]
+
+    def work():
+        ibp.ibp_compress(meta, x, S, err=err, out_stream=stream_g, out_offsets=off_g, workspace=ws)
+        ibp.ibp_decompress(meta, stream_g, off_g, n, S, out=out_full, err=err)
+        for i, r in zip(ids, rows):
+            ibp.ibp_decompress_gather(meta, stream_g, off_g, S, i, out=r, err=err)
+
+    work()  # eager once before capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    other = torch.empty_like(out_full)
+    for rep in range(4):
+        say(f"graph replay {rep}")
+        for t in (stream_g, off_g, out_full, *rows):
+            t.zero_()
+        ibp.ibp_decompress(meta, torch.from_numpy(ref_stream.copy()).to(dev),
+                           torch.from_numpy(ref_off.view(np.int64)).to(dev), n, S, out=other, err=err)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(off_g.cpu().numpy().view(np.uint64), ref_off), f"replay {rep}: offsets"
+        assert np.array_equal(stream_g[:nb].cpu().numpy(), ref_stream), f"replay {rep}: stream"
+        assert torch.equal(out_full, x), f"replay {rep}: round trip"
+        for k, (r, ref) in enumerate(zip(rows, ref_rows)):
+            assert np.array_equal(r.cpu().numpy(), ref), f"replay {rep}: gather {k}"
+        assert torch.equal(other, x)
     assert int(err.item()) == 0
