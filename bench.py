@@ -66,42 +66,40 @@ def committed_traffic(kernel: str, workload: str):
 
 
 class Timer:
-    """Per-launch HIP event pairs on the launching (current) stream.
+    """HIP events over a timed region of back-to-back launches on the launching
+    (current) stream.  The launches are queued behind a short spin kernel, so the GPU
+    runs them without waiting for the host: the span from the first launch's start
+    event to the last one's end event, divided by the launch count, is the kernel's
+    average duration (plus the dispatch gap between consecutive kernels).
+    Returns (span in seconds, mean milliseconds per launch)."""
 
-    The launches are queued behind a short spin kernel, so the GPU runs them back to
-    back and each event pair brackets its kernel, not the host's time to submit it.
-    Returns (GPU time from the first launch's start to the last one's end, in
-    seconds; mean per-launch time in milliseconds)."""
-
-    def __init__(self, torch, n):
+    def __init__(self, torch):
         self.torch = torch
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
         self.spin_per_ms = None
 
     def _hold(self, ms):
         torch = self.torch
         if self.spin_per_ms is None:
-            a, b = self.ev[0]
-            a.record()
+            self.a.record()
             torch.cuda._sleep(1_000_000)
-            b.record()
+            self.b.record()
             torch.cuda.synchronize()
-            self.spin_per_ms = 1_000_000 / max(a.elapsed_time(b), 1e-3)
+            self.spin_per_ms = 1_000_000 / max(self.a.elapsed_time(self.b), 1e-3)
         torch.cuda._sleep(int(self.spin_per_ms * ms))
 
     def run(self, fn, n):
         torch = self.torch
         torch.cuda.synchronize()
         self._hold(5.0 + 0.1 * n)
+        self.a.record()
         for i in range(n):
-            a, b = self.ev[i]
-            a.record()
             fn(i)
-            b.record()
+        self.b.record()
         torch.cuda.synchronize()
-        kern = [a.elapsed_time(b) for a, b in self.ev[:n]]
-        span = self.ev[0][0].elapsed_time(self.ev[n - 1][1]) / 1e3
-        return span, sum(kern) / len(kern)
+        span_ms = self.a.elapsed_time(self.b)
+        return span_ms / 1e3, span_ms / n
 
 
 def graph_wall(torch, fn, first, k):
@@ -155,7 +153,7 @@ def main() -> int:
     x = torch.from_numpy(inst.data.reshape(-1).view(np.uint8)).to(dev)
     sample = torch.from_numpy(inst.sample.reshape(-1).view(np.uint8)).to(dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    timer = Timer(torch, max(args.steps, 20) + args.warmup)
+    timer = Timer(torch)
 
     # ---- step 1: metadata (synchronous by definition; wall time)
     meta, _ = ibp.ibp_build_metadata(sample, W, T)
