@@ -123,7 +123,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="gnn", choices=["gnn", "dlrm", "tiny", "llm", "ids", "sparse"])
+    ap.add_argument("--workload", default="gnn", choices=["gnn", "dlrm", "tiny", "llm", "ids", "sparse", "llm16"])
     ap.add_argument("--scale", type=float, default=1.0, help="shrink the workload (testing only)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")

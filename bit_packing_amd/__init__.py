@@ -162,7 +162,7 @@ def ibp_compress_workspace_bytes(n_chunks: int, S: int) -> int:
 def ibp_build_metadata(samples: torch.Tensor, W: int, T: float, stream=None,
                        workspace: torch.Tensor | None = None) -> tuple[ibp_meta_t, list[int]]:
     """(meta, per-position one-counts) of a device sample batch of W-bit chunks."""
-    n = _nbytes(samples) // (W // 8) if W in (32, 64) else 0
+    n = _nbytes(samples) // (W // 8) if W in (16, 32, 64) else 0
     if workspace is None:
         workspace = torch.empty(max(ibp_metadata_workspace_bytes(n, W), 8), dtype=torch.uint8,
                                 device=_device(samples))
@@ -190,7 +190,7 @@ def ibp_compress(meta: ibp_meta_t, x: torch.Tensor, S: int, stream=None, err: to
     """Compress the bytes of x (read as W-bit little-endian chunks) with segments of S chunks."""
     W = meta.W
     n_bytes = _nbytes(x)
-    n = n_bytes // (W // 8) if W in (32, 64) else 0
+    n = n_bytes // (W // 8) if W in (16, 32, 64) else 0
     dev = _device(x)
     if out_stream is None:
         out_stream = torch.empty(max(ibp_max_stream_bytes(n, W), 16), dtype=torch.uint8, device=dev)

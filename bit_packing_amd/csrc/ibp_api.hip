@@ -14,7 +14,7 @@ using namespace ibp;
 
 uint64_t full_bits(uint32_t W) { return W >= 64 ? ~0ull : ((1ull << W) - 1ull); }
 
-bool width_ok(uint32_t W) { return W == 32 || W == 64; }
+bool width_ok(uint32_t W) { return W == 16 || W == 32 || W == 64; }
 
 uint32_t log2_if_pow2(uint32_t S) {
   if (S == 0 || (S & (S - 1u))) return kNotPow2;

@@ -274,6 +274,7 @@ hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather,
   if (blocks > 0x7FFFFFFFull) return hipErrorInvalidValue;
   if (a.S % kWave != 0 && kWave % a.S == 0 && a.s_log2 == kNotPow2) return hipErrorInvalidValue;
   const Launch l{dim3((uint32_t)blocks), (size_t)a.wave_dw * 4 * kWavesPerBlock, s};
+  if (p.W == 16) return gather ? go_mode<uint16_t, true>(a, p, l) : go_mode<uint16_t, false>(a, p, l);
   if (p.W == 32) return gather ? go_mode<uint32_t, true>(a, p, l) : go_mode<uint32_t, false>(a, p, l);
   return gather ? go_mode<uint64_t, true>(a, p, l) : go_mode<uint64_t, false>(a, p, l);
 }

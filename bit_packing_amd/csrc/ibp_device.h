@@ -91,6 +91,11 @@ __device__ __forceinline__ uint32_t lds_bit(const uint32_t *s, uint32_t q) {
 // sizeof(T)*8 bits starting at local bit q (stream order, low bit first).
 template <typename T> __device__ __forceinline__ T lds_field(const uint32_t *s, uint32_t q);
 
+template <> __device__ __forceinline__ uint16_t lds_field<uint16_t>(const uint32_t *s, uint32_t q) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  return (uint16_t)__builtin_amdgcn_alignbit(s[d + 1], s[d], sh);
+}
+
 template <> __device__ __forceinline__ uint32_t lds_field<uint32_t>(const uint32_t *s, uint32_t q) {
   const uint32_t d = q >> 5, sh = q & 31u;
   return __builtin_amdgcn_alignbit(s[d + 1], s[d], sh);
@@ -112,6 +117,8 @@ __device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint32_t x
   if (lo) atomicOr(&s[d], lo);
   if (hi) atomicOr(&s[d + 1], hi);
 }
+
+__device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint16_t x) { lds_or_field(s, q, (uint32_t)x); }
 
 __device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint64_t x) {
   const uint32_t d = q >> 5, sh = q & 31u;

@@ -299,6 +299,7 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   if (e != hipSuccess) return e;
   const size_t shmem = (size_t)a.obuf_dw * 4 + (kEncTileChunks / kWave) * 12 + 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
+  if (p.W == 16) return launch_encode_w<uint16_t>(a, p, shmem, s);
   return p.W == 32 ? launch_encode_w<uint32_t>(a, p, shmem, s) : launch_encode_w<uint64_t>(a, p, shmem, s);
 }
 

@@ -42,7 +42,7 @@ struct Runs {
 struct CodecParams {
   uint64_t mask;
   uint64_t bitval;
-  uint32_t W;   // 32 or 64
+  uint32_t W;   // 16, 32 or 64
   uint32_t pc;  // popcount(mask)
   Runs runs;
 };

@@ -74,7 +74,9 @@ __global__ void __launch_bounds__(kBlock) meta_finish_kernel(MetaArgs a) {
 
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s) {
   if (a.n) {
-    if (a.W == 32)
+    if (a.W == 16)
+      hipLaunchKernelGGL(count_ones_kernel<uint16_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
+    else if (a.W == 32)
       hipLaunchKernelGGL(count_ones_kernel<uint32_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
     else
       hipLaunchKernelGGL(count_ones_kernel<uint64_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);

@@ -286,6 +286,7 @@ hipError_t launch_encode_slots(const SlotArgs &a, const CodecParams &p, hipStrea
   if (!ok) return hipErrorInvalidValue;
   hipError_t e = launch_zero(a.flags, (a.n_rows + 63) / 64, s);
   if (e != hipSuccess) return e;
+  if (p.W == 16) return go_enc_runs<uint16_t>(a, p, l);
   return p.W == 32 ? go_enc_runs<uint32_t>(a, p, l) : go_enc_runs<uint64_t>(a, p, l);
 }
 
@@ -295,6 +296,7 @@ hipError_t launch_decode_slots(const SlotArgs &a, const CodecParams &p, hipStrea
   const Launch l = make_launch(a, s, ok);
   if (!ok) return hipErrorInvalidValue;
   if (a.S % kWave != 0 && kWave % a.S == 0 && a.s_log2 == kNotPow2) return hipErrorInvalidValue;
+  if (p.W == 16) return go_dec_mode<uint16_t>(a, p, l);
   return p.W == 32 ? go_dec_mode<uint32_t>(a, p, l) : go_dec_mode<uint64_t>(a, p, l);
 }
 

@@ -63,7 +63,7 @@ extern "C" {
 
 typedef enum {
   IBP_OK = 0,
-  IBP_ERR_INVALID_ARG = 1, /* NULL pointer; W not 32 or 64; S == 0 or S > IBP_MAX_S;
+  IBP_ERR_INVALID_ARG = 1, /* NULL pointer; W not 16, 32 or 64; S == 0 or S > IBP_MAX_S;
                               T not in (0.5, 1]; misaligned pointer; Bitval outside Mask */
   IBP_ERR_SIZE = 2,        /* byte count not a whole number of chunks; too many chunks */
   IBP_ERR_CAPACITY = 3,    /* stream capacity or workspace below the required size */
@@ -82,7 +82,7 @@ typedef enum {
 /* Invariant-bit metadata of one dataset ("Algoritmo Core", step 1).  Only the low
  * W bits of mask and bitval are used; bitval must be 0 outside mask. */
 typedef struct {
-  uint32_t W;        /* chunk width in bits: 32 or 64 */
+  uint32_t W;        /* chunk width in bits: 16, 32 or 64 */
   uint32_t reserved; /* must be 0 */
   uint64_t mask;     /* 1 = invariant position */
   uint64_t bitval;   /* value of each invariant position, 0 elsewhere */

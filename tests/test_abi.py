@@ -77,7 +77,8 @@ def test_compress_argument_checks(ibp):
     cap = ibp.ibp_max_stream_bytes(1024, 32)
     call = lambda meta, n_bytes=4096, S=256, cap=cap, ws=ok_ws, inp=FAKE: lib.ibp_compress(
         ctypes.byref(meta), inp, n_bytes, S, FAKE, cap, FAKE, FAKE, ws, None, None)
-    assert call(_meta(ibp, W=16)) == ibp.IBP_ERR_INVALID_ARG            # W not 32/64
+    assert call(_meta(ibp, W=8, mask=0xC0)) == ibp.IBP_ERR_INVALID_ARG  # W not 16/32/64
+    assert call(_meta(ibp, W=16)) == ibp.IBP_ERR_INVALID_ARG            # Mask wider than W = 16
     assert call(_meta(ibp, reserved=1)) == ibp.IBP_ERR_INVALID_ARG      # reserved must be 0
     assert call(_meta(ibp, bitval=0x1)) == ibp.IBP_ERR_INVALID_ARG      # Bitval outside Mask
     assert call(_meta(ibp, mask=1 << 40)) == ibp.IBP_ERR_INVALID_ARG    # Mask wider than W

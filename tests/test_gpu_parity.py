@@ -13,7 +13,9 @@ import oracle
 
 pytestmark = pytest.mark.gpu
 
-DT = {32: np.uint32, 64: np.uint64}
+DT = {16: np.uint16, 32: np.uint32, 64: np.uint64}
+# an exponent-like Mask and its Bitval per width, for the gather and slot tests
+GMASK = {16: (0x7800, 0x3800), 32: (0xC0000000, 0), 64: (0x7800000078000000, 0x3800000038000000)}
 
 
 @pytest.fixture(scope="module")
@@ -31,7 +33,9 @@ def say(msg):
 
 def _data(rng, n, W, mask, bitval, p_match):
     """n W-bit chunks: random free bits; invariant bits equal Bitval with probability p_match."""
-    if W == 32:
+    if W == 16:
+        v = rng.integers(0, 1 << 16, size=n, dtype=np.uint64).astype(np.uint16)
+    elif W == 32:
         v = rng.integers(0, 1 << 32, size=n, dtype=np.uint64).astype(np.uint32)
     else:
         v = rng.integers(0, 1 << 63, size=n, dtype=np.uint64) * np.uint64(2) + \
@@ -44,7 +48,7 @@ def _data(rng, n, W, mask, bitval, p_match):
 
 def _masks(rng, W):
     full = (1 << W) - 1
-    exp = 0x78000000 if W == 32 else 0x7C007C007C007C00
+    exp = {16: 0x7C00, 32: 0x78000000, 64: 0x7C007C007C007C00}[W]
     m = int(rng.integers(0, 1 << 62)) & full
     return [
         ("zero", 0, 0),
@@ -81,7 +85,7 @@ def _run_case(ibp, dev, v, W, S, mask, bitval, tag):
     assert int(err.item()) == 0, f"{tag}: device error word {int(err.item())}"
 
 
-@pytest.mark.parametrize("W", [32, 64])
+@pytest.mark.parametrize("W", [16, 32, 64])
 @pytest.mark.parametrize("S", [1, 3, 32, 100, 128, 256, 1000, 1024])
 def test_compress_decompress_parity(ibp, W, S):
     dev = torch.device("cuda:0")
@@ -93,7 +97,7 @@ def test_compress_decompress_parity(ibp, W, S):
             _run_case(ibp, dev, _data(rng, n, W, mask, bitval, p), W, S, mask, bitval, f"{name}-{n}")
 
 
-@pytest.mark.parametrize("W", [32, 64])
+@pytest.mark.parametrize("W", [16, 32, 64])
 def test_all_invariant_and_raw_streams(ibp, W):
     """Minimum size (all chunks equal Bitval on a full Mask) and +1 bit per chunk (Mask = 0)."""
     dev = torch.device("cuda:0")
@@ -104,7 +108,7 @@ def test_all_invariant_and_raw_streams(ibp, W):
     _run_case(ibp, dev, _data(rng, 40_000, W, 0, 0, 0.0), W, 256, 0, 0, "raw")
 
 
-@pytest.mark.parametrize("W", [32, 64])
+@pytest.mark.parametrize("W", [16, 32, 64])
 @pytest.mark.parametrize("T", [0.51, 0.9, 0.99, 1.0])
 def test_metadata_parity(ibp, W, T):
     dev = torch.device("cuda:0")
@@ -112,7 +116,7 @@ def test_metadata_parity(ibp, W, T):
     for n in (1, 2, 255, 4096, 100_003, 1_500_000):
         base = _data(rng, n, W, 0, 0, 0.0)
         # bias the bits so that several positions sit near the threshold
-        bias = DT[W](rng.integers(0, 1 << 31)) if W == 32 else DT[W](rng.integers(0, 1 << 62))
+        bias = DT[W](rng.integers(0, 1 << min(W - 1, 62)))
         v = np.where(rng.random(n) < T, base & bias, base)
         say(f"metadata W={W} T={T} n={n}")
         meta, counts = ibp.ibp_build_metadata(torch.from_numpy(v.view(np.uint8).copy()).to(dev), W, T)
@@ -121,14 +125,13 @@ def test_metadata_parity(ibp, W, T):
         assert (meta.mask, meta.bitval, meta.W) == (mask, bitval, W)
 
 
-@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (64, 1), (32, 1000)])
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (64, 1), (32, 1000), (16, 128), (16, 40)])
 @pytest.mark.parametrize("where", ["device", "pinned"])
 def test_gather_parity(ibp, W, S, where):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(S + W)
     nseg = 3000
-    mask = 0xC0000000 if W == 32 else 0x7800000078000000
-    bitval = 0 if W == 32 else 0x3800000038000000
+    mask, bitval = GMASK[W]
     v = _data(rng, nseg * S, W, mask, bitval, 0.95)
     ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
     meta = ibp.make_meta(W, mask, bitval)
@@ -150,7 +153,7 @@ def test_gather_parity(ibp, W, S, where):
     assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1), (32, 256)])
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1), (32, 256), (16, 256)])
 def test_gather_many_ids(ibp, W, S):
     """A gather from HBM large enough that several rounds of wavefronts run (and,
     for S >= 64, the per-row staging path); compared with the rows themselves and,
@@ -158,8 +161,7 @@ def test_gather_many_ids(ibp, W, S):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(1000 + S + W)
     nseg = 5000
-    mask = 0xC0000000 if W == 32 else 0x7800000078000000
-    bitval = 0 if W == 32 else 0x3800000038000000
+    mask, bitval = GMASK[W]
     v = _data(rng, nseg * S, W, mask, bitval, 0.9)
     ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
     meta = ibp.make_meta(W, mask, bitval)
@@ -271,7 +273,7 @@ def test_zero_copy_compress(ibp, src, dst):
     assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1024), (32, 4)])
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1024), (32, 4), (16, 64), (16, 200)])
 @pytest.mark.parametrize("where", ["device", "pinned"])
 def test_slots_parity(ibp, W, S, where):
     """Fixed-slot layout: flags and the used prefix of every slot equal the oracle's;
@@ -279,7 +281,7 @@ def test_slots_parity(ibp, W, S, where):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(W * 7 + S)
     R = 1500 if S < 1024 else 300
-    mask = 0x78000000 if W == 32 else 0x7C007C007C007C00
+    mask = {16: 0x7C00, 32: 0x78000000, 64: 0x7C007C007C007C00}[W]
     bitval = mask & 0x3838383838383838
     rows = [_data(rng, S, W, mask, bitval, 0.97 if r % 5 else 0.02) for r in range(R)]
     v = np.concatenate(rows)

@@ -26,7 +26,7 @@ def _bits(buf: np.ndarray, a: int, b: int) -> np.ndarray:
     return np.unpackbits(chunk, bitorder="little")[a % 8:a % 8 + (b - a)]
 
 
-@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids", "sparse"])
+@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids", "sparse", "llm16"])
 def test_workload_full_size(name):
     import bit_packing_amd as ibp
 

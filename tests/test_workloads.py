@@ -57,12 +57,16 @@ EXPECTED = {
     # 95% exact zeros: every bit keeps the value 0 in >= 90% of the samples, so a zero
     # chunk costs its participation bit only: 32 / (0.95 * 1 + 0.05 * 33) = 12.31
     "sparse": (0xFFFFFFFF, 0x0, 12.31),
+    # the llm tensor one bf16 per chunk: the same exponent bits per element, matched with
+    # P = 0.97468, so 16 / (17 - 5 * 0.97468) = 1.3194 (one participation bit per element)
+    "llm16": (0x7C00, 0x3800, 1.3194),
 }
 
 
 @pytest.mark.parametrize("name", list(EXPECTED))
 def test_expected_metadata_and_ratio(name):
-    inst = workloads.generate(name, {"tiny": 1, "gnn": 0.02, "dlrm": 0.002, "llm": 0.002, "ids": 0.002, "sparse": 0.02}[name])
+    inst = workloads.generate(name, {"tiny": 1, "gnn": 0.02, "dlrm": 0.002, "llm": 0.002, "ids": 0.002, "sparse": 0.02,
+                                    "llm16": 0.002}[name])
     W = inst.w.W
     mask, bitval, _ = oracle.build_meta(inst.sample, W, inst.w.T)
     em, eb, er = EXPECTED[name]

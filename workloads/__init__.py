@@ -14,11 +14,13 @@ llm    2^30 bf16 ~ N(0,1e-3), 0.1% N(0,1) outliers 64    0.97   256   first 2^20
 ids    500,000,000 int64 ~ U[0,2^24), 5% U[0,2^40)  64    0.999  256   first 1,000,000 (before
                                                                       the 5% replacement)
 sparse 1,000,000 x 128 fp32, 95% +0, rest |N(0,1)|   32    0.9    128   10,000 distinct rows
+llm16  the llm tensor (same bytes), one bf16/chunk  16    0.97   1024  first 2^20 elements
 =====  ==========================================  ====  =====  ====  =========================
 
 The first five are the measured configurations; "sparse" is the sparse-feature
 regime of the IBP page's "Risultati" section (a GNN cache whose features are
-mostly exact zeros).  gnn, dlrm and sparse rows are one segment each (S = one row) and are read back by gathers:
+mostly exact zeros); "llm16" codes the llm tensor with one bf16 element per
+chunk (W = 16) instead of four.  gnn, dlrm and sparse rows are one segment each (S = one row) and are read back by gathers:
 65,536 uniform row ids per step (gnn) and 32,768 Zipf(1.05) row ids per step (dlrm).
 ``scale`` shrinks the row/element counts (same distributions) for CPU-sized tests.
 All randomness comes from ``gen.c`` (counter-based SplitMix64), keyed by
@@ -113,11 +115,14 @@ WORKLOADS = {
                     "int64", 0, 0),
     "sparse": Workload(6, "sparse", "Sparse GNN feature cache: 1,000,000 nodes x 128 fp32, 95% zeros, rest |N(0,1)|",
                        32, 0.9, 128, "float32", 128, 65536),
+    "llm16": Workload(7, "llm16", "LLM gradient buffer (the llm tensor) coded per element: 2^30 bf16, W=16", 16, 0.97,
+                      1024, "uint16", 0, 0),
 }
 
 FULL_SIZE = {"tiny": 262_144, "gnn": 1_000_000, "dlrm": 10_000_000, "llm": 1 << 30, "ids": 500_000_000,
-             "sparse": 1_000_000}
-SAMPLE_SIZE = {"tiny": 4096, "gnn": 10_000, "dlrm": 100_000, "llm": 1 << 20, "ids": 1_000_000, "sparse": 10_000}
+             "sparse": 1_000_000, "llm16": 1 << 30}
+SAMPLE_SIZE = {"tiny": 4096, "gnn": 10_000, "dlrm": 100_000, "llm": 1 << 20, "ids": 1_000_000, "sparse": 10_000,
+               "llm16": 1 << 20}
 
 
 @dataclass
@@ -141,8 +146,8 @@ class Instance:
 def size_at(name: str, scale: float) -> int:
     """Row count (gather workloads) or element count at a scale."""
     n = int(FULL_SIZE[name] * scale)
-    if name == "llm":
-        n -= n % 4  # whole 64-bit chunks of bf16
+    if name in ("llm", "llm16"):
+        n -= n % 4  # whole 64-bit chunks of bf16 (llm16 codes the same tensor)
     return max(n, 1 if name in ("gnn", "dlrm", "sparse") else 64)
 
 
@@ -166,9 +171,9 @@ def generate(name: str, scale: float = 1.0) -> Instance:
     elif name == "sparse":
         data = np.empty((n, w.row_elems), np.float32)
         L.gen_sparse_abs_normal_f32(k_data, data.size, 0.05, data.ctypes.data)
-    elif name == "llm":
+    elif name in ("llm", "llm16"):
         data = np.empty(n, np.uint16)
-        L.gen_bf16_grad(k_data, n, 1e-3, 1e-3, data.ctypes.data)
+        L.gen_bf16_grad(key(WORKLOADS["llm"].seed, 1), n, 1e-3, 1e-3, data.ctypes.data)
         sample = data[: min(SAMPLE_SIZE[name], n)].copy()
         return Instance(w, data, sample, None)
     elif name == "ids":
