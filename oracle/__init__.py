@@ -79,9 +79,14 @@ def _load():
         lib.ibpo_slot_bits.argtypes = [_vp, _u64, _uint, _u64, _u64, _vp]
         lib.ibpo_slot_bits.restype = _u64
         lib.ibpo_decode_slots_gather.argtypes = [_vp, _u64, _uint, _u64, _u64, _u64, _vp, _vp, _u64, _vp, _int]
+        lib.ibpo_build_meta_pos.argtypes = [_vp, _int, _u64, _uint, _u64, ctypes.c_double, _vp, _vp, _vp]
+        lib.ibpo_offsets_pos.argtypes = [_vp, _int, _u64, _uint, _vp, _vp, _u64, _vp]
+        lib.ibpo_encode_pos.argtypes = [_vp, _int, _u64, _uint, _vp, _vp, _u64, _vp, _vp, _u64]
+        lib.ibpo_decode_pos.argtypes = [_vp, _u64, _vp, _u64, _uint, _vp, _vp, _u64, _vp, _int]
         for f in ("ibpo_count_ones", "ibpo_meta_from_counts", "ibpo_build_meta", "ibpo_offsets",
                   "ibpo_encode", "ibpo_encode_segment", "ibpo_decode", "ibpo_decode_gather",
-                  "ibpo_encode_slots", "ibpo_decode_slots_gather"):
+                  "ibpo_encode_slots", "ibpo_decode_slots_gather", "ibpo_build_meta_pos",
+                  "ibpo_offsets_pos", "ibpo_encode_pos", "ibpo_decode_pos"):
             getattr(lib, f).restype = _int
         _lib = lib
     return _lib
@@ -256,3 +261,72 @@ def decode_slots_gather(slots: np.ndarray, flags: np.ndarray, S: int, ids: np.nd
     if rc:
         raise OracleError(rc, "decode_slots_gather")
     return out[: ids.size * S * W // 8].view(out_dtype)
+
+
+# ------------------------------------------------------------------ position-dependent metadata
+
+def _pos_tables(mask, bitval, S: int):
+    m = np.ascontiguousarray(np.asarray(mask, np.uint64).reshape(-1))
+    b = np.ascontiguousarray(np.asarray(bitval, np.uint64).reshape(-1))
+    if m.size != S or b.size != S:
+        raise ValueError("one Mask and one Bitval per position")
+    return m, b
+
+
+def build_meta_pos(samples: np.ndarray, W: int, S: int, T: float) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(Mask_i, Bitval_i, one-counts [S, W]) from sample rows of S chunks: position i's
+    metadata is the step-1 rule applied to the i-th chunk of every sample row."""
+    p, isb, n, keep = _src(samples, W)
+    if n % S or n == 0:
+        raise ValueError("samples must be whole rows of S chunks")
+    mask = np.zeros(S, np.uint64)
+    bitval = np.zeros(S, np.uint64)
+    c1 = np.zeros(S * W, np.uint64)
+    rc = _load().ibpo_build_meta_pos(p, isb, n // S, W, S, T, _ptr(mask), _ptr(bitval), _ptr(c1))
+    if rc:
+        raise OracleError(rc, "build_meta_pos")
+    return mask, bitval, c1.reshape(S, W)
+
+
+def offsets_pos(x: np.ndarray, W: int, mask, bitval, S: int) -> np.ndarray:
+    """Bit offset table of x when chunk position i of a segment uses Mask_i / Bitval_i."""
+    m, b = _pos_tables(mask, bitval, S)
+    p, isb, n, keep = _src(x, W)
+    off = np.zeros((n + S - 1) // S + 1, np.uint64)
+    rc = _load().ibpo_offsets_pos(p, isb, n, W, _ptr(m), _ptr(b), S, _ptr(off))
+    if rc:
+        raise OracleError(rc, "offsets_pos")
+    return off
+
+
+def encode_pos(x: np.ndarray, W: int, mask, bitval, S: int) -> tuple[np.ndarray, np.ndarray]:
+    """(stream bytes, bit offsets) of x under position-dependent metadata."""
+    m, b = _pos_tables(mask, bitval, S)
+    off = offsets_pos(x, W, m, b, S)
+    p, isb, n, keep = _src(x, W)
+    stream = np.zeros(max((int(off[-1]) + 7) // 8, 1), np.uint8)
+    rc = _load().ibpo_encode_pos(p, isb, n, W, _ptr(m), _ptr(b), S, _ptr(off), _ptr(stream), stream.size)
+    if rc:
+        raise OracleError(rc, "encode_pos")
+    return stream[: (int(off[-1]) + 7) // 8], off
+
+
+def decode_pos(stream: np.ndarray, off: np.ndarray, n: int, W: int, mask, bitval, S: int,
+               out_dtype=None) -> np.ndarray:
+    """Decompress n chunks encoded under position-dependent metadata."""
+    m, b = _pos_tables(mask, bitval, S)
+    stream = np.ascontiguousarray(stream, np.uint8)
+    off = np.ascontiguousarray(off, np.uint64)
+    if out_dtype is None or W % 8:
+        out = np.zeros(max(n, 1), np.uint64)
+        isb = 0
+    else:
+        out = np.zeros(max(n * (W // 8), 1), np.uint8)
+        isb = 1
+    rc = _load().ibpo_decode_pos(_ptr(stream) if stream.size else None, stream.size, _ptr(off), n, W, _ptr(m),
+                                 _ptr(b), S, _ptr(out), isb)
+    if rc:
+        raise OracleError(rc, "decode_pos")
+    if isb:
+        return out[: n * (W // 8)].view(out_dtype)
+    return out[:n]

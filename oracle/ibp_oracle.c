@@ -11,6 +11,10 @@
  *   step 1 "Preprocessing"   -> ibpo_count_ones, ibpo_threshold, ibpo_meta_from_counts
  *   step 2 "Compressione"    -> ibpo_offsets, ibpo_encode, ibpo_encode_segment
  *   step 3 "Decompressione"  -> ibpo_decode, ibpo_decode_gather
+ * and, from section "Integrazione del Sistema", the fixed-slot layout
+ * (ibpo_encode_slots, ibpo_decode_slots_gather), plus the position-dependent
+ * metadata variant (ibpo_build_meta_pos, ibpo_offsets_pos, ibpo_encode_pos,
+ * ibpo_decode_pos; readings R11-R13 below).
  *
  * The page fixes the idea, not a bit layout.  Where it is silent this file takes
  * these readings (the same list, with reasons, is kept in the design notes):
@@ -408,6 +412,139 @@ int ibpo_decode_slots_gather(const uint8_t *slots, uint64_t n_rows, unsigned W, 
     } else {
       for (uint64_t i = 0; i < S; ++i) chunk_put(dst, is_bytes, W, j * S + i, chunk_at(slot, 1, W, i));
     }
+  }
+  return IBPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* position-dependent metadata (Algoritmo Core, Preprocessing: a      */
+/* fixed-size metadata block "of the order of kilobytes")             */
+/* ------------------------------------------------------------------ */
+/*
+ * Variant where chunk position i inside a segment (row) has its own Mask_i and
+ * Bitval_i, i = 0 .. S-1.  Readings:
+ *   R11 A sample unit is a whole row of S chunks; the statistics of position i
+ *       are taken over the i-th chunk of every sample row, with the rule of R2
+ *       and N = number of sample rows.
+ *   R12 The stream layout is that of R4-R6: a participating chunk at position i
+ *       carries W - popcount(Mask_i) payload bits (the bits outside Mask_i).
+ *   R13 A short last segment of m < S chunks uses positions 0 .. m-1.
+ */
+
+/* Mask_i, Bitval_i (and optionally the one-counts c1[i*W + b]) from n_rows sample rows. */
+int ibpo_build_meta_pos(const void *samples, int is_bytes, uint64_t n_rows, unsigned W, uint64_t S, double T,
+                        uint64_t *mask, uint64_t *bitval, uint64_t *c1) {
+  if (!width_ok(W, is_bytes) || S == 0 || n_rows == 0 || !samples || !mask || !bitval) return IBPO_EARG;
+  for (uint64_t i = 0; i < S; ++i) {
+    uint64_t c[64] = {0};
+    for (uint64_t r = 0; r < n_rows; ++r) {
+      uint64_t v = chunk_at(samples, is_bytes, W, r * S + i);
+      for (unsigned b = 0; b < W; ++b) c[b] += bit_of(v, b);
+    }
+    int rc = ibpo_meta_from_counts(c, n_rows, W, T, &mask[i], &bitval[i]);
+    if (rc) return rc;
+    if (c1)
+      for (unsigned b = 0; b < W; ++b) c1[i * W + b] = c[b];
+  }
+  return IBPO_OK;
+}
+
+static int meta_pos_ok(unsigned W, const uint64_t *mask, const uint64_t *bitval, uint64_t S) {
+  for (uint64_t i = 0; i < S; ++i)
+    if (!meta_ok(W, mask[i], bitval[i])) return 0;
+  return 1;
+}
+
+/* Bits of segment k when position i uses Mask_i / Bitval_i (R12, R13). */
+static uint64_t segment_bits_pos(const void *src, int is_bytes, uint64_t n, unsigned W, const uint64_t *mask,
+                                 const uint64_t *bitval, uint64_t S, uint64_t k) {
+  uint64_t first = k * S, last = first + S < n ? first + S : n;
+  uint64_t bits = last - first;
+  for (uint64_t c = first; c < last; ++c) {
+    uint64_t i = c - first;
+    bits += participates(chunk_at(src, is_bytes, W, c), mask[i], bitval[i]) ? (uint64_t)(W - count_set(mask[i], W))
+                                                                            : W;
+  }
+  return bits;
+}
+
+int ibpo_offsets_pos(const void *src, int is_bytes, uint64_t n, unsigned W, const uint64_t *mask,
+                     const uint64_t *bitval, uint64_t S, uint64_t *off) {
+  if (!width_ok(W, is_bytes) || S == 0 || !off || (n && !src) || !mask || !bitval || !meta_pos_ok(W, mask, bitval, S))
+    return IBPO_EARG;
+  if (!values_ok(src, is_bytes, n, W)) return IBPO_EARG;
+  uint64_t nseg = (n + S - 1) / S;
+  off[0] = 0;
+  for (uint64_t k = 0; k < nseg; ++k) off[k + 1] = off[k] + segment_bits_pos(src, is_bytes, n, W, mask, bitval, S, k);
+  return IBPO_OK;
+}
+
+/* Segment k at stream bit q: header, then each chunk's payload under its position's metadata. */
+static uint64_t write_segment_pos(uint8_t *stream, uint64_t q, const void *src, int is_bytes, uint64_t n,
+                                  unsigned W, const uint64_t *mask, const uint64_t *bitval, uint64_t S,
+                                  uint64_t k) {
+  uint64_t first = k * S, last = first + S < n ? first + S : n;
+  for (uint64_t c = first; c < last; ++c) {
+    uint64_t i = c - first;
+    put_bits(stream, q, (uint64_t)participates(chunk_at(src, is_bytes, W, c), mask[i], bitval[i]), 1);
+    q += 1;
+  }
+  for (uint64_t c = first; c < last; ++c) {
+    uint64_t i = c - first, v = chunk_at(src, is_bytes, W, c);
+    if (participates(v, mask[i], bitval[i])) {
+      unsigned L = W - count_set(mask[i], W);
+      put_bits(stream, q, extract_bits(v, ~mask[i] & low_bits(W), W), L);
+      q += L;
+    } else {
+      put_bits(stream, q, v, W);
+      q += W;
+    }
+  }
+  return q;
+}
+
+int ibpo_encode_pos(const void *src, int is_bytes, uint64_t n, unsigned W, const uint64_t *mask,
+                    const uint64_t *bitval, uint64_t S, uint64_t *off, uint8_t *stream, uint64_t cap) {
+  int rc = ibpo_offsets_pos(src, is_bytes, n, W, mask, bitval, S, off);
+  if (rc) return rc;
+  uint64_t nseg = (n + S - 1) / S;
+  uint64_t nbytes = (off[nseg] + 7) / 8;
+  if (nbytes > cap) return IBPO_ECAP;
+  if (nbytes && !stream) return IBPO_EARG;
+  if (nbytes) memset(stream, 0, nbytes);
+  for (uint64_t k = 0; k < nseg; ++k)
+    if (write_segment_pos(stream, off[k], src, is_bytes, n, W, mask, bitval, S, k) != off[k + 1]) return IBPO_ECORRUPT;
+  return IBPO_OK;
+}
+
+/* Decode the m chunks of the segment at bits [a, b) under per-position metadata. */
+static int read_segment_pos(const uint8_t *stream, uint64_t a, uint64_t b, uint64_t m, unsigned W,
+                            const uint64_t *mask, const uint64_t *bitval, void *dst, int is_bytes, uint64_t d0) {
+  if (b < a || b - a < m) return IBPO_ECORRUPT;
+  uint64_t q = a + m;
+  for (uint64_t i = 0; i < m; ++i) {
+    unsigned p = (unsigned)get_bits(stream, a + i, 1);
+    unsigned L = p ? W - count_set(mask[i], W) : W;
+    if (q + L > b) return IBPO_ECORRUPT;
+    uint64_t x = get_bits(stream, q, L);
+    q += L;
+    chunk_put(dst, is_bytes, W, d0 + i, p ? (deposit_bits(x, ~mask[i] & low_bits(W), W) | bitval[i]) : x);
+  }
+  return q == b ? IBPO_OK : IBPO_ECORRUPT;
+}
+
+int ibpo_decode_pos(const uint8_t *stream, uint64_t stream_bytes, const uint64_t *off, uint64_t n, unsigned W,
+                    const uint64_t *mask, const uint64_t *bitval, uint64_t S, void *dst, int is_bytes) {
+  if (!width_ok(W, is_bytes) || S == 0 || !off || (n && (!dst || !stream)) || !mask || !bitval ||
+      !meta_pos_ok(W, mask, bitval, S))
+    return IBPO_EARG;
+  uint64_t nseg = (n + S - 1) / S;
+  if (off[nseg] > stream_bytes * 8) return IBPO_ECORRUPT;
+  for (uint64_t k = 0; k < nseg; ++k) {
+    uint64_t first = k * S, m = (first + S < n ? first + S : n) - first;
+    if (off[k] > off[k + 1]) return IBPO_ECORRUPT;
+    int rc = read_segment_pos(stream, off[k], off[k + 1], m, W, mask, bitval, dst, is_bytes, first);
+    if (rc) return rc;
   }
   return IBPO_OK;
 }

@@ -109,3 +109,27 @@ def spec_decode(data: bytes, offsets: list[int], n: int, W: int, mask: int, bitv
         if rest:
             raise ValueError("segment longer than its chunks")
     return out
+
+
+# ------------------------------------------------------------------ position-dependent metadata
+# Chunk i of every segment (row) has its own mask_i / bitval_i; the stream layout is unchanged.
+
+def spec_meta_pos(rows: list[list[str]], T: float) -> list[tuple[str, str]]:
+    """Per position i: spec_meta over the i-th chunk of every sample row."""
+    S = len(rows[0])
+    return [spec_meta([row[i] for row in rows], T) for i in range(S)]
+
+
+def spec_encode_pos(values: list[int], W: int, masks: list[int], bitvals: list[int], S: int) -> tuple[bytes, list[int]]:
+    chunks = [int_to_bits(v, W) for v in values]
+    ms = [int_to_bits(m, W) for m in masks]
+    bs = [int_to_bits(b, W) for b in bitvals]
+    stream = ""
+    offsets = [0]
+    for start in range(0, len(chunks), S):
+        seg = chunks[start:start + S]
+        header = "".join("1" if _matches(c, ms[i], bs[i]) else "0" for i, c in enumerate(seg))
+        payload = "".join(_free_bits(c, ms[i]) if _matches(c, ms[i], bs[i]) else c for i, c in enumerate(seg))
+        stream += header + payload
+        offsets.append(len(stream))
+    return bitstring_to_bytes(stream), offsets

@@ -62,3 +62,13 @@ def test_golden_slots():
     assert used.tolist() == g["used_bits"]
     back = oracle.decode_slots_gather(slots, flags, S, np.array([1, 0, 1], np.int64), W, mask, bitval)
     assert back.tolist() == g["bytes"][4:] + g["bytes"][:4] + g["bytes"][4:]
+
+
+def test_golden_encode_pos():
+    g = _parse("encode_pos_w4_s2.txt")
+    W, S = g["W"][0], g["S"][0]
+    x = np.array(g["values"], np.uint64)
+    stream, off = oracle.encode_pos(x, W, g["mask"], g["bitval"], S)
+    assert off.tolist() == g["offsets"]
+    assert stream.tolist() == g["stream"]
+    assert oracle.decode_pos(stream, off, x.size, W, g["mask"], g["bitval"], S).tolist() == x.tolist()

@@ -335,3 +335,114 @@ def test_slots_layout(W, S):
     ids = rng.integers(0, R, size=500).astype(np.int64)
     back = oracle.decode_slots_gather(slots, flags, S, ids, W, mask, bitval, dt).reshape(500, S)
     assert np.array_equal(back, x.reshape(R, S)[ids])
+
+
+# ------------------------------------------------------------------ position-dependent metadata
+
+from spec_bits import spec_encode_pos, spec_meta_pos  # noqa: E402
+
+
+def _pairs(W):
+    """Every (mask, bitval) with bitval inside mask, for width W."""
+    return [(m, b) for m in range(1 << W) for b in range(1 << W) if b & ~m == 0]
+
+
+@pytest.mark.parametrize("W,S,nmax", [(2, 2, 4), (1, 3, 5)])
+def test_pos_exhaustive_vs_spec(W, S, nmax):
+    """Every per-position metadata assignment and every input up to nmax chunks: the
+    oracle's stream and offsets equal the bit-string specification's, and decode back."""
+    import itertools
+    pairs = _pairs(W)
+    for combo in itertools.product(pairs, repeat=S):
+        masks = [p[0] for p in combo]
+        bitvals = [p[1] for p in combo]
+        for n in range(nmax + 1):
+            for vals in itertools.product(range(1 << W), repeat=n):
+                x = np.array(vals, np.uint64)
+                stream, off = oracle.encode_pos(x, W, masks, bitvals, S)
+                ref, ref_off = spec_encode_pos(list(vals), W, masks, bitvals, S)
+                assert off.tolist() == ref_off
+                assert bytes(stream.tolist()) == ref
+                assert oracle.decode_pos(stream, off, n, W, masks, bitvals, S).tolist() == list(vals)
+
+
+def test_pos_random_vs_spec():
+    rng = np.random.default_rng(71)
+    for _ in range(150):
+        W = int(rng.choice([3, 5, 8, 16, 31, 32, 33, 64]))
+        S = int(rng.integers(1, 7))
+        n = int(rng.integers(0, 40))
+        full = (1 << W) - 1
+        masks = [int(rng.integers(0, 1 << 62)) & full for _ in range(S)]
+        bitvals = [int(rng.integers(0, 1 << 62)) & m for m in masks]
+        vals = [int(rng.integers(0, 1 << 62)) & full for _ in range(n)]
+        # make about half the chunks match their position's invariant bits
+        vals = [(v & ~masks[i % S]) | bitvals[i % S] if rng.random() < 0.5 else v for i, v in enumerate(vals)]
+        x = np.array(vals, np.uint64)
+        stream, off = oracle.encode_pos(x, W, masks, bitvals, S)
+        ref, ref_off = spec_encode_pos(vals, W, masks, bitvals, S)
+        assert off.tolist() == ref_off and bytes(stream.tolist()) == ref
+        assert oracle.decode_pos(stream, off, n, W, masks, bitvals, S).tolist() == vals
+
+
+@pytest.mark.parametrize("W,S", [(8, 1), (8, 5), (32, 128), (64, 3)])
+def test_pos_meta_is_per_column_meta(W, S):
+    """Position i's Mask/Bitval/counts equal the single-Mask rule applied to the column
+    of i-th chunks, and equal the bit-string specification on a small case."""
+    rng = np.random.default_rng(W + S)
+    dt = {8: np.uint8, 32: np.uint32, 64: np.uint64}[W]
+    R = 501
+    base = rng.integers(0, 1 << min(W, 62), size=(R, S), dtype=np.uint64)
+    bias = rng.integers(0, 1 << min(W, 62), size=S, dtype=np.uint64)
+    keep = rng.random((R, S)) < 0.93
+    rows = np.where(keep, base & bias, base).astype(dt)
+    for T in (0.51, 0.9, 0.95):
+        masks, bitvals, c1 = oracle.build_meta_pos(rows.reshape(-1), W, S, T)
+        for i in range(S):
+            m, b, c = oracle.build_meta(np.ascontiguousarray(rows[:, i]), W, T)
+            assert (int(masks[i]), int(bitvals[i])) == (m, b)
+            assert c1[i].tolist() == c.tolist()
+    if W == 8 and S <= 5:
+        small = rows[:40]
+        strs = [[int_to_bits(int(v), W) for v in row] for row in small]
+        masks, bitvals, _ = oracle.build_meta_pos(small.reshape(-1), W, S, 0.9)
+        ref = spec_meta_pos(strs, 0.9)
+        for i in range(S):
+            assert int_to_bits(int(masks[i]), W) == ref[i][0] and int_to_bits(int(bitvals[i]), W) == ref[i][1]
+
+
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 7), (16, 33)])
+def test_pos_equal_masks_is_single_mask(W, S):
+    """With the same Mask/Bitval at every position the variant is the single-Mask codec."""
+    rng = np.random.default_rng(5 * W + S)
+    full = (1 << W) - 1
+    mask = int(rng.integers(0, 1 << 62)) & full
+    bitval = int(rng.integers(0, 1 << 62)) & mask
+    n = 50 * S + 3
+    x = rng.integers(0, 1 << 62, size=n, dtype=np.uint64) & np.uint64(full)
+    hit = rng.random(n) < 0.7
+    x[hit] = (x[hit] & np.uint64(~mask & full)) | np.uint64(bitval)
+    s1, o1 = oracle.encode(x, W, mask, bitval, S)
+    s2, o2 = oracle.encode_pos(x, W, [mask] * S, [bitval] * S, S)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+
+
+def test_pos_size_formula():
+    """total bits = n + sum over chunks of (W - [match] * popcount(Mask_position)),
+    computed here with numpy bit counts."""
+    rng = np.random.default_rng(9)
+    W, S, n = 32, 10, 12_345
+    masks = rng.integers(0, 1 << 32, size=S, dtype=np.uint64)
+    bitvals = rng.integers(0, 1 << 32, size=S, dtype=np.uint64) & masks
+    x = rng.integers(0, 1 << 32, size=n, dtype=np.uint64)
+    pos = np.arange(n) % S
+    hit = rng.random(n) < 0.6
+    x[hit] = (x[hit] & ~masks[pos[hit]] & np.uint64(0xFFFFFFFF)) | bitvals[pos[hit]]
+    match = (x & masks[pos]) == bitvals[pos]
+    pc = np.unpackbits(masks.astype(">u8").view(np.uint8)).reshape(S, 64).sum(1)
+    expect = n + int((W - match * pc[pos]).sum())
+    off = oracle.offsets_pos(x, W, masks, bitvals, S)
+    assert int(off[-1]) == expect
+    stream, off2 = oracle.encode_pos(x.astype(np.uint32), W, masks, bitvals, S)
+    assert np.array_equal(off, off2)
+    assert np.array_equal(oracle.decode_pos(stream, off, n, W, masks, bitvals, S), x)
