@@ -205,6 +205,36 @@ def main() -> int:
     roundtrip_ok = bool(torch.equal(out_full, x))
     del out_full
 
+    # ---- variant: position-dependent metadata (one Mask/Bitval per chunk position
+    # of a segment), built from the same sample taken as rows of S chunks
+    pos_ok = None
+    n_rows_sample = inst.sample.nbytes // (S * W // 8)
+    if n_rows_sample >= 1:
+        pmeta, _ = ibp.ibp_build_metadata_pos(sample[: n_rows_sample * S * W // 8], W, S, T, counts=False)
+        pstream = torch.empty(cap, dtype=torch.uint8, device=dev)
+        poff = torch.empty_like(off_d)
+        pcomp = lambda i: ibp.ibp_compress_pos(pmeta, x, err=err, out_stream=pstream, out_offsets=poff, workspace=ws)
+        pcomp(0)
+        _, pc_ms = timer.run(pcomp, creps)
+        pbits = int(poff[-1].item())
+        PC = (pbits + 7) // 8
+        pview = pstream[: ibp.ibp_stream_bytes(pbits)]
+        pout = torch.empty_like(x)
+        pdec = lambda i: ibp.ibp_decompress_pos(pmeta, pview, poff, n_chunks, out=pout, err=err)
+        pdec(0)
+        _, pd_ms = timer.run(pdec, dreps)
+        torch.cuda.synchronize()
+        pos_ok = bool(torch.equal(pout, x))
+        pm = pmeta.mask.cpu().numpy().view(np.uint64)
+        pd_alg = PC + 8 * (nseg + 1) + U
+        extra["position_metadata"] = {
+            "ratio": U / PC, "ratio_single_mask": r_stream, "positions": S, "sample_rows": n_rows_sample,
+            "positions_whose_mask_differs": int((pm != np.uint64(meta.mask)).sum()),
+            "compress_kernel_ms": pc_ms, "decompress_kernel_ms": pd_ms,
+            "decompress_algorithmic_GBps": pd_alg / pd_ms / 1e6, "hbm_fraction": pd_alg / pd_ms / 1e6 / HBM_PEAK_GBPS,
+            "parity_ok": pos_ok}
+        del pstream, pout, pview
+
     off_h = off_d.cpu().numpy().view(np.uint64)
     if gather:
         n_rows = inst.data.shape[0]
@@ -358,6 +388,8 @@ def main() -> int:
         config = {"workload": f"{args.workload}: {w.description}", "elements": int(inst.data.size),
                   "W": W, "T": T, "S": S, "source": "compressed stream resident in HBM"}
         cpu_work = ("decode", None, None)
+    if pos_ok is not None:
+        checks["position_metadata_roundtrip"] = pos_ok
     torch.cuda.synchronize()
     errword = int(err.item())
 

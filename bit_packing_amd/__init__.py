@@ -40,6 +40,7 @@ EXPORTS = (
     "ibp_metadata_workspace_bytes", "ibp_compress_workspace_bytes", "ibp_build_metadata",
     "ibp_compress", "ibp_decompress", "ibp_decompress_gather", "ibp_gather_raw",
     "ibp_slot_flag_words", "ibp_compress_slots", "ibp_decompress_gather_slots",
+    "ibp_metadata_pos_workspace_bytes", "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos",
 )
 
 
@@ -50,6 +51,25 @@ class ibp_meta_t(ctypes.Structure):
 
     def __repr__(self):
         return f"ibp_meta_t(W={self.W}, mask={self.mask:#x}, bitval={self.bitval:#x})"
+
+
+class ibp_pos_meta_t(ctypes.Structure):
+    """Position-dependent metadata: Mask_i / Bitval_i (device arrays of S words) for
+    chunk position i of every segment."""
+    _fields_ = [("W", ctypes.c_uint32), ("S", ctypes.c_uint32),
+                ("mask", ctypes.c_void_p), ("bitval", ctypes.c_void_p)]
+
+
+@dataclass
+class PosMeta:
+    """ibp_pos_meta_t plus the device tensors that hold its tables (kept alive here)."""
+    W: int
+    S: int
+    mask: torch.Tensor    # int64[S], device
+    bitval: torch.Tensor  # int64[S], device
+
+    def struct(self) -> ibp_pos_meta_t:
+        return ibp_pos_meta_t(self.W, self.S, _ptr(self.mask), _ptr(self.bitval))
 
 
 def make_meta(W: int, mask: int, bitval: int) -> ibp_meta_t:
@@ -94,8 +114,15 @@ def load_library() -> ctypes.CDLL:
         lib.ibp_slot_flag_words.restype = _u64
         lib.ibp_compress_slots.argtypes = [_metap, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]
         lib.ibp_decompress_gather_slots.argtypes = [_metap, _vp, _u64, _u64, _u32, _vp, _vp, _u64, _vp, _vp, _vp]
+        _posp = ctypes.POINTER(ibp_pos_meta_t)
+        lib.ibp_metadata_pos_workspace_bytes.argtypes = [_u32, _u32]
+        lib.ibp_metadata_pos_workspace_bytes.restype = _u64
+        lib.ibp_build_metadata_pos.argtypes = [_vp, _u64, _u32, _u32, _dbl, _vp, _vp, _vp, _vp, _u64, _vp]
+        lib.ibp_compress_pos.argtypes = [_posp, _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp, _vp]
+        lib.ibp_decompress_pos.argtypes = [_posp, _vp, _u64, _vp, _u64, _vp, _vp, _vp]
         for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",
-                  "ibp_gather_raw", "ibp_compress_slots", "ibp_decompress_gather_slots"):
+                  "ibp_gather_raw", "ibp_compress_slots", "ibp_decompress_gather_slots",
+                  "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos"):
             getattr(lib, f).restype = _int
         _lib = lib
     return _lib
@@ -281,4 +308,59 @@ def ibp_decompress_gather_slots(meta: ibp_meta_t, slots: torch.Tensor, flags: to
                                                     _ptr(flags), _ptr(ids), ids.numel(), _ptr(out), _ptr(err),
                                                     _stream(stream))
     _check(rc, "ibp_decompress_gather_slots")
+    return out
+
+
+# ------------------------------------------------------------------ position-dependent metadata
+
+def ibp_build_metadata_pos(samples: torch.Tensor, W: int, S: int, T: float, stream=None,
+                           workspace: torch.Tensor | None = None, counts: bool = True) -> tuple[PosMeta, list | None]:
+    """Mask_i / Bitval_i for the S chunk positions of a row, from device sample rows of S
+    W-bit chunks.  Returns (PosMeta with device tables, counts[S][W] or None)."""
+    n_rows = _nbytes(samples) // (S * W // 8) if W in (16, 32, 64) and S else 0
+    dev = _device(samples)
+    mask = torch.empty(max(S, 1), dtype=torch.int64, device=dev)
+    bitval = torch.empty_like(mask)
+    if workspace is None:
+        workspace = torch.empty(max(int(load_library().ibp_metadata_pos_workspace_bytes(S, W)), 8),
+                                dtype=torch.uint8, device=dev)
+    host = (ctypes.c_uint64 * (S * W))() if counts else None
+    rc = load_library().ibp_build_metadata_pos(_ptr(samples), n_rows, S, W, T, _ptr(mask), _ptr(bitval), host,
+                                               _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(rc, "ibp_build_metadata_pos")
+    cl = [[host[i * W + b] for b in range(W)] for i in range(S)] if counts else None
+    return PosMeta(W, S, mask, bitval), cl
+
+
+def ibp_compress_pos(meta: PosMeta, x: torch.Tensor, stream=None, err: torch.Tensor | None = None,
+                     out_stream: torch.Tensor | None = None, out_offsets: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> Compressed:
+    """Compress the bytes of x with position-dependent metadata (segments of meta.S chunks)."""
+    W, S = meta.W, meta.S
+    n_bytes = _nbytes(x)
+    n = n_bytes // (W // 8)
+    dev = _device(x)
+    if out_stream is None:
+        out_stream = torch.empty(max(ibp_max_stream_bytes(n, W), 16), dtype=torch.uint8, device=dev)
+    if out_offsets is None:
+        out_offsets = torch.empty(ibp_num_segments(n, S) + 1, dtype=torch.int64, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(ibp_compress_workspace_bytes(n, S), 8), dtype=torch.uint8, device=dev)
+    st = meta.struct()
+    rc = load_library().ibp_compress_pos(ctypes.byref(st), _ptr(x), n_bytes, _ptr(out_stream), _nbytes(out_stream),
+                                         _ptr(out_offsets), _ptr(workspace), _nbytes(workspace), _ptr(err),
+                                         _stream(stream))
+    _check(rc, "ibp_compress_pos")
+    return Compressed(out_stream, out_offsets, n, S, None)
+
+
+def ibp_decompress_pos(meta: PosMeta, stream_buf: torch.Tensor, offsets: torch.Tensor, n_chunks: int,
+                       out: torch.Tensor | None = None, err: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decompress n_chunks chunks encoded with position-dependent metadata."""
+    if out is None:
+        out = torch.empty(n_chunks * (meta.W // 8), dtype=torch.uint8, device=_device(offsets, stream_buf))
+    st = meta.struct()
+    rc = load_library().ibp_decompress_pos(ctypes.byref(st), _ptr(stream_buf), _nbytes(stream_buf), _ptr(offsets),
+                                           n_chunks, _ptr(out), _ptr(err), _stream(stream))
+    _check(rc, "ibp_decompress_pos")
     return out

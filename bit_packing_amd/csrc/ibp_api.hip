@@ -196,12 +196,10 @@ IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, 
   return IBP_OK;
 }
 
-IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_bytes, uint32_t S,
-                         void *d_stream, uint64_t stream_capacity, uint64_t *d_offsets,
-                         void *d_workspace, uint64_t workspace_bytes, uint32_t *d_err_word,
-                         void *hip_stream) {
-  CodecParams p;
-  if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
+static int compress_common(const CodecParams &p, const uint64_t *pmask, const uint64_t *pbitval, const void *d_in,
+                           uint64_t n_bytes, uint32_t S, void *d_stream, uint64_t stream_capacity,
+                           uint64_t *d_offsets, void *d_workspace, uint64_t workspace_bytes, uint32_t *d_err_word,
+                           void *hip_stream) {
   if (S == 0 || S > IBP_MAX_S || !d_offsets) return IBP_ERR_INVALID_ARG;
   const uint32_t cb = p.W / 8;
   if (n_bytes % cb) return IBP_ERR_SIZE;
@@ -219,6 +217,8 @@ IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_by
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (n == 0) return status_of(launch_zero(d_offsets, 1, s));  // offset table = {0}
   EncodeArgs a;
+  a.pmask = pmask;
+  a.pbitval = pbitval;
   a.in = d_in;
   a.stream = static_cast<uint32_t *>(d_stream);
   a.off = d_offsets;
@@ -237,12 +237,80 @@ IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_by
   return status_of(launch_encode(a, p, s));
 }
 
-static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
-                         const uint64_t *d_offsets, uint64_t nseg, uint32_t S, const int64_t *d_ids,
-                         uint64_t n_units, uint64_t n_chunks, void *d_out, uint32_t *d_err_word,
-                         void *hip_stream, bool gather) {
+IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_bytes, uint32_t S,
+                         void *d_stream, uint64_t stream_capacity, uint64_t *d_offsets,
+                         void *d_workspace, uint64_t workspace_bytes, uint32_t *d_err_word,
+                         void *hip_stream) {
   CodecParams p;
   if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
+  return compress_common(p, nullptr, nullptr, d_in, n_bytes, S, d_stream, stream_capacity, d_offsets, d_workspace,
+                         workspace_bytes, d_err_word, hip_stream);
+}
+
+// Position-dependent metadata: W/S checks, device tables of S words each.
+static bool pos_params(const ibp_pos_meta_t *m, CodecParams *p, const uint64_t **mask, const uint64_t **bitval) {
+  if (!m || !width_ok(m->W) || m->S == 0 || m->S > IBP_MAX_S || !m->mask || !m->bitval) return false;
+  if (!aligned(m->mask, 8) || !aligned(m->bitval, 8)) return false;
+  *mask = m->mask;
+  *bitval = m->bitval;
+  if (!view(*mask, 8ull * m->S) || !view(*bitval, 8ull * m->S)) return false;
+  memset(p, 0, sizeof(*p));
+  p->W = m->W;
+  return true;
+}
+
+IBP_API uint64_t ibp_metadata_pos_workspace_bytes(uint32_t S, uint32_t W) {
+  const uint64_t w = width_ok(W) ? W : 64;
+  return 8ull * S * w;
+}
+
+IBP_API int ibp_build_metadata_pos(const void *d_samples, uint64_t n_rows, uint32_t S, uint32_t W, double T,
+                                   uint64_t *d_mask, uint64_t *d_bitval, uint64_t *counts_out, void *d_workspace,
+                                   uint64_t workspace_bytes, void *hip_stream) {
+  if (!width_ok(W) || S == 0 || S > IBP_MAX_S || !(T > 0.5 && T <= 1.0)) return IBP_ERR_INVALID_ARG;
+  if (n_rows == 0 || !d_samples || !d_mask || !d_bitval || !d_workspace) return IBP_ERR_INVALID_ARG;
+  if (!aligned(d_samples, W / 8) || !aligned(d_mask, 8) || !aligned(d_bitval, 8) || !aligned(d_workspace, 8))
+    return IBP_ERR_INVALID_ARG;
+  if (n_rows >= (1ull << 32) || n_rows * S >= (1ull << 40)) return IBP_ERR_SIZE;
+  if (workspace_bytes < ibp_metadata_pos_workspace_bytes(S, W)) return IBP_ERR_CAPACITY;
+  if (!view(d_samples, n_rows * S * (W / 8)) || !view(d_mask, 8ull * S) || !view(d_bitval, 8ull * S) ||
+      !view(d_workspace, ibp_metadata_pos_workspace_bytes(S, W)))
+    return IBP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  MetaArgs a;
+  a.in = d_samples;
+  a.n = n_rows;
+  a.W = W;
+  a.blocks = 0;
+  a.partial = static_cast<uint64_t *>(d_workspace);
+  a.result = nullptr;
+  const uint64_t tppm = (uint64_t)(T * 1e6 + 0.5);
+  const unsigned __int128 num = (unsigned __int128)tppm * n_rows;
+  a.k = (uint64_t)((num + 999999u) / 1000000u);
+  hipError_t e = launch_meta_pos(a, S, d_mask, d_bitval, s);
+  if (e != hipSuccess) return IBP_ERR_DEVICE;
+  if (counts_out) {
+    e = hipMemcpyAsync(counts_out, a.partial, 8ull * S * W, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return IBP_ERR_DEVICE;
+  }
+  return IBP_OK;
+}
+
+IBP_API int ibp_compress_pos(const ibp_pos_meta_t *meta, const void *d_in, uint64_t n_bytes, void *d_stream,
+                             uint64_t stream_capacity, uint64_t *d_offsets, void *d_workspace,
+                             uint64_t workspace_bytes, uint32_t *d_err_word, void *hip_stream) {
+  CodecParams p;
+  const uint64_t *pm, *pb;
+  if (!pos_params(meta, &p, &pm, &pb)) return IBP_ERR_INVALID_ARG;
+  return compress_common(p, pm, pb, d_in, n_bytes, meta->S, d_stream, stream_capacity, d_offsets,
+                         d_workspace, workspace_bytes, d_err_word, hip_stream);
+}
+
+static int decode_common(const CodecParams &p, const uint64_t *pmask, const uint64_t *pbitval, const void *stream_in,
+                         uint64_t stream_bytes, const uint64_t *d_offsets, uint64_t nseg, uint32_t S,
+                         const int64_t *d_ids, uint64_t n_units, uint64_t n_chunks, void *d_out,
+                         uint32_t *d_err_word, void *hip_stream, bool gather) {
   if (S == 0 || S > IBP_MAX_S || !d_offsets) return IBP_ERR_INVALID_ARG;
   const uint32_t cb = p.W / 8;
   if (n_chunks && (!d_out || !stream_in)) return IBP_ERR_INVALID_ARG;
@@ -256,6 +324,8 @@ static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t
       !view(d_out, n_chunks * cb) || !view(d_err_word, d_err_word ? 4 : 0))
     return IBP_ERR_INVALID_ARG;
   DecodeArgs a;
+  a.pmask = pmask;
+  a.pbitval = pbitval;
   a.stream = static_cast<const uint8_t *>(stream_in);
   a.stream_bytes = stream_bytes;
   a.off = d_offsets;
@@ -283,23 +353,39 @@ static int decode_common(const ibp_meta_t *meta, const void *stream_in, uint64_t
   uint32_t per_unit = 3 * a.G;
   if (gather) per_unit += (a.G & 1u) + 3 * a.G;  // 8-byte aligned first-block table + block counts
   a.wave_dw = (a.stage_dw + per_unit + 3) & ~3u;
+  if (pmask) return status_of(launch_decode_pos(a, p, static_cast<hipStream_t>(hip_stream)));
   return status_of(launch_decode(a, p, gather, static_cast<hipStream_t>(hip_stream)));
 }
 
 IBP_API int ibp_decompress(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
                            const uint64_t *d_offsets, uint64_t n_chunks, uint32_t S, void *d_out,
                            uint32_t *d_err_word, void *hip_stream) {
+  CodecParams p;
+  if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
   const uint64_t nseg = ibp_num_segments(n_chunks, S);
-  return decode_common(meta, stream_in, stream_bytes, d_offsets, nseg, S, nullptr, nseg, n_chunks, d_out,
-                       d_err_word, hip_stream, false);
+  return decode_common(p, nullptr, nullptr, stream_in, stream_bytes, d_offsets, nseg, S, nullptr, nseg, n_chunks,
+                       d_out, d_err_word, hip_stream, false);
+}
+
+IBP_API int ibp_decompress_pos(const ibp_pos_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                               const uint64_t *d_offsets, uint64_t n_chunks, void *d_out, uint32_t *d_err_word,
+                               void *hip_stream) {
+  CodecParams p;
+  const uint64_t *pm, *pb;
+  if (!pos_params(meta, &p, &pm, &pb)) return IBP_ERR_INVALID_ARG;
+  const uint64_t nseg = ibp_num_segments(n_chunks, meta->S);
+  return decode_common(p, pm, pb, stream_in, stream_bytes, d_offsets, nseg, meta->S, nullptr, nseg,
+                       n_chunks, d_out, d_err_word, hip_stream, false);
 }
 
 IBP_API int ibp_decompress_gather(const ibp_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
                                   const uint64_t *d_offsets, uint64_t n_segments, uint32_t S,
                                   const int64_t *d_ids, uint64_t n_ids, void *d_out,
                                   uint32_t *d_err_word, void *hip_stream) {
+  CodecParams p;
+  if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
   if (S != 0 && n_ids > (1ull << 55) / S) return IBP_ERR_SIZE;
-  return decode_common(meta, stream_in, stream_bytes, d_offsets, n_segments, S, d_ids, n_ids,
+  return decode_common(p, nullptr, nullptr, stream_in, stream_bytes, d_offsets, n_segments, S, d_ids, n_ids,
                        n_ids * (uint64_t)S, d_out, d_err_word, hip_stream, true);
 }
 

@@ -40,7 +40,14 @@ enum : uint32_t {
 //     dword shared with the next tile is handed over instead of written.
 // The per-chunk prefix count has the decoder's three forms (S a multiple of 64,
 // S dividing 64, any S).
-template <typename T, uint32_t kMode, uint32_t NR>
+//
+// kPos: position-dependent metadata.  Chunk position i of a segment has its own
+// Mask_i / Bitval_i (tables in device memory, copied to LDS), so a matching chunk
+// saves popcount(Mask_i) bits instead of a constant: the count of compressed
+// chunks times popcount(Mask) becomes a prefix sum of per-chunk savings (a wave
+// scan per 64-chunk block plus a scan over the blocks), and the extraction walks
+// the runs of each lane's own free positions.
+template <typename T, uint32_t kMode, uint32_t NR, bool kPos>
 __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kQ = kEncTileChunks / kBlock;   // passes of 256 chunks
@@ -50,6 +57,11 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   uint32_t *obuf = smem;
   uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // kBal words
   uint32_t *pref = reinterpret_cast<uint32_t *>(bal + kBal);        // kBal + 1 words
+  // kPos: Mask_i / Bitval_i tables (S words each) and each chunk's inclusive prefix
+  // of saved bits within its 64-chunk block
+  uint64_t *mtab = reinterpret_cast<uint64_t *>(pref + kBal + 2);
+  uint64_t *btab = mtab + (kPos ? a.S : 0u);
+  uint16_t *wpre = reinterpret_cast<uint16_t *>(btab + (kPos ? a.S : 0u));
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_tile;
   __shared__ uint32_t s_failed;
@@ -77,17 +89,53 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   }
   for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kBlock)
     *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t ip[kQ];   // kPos: position of chunk q * kBlock + tid in its segment (tiles start on a segment)
+  uint32_t svx[kQ];  // kPos: saved bits of the earlier chunks of its 64-chunk block
+  if constexpr (kPos) {
+    const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
+    for (uint32_t i = tid; i < a.S; i += kBlock) {
+      const uint64_t m = a.pmask[i] & full;
+      mtab[i] = m;
+      btab[i] = a.pbitval[i] & m;
+    }
+    const uint32_t step = kBlock % a.S;
+    uint32_t i0 = tid % a.S;
+#pragma unroll
+    for (uint32_t q = 0; q < kQ; ++q) {
+      ip[q] = i0;
+      i0 += step;
+      if (i0 >= a.S) i0 -= a.S;
+    }
+    __syncthreads();
+  }
   uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
     const uint32_t cl = q * kBlock + tid;
-    B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
-    if (lane == 0) bal[q * kWavesPerBlock + wave] = B[q];
+    if constexpr (kPos) {
+      const uint64_t m = mtab[ip[q]];
+      const bool h = cl < nch && ((v[q] ^ (T)btab[ip[q]]) & (T)m) == 0;
+      B[q] = ballot(h);
+      // saved bits: an inclusive wave scan over the block's 64 chunks
+      const uint32_t sv = h ? popc(m) : 0u;
+      uint32_t x = sv;
+#pragma unroll
+      for (uint32_t o = 1; o < kWave; o <<= 1) {
+        const uint32_t y = __shfl_up(x, o, kWave);
+        if (lane >= o) x += y;
+      }
+      svx[q] = x - sv;
+      wpre[cl] = (uint16_t)x;
+      if (lane == kWave - 1) bal[q * kWavesPerBlock + wave] = x;  // the block's saved bits
+    } else {
+      B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
+      if (lane == 0) bal[q * kWavesPerBlock + wave] = B[q];
+    }
   }
   __syncthreads();
   // 3. compressed chunks before each 64-chunk block
   if (wave == 0) {
-    const uint32_t c = popc(bal[lane]);
+    const uint32_t c = kPos ? (uint32_t)bal[lane] : popc(bal[lane]);
     uint32_t x = c;
 #pragma unroll
     for (uint32_t o = 1; o < kWave; o <<= 1) {
@@ -103,7 +151,16 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     const uint32_t b = x >> 6, o = x & 63u;
     return pref[b] + (o ? popc(bal[b] & low_lanes(o)) : 0u);
   };
-  const uint64_t agg = (uint64_t)nch * (W + 1) - (uint64_t)pc * pref[kBal];
+  // bits saved by the matching chunks among tile chunks [0, x), any x < tile size
+  auto cost = [&](uint32_t x) -> uint32_t {
+    if constexpr (kPos) {
+      const uint32_t b = x >> 6, o = x & 63u;
+      return pref[b] + (o ? (uint32_t)wpre[x - 1] : 0u);
+    } else {
+      return pc * g(x);
+    }
+  };
+  const uint64_t agg = (uint64_t)nch * (W + 1) - (kPos ? (uint64_t)pref[kBal] : (uint64_t)pc * pref[kBal]);
 
   // decoupled look-back
   if (wave == 0) {
@@ -160,7 +217,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
 
   // 4a. segment offsets
   for (uint32_t r = tid; r < nsegt; r += kBlock)
-    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)pc * g(r * a.S);
+    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)cost(r * a.S);
   if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
 
   // 4b. pack into LDS
@@ -175,37 +232,46 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     const uint32_t cl = cb + lane;
     const bool valid = cl < nch;
     const bool h = (B[q] >> lane) & 1ull;
-    const uint32_t g_cl = uniform(pref[blk]) + count_below(B[q]);
+    // saved bits of the tile chunks before this one
+    const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : pc * (uniform(pref[blk]) + count_below(B[q]));
+    auto payload = [&]() -> T {
+      if constexpr (kPos) {
+        const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
+        return h ? extract_var<T>(v[q], ~mtab[ip[q]] & full) : v[q];
+      } else {
+        return h ? extract_free<T, NR>(v[q], p.runs) : v[q];
+      }
+    };
     uint32_t i, s0, gs;
     if constexpr (kMode == kModeLargeS) {
       s0 = (cb / a.S) * a.S;  // uniform: the block lies in one segment
       i = cl - s0;
-      gs = uniform(pref[s0 >> 6]);
+      gs = kPos ? uniform(pref[s0 >> 6]) : pc * uniform(pref[s0 >> 6]);
       const uint32_t m = min(a.S, nch - s0);
-      const uint32_t segbase = lb0 + s0 * (W + 1) - pc * gs;
+      const uint32_t segbase = lb0 + s0 * (W + 1) - gs;
       if (lane == 0) lds_or_field(obuf, segbase + (cb - s0), B[q]);  // 64 header bits
-      const uint32_t pos = segbase + m + i * W - pc * (g_cl - gs);
-      if (valid) lds_or_field(obuf, pos, h ? extract_free<T, NR>(v[q], p.runs) : v[q]);
+      const uint32_t pos = segbase + m + i * W - (c_cl - gs);
+      if (valid) lds_or_field(obuf, pos, payload());
     } else if constexpr (kMode == kModeSmallS) {
       s0 = cb + (lane & ~(a.S - 1u));
       i = i_lane;
-      gs = uniform(pref[blk]) + popc(B[q] & seg_below);
+      gs = kPos ? cost(min(s0, nch - 1u)) : pc * (uniform(pref[blk]) + popc(B[q] & seg_below));
       const uint32_t m = min(a.S, nch - min(s0, nch));
-      const uint32_t segbase = lb0 + s0 * (W + 1) - pc * gs;
+      const uint32_t segbase = lb0 + s0 * (W + 1) - gs;
       if (valid && i == 0) lds_or_field(obuf, segbase, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
-      const uint32_t pos = segbase + m + i * W - pc * (g_cl - gs);
-      if (valid) lds_or_field(obuf, pos, h ? extract_free<T, NR>(v[q], p.runs) : v[q]);
+      const uint32_t pos = segbase + m + i * W - (c_cl - gs);
+      if (valid) lds_or_field(obuf, pos, payload());
     } else {
       const uint32_t r = cl / a.S;
       s0 = r * a.S;
       i = cl - s0;
       if (valid) {
-        gs = g(s0);
+        gs = cost(s0);
         const uint32_t m = min(a.S, nch - s0);
-        const uint32_t segbase = lb0 + s0 * (W + 1) - pc * gs;
+        const uint32_t segbase = lb0 + s0 * (W + 1) - gs;
         if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
-        const uint32_t pos = segbase + m + i * W - pc * (g_cl - gs);
-        lds_or_field(obuf, pos, h ? extract_free<T, NR>(v[q], p.runs) : v[q]);
+        const uint32_t pos = segbase + m + i * W - (c_cl - gs);
+        lds_or_field(obuf, pos, payload());
       }
     }
   }
@@ -255,10 +321,17 @@ __global__ void __launch_bounds__(kBlock) zero_kernel(uint64_t *p, uint64_t n) {
 
 static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; }
 
-template <typename T, uint32_t M, uint32_t NR>
+template <typename T, uint32_t M, uint32_t NR, bool kPos = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  hipLaunchKernelGGL((encode_kernel<T, M, NR>), dim3((uint32_t)a.ntiles), dim3(kBlock), shmem, s, a, p);
+  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos>), dim3((uint32_t)a.ntiles), dim3(kBlock), shmem, s, a, p);
   return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_encode_pos_w(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
+  if (a.S % kWave == 0) return launch_encode_t<T, kModeLargeS, 0, true>(a, p, shmem, s);
+  if (kWave % a.S == 0) return launch_encode_t<T, kModeSmallS, 0, true>(a, p, shmem, s);
+  return launch_encode_t<T, kModeGeneral, 0, true>(a, p, shmem, s);
 }
 
 template <typename T, uint32_t M>
@@ -297,8 +370,15 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   // memset node, so the sequence stays valid inside a captured graph)
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
-  const size_t shmem = (size_t)a.obuf_dw * 4 + (kEncTileChunks / kWave) * 12 + 4;
+  // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
+  size_t shmem = (size_t)a.obuf_dw * 4 + (kEncTileChunks / kWave) * 8 + ((kEncTileChunks / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
+  if (a.pmask) {
+    // position tables and per-chunk saved-bit prefixes
+    shmem += (size_t)a.S * 16 + (size_t)kEncTileChunks * 2;
+    if (p.W == 16) return launch_encode_pos_w<uint16_t>(a, p, shmem, s);
+    return p.W == 32 ? launch_encode_pos_w<uint32_t>(a, p, shmem, s) : launch_encode_pos_w<uint64_t>(a, p, shmem, s);
+  }
   if (p.W == 16) return launch_encode_w<uint16_t>(a, p, shmem, s);
   return p.W == 32 ? launch_encode_w<uint32_t>(a, p, shmem, s) : launch_encode_w<uint64_t>(a, p, shmem, s);
 }

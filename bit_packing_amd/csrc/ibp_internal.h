@@ -65,6 +65,8 @@ struct EncodeArgs {
   uint64_t *tails;     // ntiles hand-over words (last partial dword of a tile)
   uint32_t *control;   // [0] tile ticket, [1] abort flag
   uint32_t *err;       // optional
+  const uint64_t *pmask;    // position-dependent metadata: Mask_i, i < S (device), else null
+  const uint64_t *pbitval;  // Bitval_i, i < S
   uint64_t n_chunks;
   uint64_t nseg;
   uint64_t ntiles;
@@ -76,6 +78,8 @@ struct EncodeArgs {
 };
 
 struct DecodeArgs {
+  const uint64_t *pmask;    // position-dependent metadata: Mask_i, i < S (device), else null
+  const uint64_t *pbitval;  // Bitval_i, i < S
   const uint8_t *stream;
   uint64_t stream_bytes;
   const uint64_t *off;
@@ -127,8 +131,10 @@ constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;
 
 // Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip, ibp_slots.hip).  Each returns the hipError_t of its launch(es).
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s);
+hipError_t launch_meta_pos(const MetaArgs &a, uint32_t S, uint64_t *d_mask, uint64_t *d_bitval, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather, hipStream_t s);
+hipError_t launch_decode_pos(const DecodeArgs &a, const CodecParams &p, hipStream_t s);
 hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s);
 hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s);
 hipError_t launch_encode_slots(const SlotArgs &a, const CodecParams &p, hipStream_t s);  // ibp_slots.hip

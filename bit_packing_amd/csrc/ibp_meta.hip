@@ -70,7 +70,67 @@ __global__ void __launch_bounds__(kBlock) meta_finish_kernel(MetaArgs a) {
   }
 }
 
+// Position-dependent metadata, step 1 per chunk position of a row: thread
+// (i, g) counts position i over sample rows g, g + RG, g + 2 RG, ... in W
+// register counters and adds them to counts[i W + b] (64-bit atomics; every
+// thread of a wavefront handles a different position or row group).
+template <typename T>
+__global__ void __launch_bounds__(kBlock) count_ones_pos_kernel(MetaArgs a, uint32_t S, uint32_t RG) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  const uint64_t t = (uint64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (t >= (uint64_t)S * RG) return;
+  const uint32_t i = (uint32_t)(t % S), g = (uint32_t)(t / S);
+  const T *in = static_cast<const T *>(a.in);
+  uint32_t c[W];
+#pragma unroll
+  for (uint32_t b = 0; b < W; ++b) c[b] = 0;
+  for (uint64_t r = g; r < a.n; r += RG) {
+    const T v = in[r * S + i];
+#pragma unroll
+    for (uint32_t b = 0; b < W; ++b) c[b] += (uint32_t)((v >> b) & 1u);
+  }
+#pragma unroll
+  for (uint32_t b = 0; b < W; ++b)
+    if (c[b]) atomicAdd(reinterpret_cast<unsigned long long *>(&a.partial[(uint64_t)i * W + b]), (unsigned long long)c[b]);
+}
+
+// One thread per position: the threshold rule over its counts gives Mask_i, Bitval_i.
+__global__ void __launch_bounds__(kBlock) meta_pos_finish_kernel(MetaArgs a, uint32_t S, uint64_t *mask,
+                                                                 uint64_t *bitval) {
+  const uint32_t i = blockIdx.x * kBlock + threadIdx.x;
+  if (i >= S) return;
+  uint64_t m = 0, bv = 0;
+  for (uint32_t b = 0; b < a.W; ++b) {
+    const uint64_t c1 = a.partial[(uint64_t)i * a.W + b], c0 = a.n - c1;
+    if ((c1 > c0 ? c1 : c0) >= a.k) {
+      m |= 1ull << b;
+      if (c1 > c0) bv |= 1ull << b;
+    }
+  }
+  mask[i] = m;
+  bitval[i] = bv;
+}
+
 }  // namespace
+
+hipError_t launch_meta_pos(const MetaArgs &a, uint32_t S, uint64_t *d_mask, uint64_t *d_bitval, hipStream_t s) {
+  hipError_t e = launch_zero(a.partial, (uint64_t)S * a.W, s);
+  if (e != hipSuccess) return e;
+  const uint64_t want = (65536u + S - 1) / S;
+  const uint32_t RG = (uint32_t)(want < a.n ? want : a.n);
+  const uint64_t threads = (uint64_t)S * RG;
+  const dim3 grid((uint32_t)((threads + kBlock - 1) / kBlock));
+  if (a.W == 16)
+    hipLaunchKernelGGL(count_ones_pos_kernel<uint16_t>, grid, dim3(kBlock), 0, s, a, S, RG);
+  else if (a.W == 32)
+    hipLaunchKernelGGL(count_ones_pos_kernel<uint32_t>, grid, dim3(kBlock), 0, s, a, S, RG);
+  else
+    hipLaunchKernelGGL(count_ones_pos_kernel<uint64_t>, grid, dim3(kBlock), 0, s, a, S, RG);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(meta_pos_finish_kernel, dim3((S + kBlock - 1) / kBlock), dim3(kBlock), 0, s, a, S, d_mask, d_bitval);
+  return hipGetLastError();
+}
 
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s) {
   if (a.n) {

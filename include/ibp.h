@@ -209,6 +209,45 @@ IBP_API int ibp_decompress_gather_slots(const ibp_meta_t *meta, const void *slot
                                         const int64_t *d_ids, uint64_t n_ids, void *d_out,
                                         uint32_t *d_err_word, void *hip_stream);
 
+/*
+ * Position-dependent metadata ("Algoritmo Core", Preprocessing: metadata of fixed
+ * size, of the order of kilobytes).  Chunk position i of every segment (row of S
+ * chunks), i < S, has its own Mask_i and Bitval_i; the stream layout is that of
+ * ibp_compress, a matching chunk at position i keeping its W - popcount(Mask_i)
+ * bits outside Mask_i.  A short last segment uses positions 0 .. m-1.
+ */
+typedef struct {
+  uint32_t W;             /* chunk width in bits: 16, 32 or 64 */
+  uint32_t S;             /* positions = chunks per segment, 1..IBP_MAX_S */
+  const uint64_t *mask;   /* device memory, S words: Mask_i (bits at or above W are ignored) */
+  const uint64_t *bitval; /* device memory, S words: Bitval_i (bits outside Mask_i are ignored) */
+} ibp_pos_meta_t;
+
+/* Workspace for ibp_build_metadata_pos: 8 * S * W bytes (the per-position counts). */
+IBP_API uint64_t ibp_metadata_pos_workspace_bytes(uint32_t S, uint32_t W);
+
+/* Step 1 per position: d_samples holds n_rows sample rows of S chunks (device,
+ * aligned to W/8); Mask_i / Bitval_i follow the rule of ibp_build_metadata over
+ * the i-th chunk of every row (N = n_rows) and are written to d_mask[i] /
+ * d_bitval[i] (device, S words each).  counts_out (host, optional): S*W uint64,
+ * counts_out[i*W + b] = rows whose chunk i has bit b set; when given, the call
+ * waits for hip_stream, otherwise it is asynchronous. */
+IBP_API int ibp_build_metadata_pos(const void *d_samples, uint64_t n_rows, uint32_t S, uint32_t W, double T,
+                                   uint64_t *d_mask, uint64_t *d_bitval, uint64_t *counts_out, void *d_workspace,
+                                   uint64_t workspace_bytes, void *hip_stream);
+
+/* Step 2 with position-dependent metadata; S = meta->S.  Arguments, sizes,
+ * workspace (ibp_compress_workspace_bytes(n, S)) and errors as ibp_compress. */
+IBP_API int ibp_compress_pos(const ibp_pos_meta_t *meta, const void *d_in, uint64_t n_bytes, void *d_stream,
+                             uint64_t stream_capacity, uint64_t *d_offsets, void *d_workspace,
+                             uint64_t workspace_bytes, uint32_t *d_err_word, void *hip_stream);
+
+/* Step 3 with position-dependent metadata; S = meta->S.  Arguments and errors as
+ * ibp_decompress. */
+IBP_API int ibp_decompress_pos(const ibp_pos_meta_t *meta, const void *stream_in, uint64_t stream_bytes,
+                               const uint64_t *d_offsets, uint64_t n_chunks, void *d_out, uint32_t *d_err_word,
+                               void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,143 @@
+"""GPU parity of the position-dependent metadata variant (one Mask/Bitval per chunk
+position of a segment) against the oracle, bit-exact: per-position counts, Masks
+and Bitvals, offsets, stream bytes and round trips, for W = 16, 32, 64 and the
+three segment-size regimes (S dividing 64, S a multiple of 64, any other S)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+pytestmark = pytest.mark.gpu
+
+DT = {16: np.uint16, 32: np.uint32, 64: np.uint64}
+
+
+@pytest.fixture(scope="module")
+def ibp():
+    import bit_packing_amd
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    bit_packing_amd.load_library()
+    return bit_packing_amd
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def _rand(rng, n, W):
+    return (rng.integers(0, 1 << 62, size=n, dtype=np.uint64) * np.uint64(4) +
+            rng.integers(0, 4, size=n, dtype=np.uint64)) & np.uint64((1 << W) - 1 if W < 64 else ~0 & (2**64 - 1))
+
+
+def _tables(rng, S, W):
+    """Per-position Masks of every kind: empty, full, one run, alternating bits, random."""
+    full = (1 << W) - 1
+    kinds = [0, full, ((1 << (W // 2)) - 1) << (W // 4), int("01" * (W // 2), 2), int("0011" * (W // 4), 2)]
+    masks = [kinds[i] if i < len(kinds) else int(rng.integers(0, 1 << 62)) & full for i in range(S)]
+    rng.shuffle(masks)
+    bitvals = [int(rng.integers(0, 1 << 62)) & m for m in masks]
+    return np.array(masks, np.uint64), np.array(bitvals, np.uint64)
+
+
+def _data(rng, n, W, masks, bitvals, S, p=0.7):
+    v = _rand(rng, n, W)
+    pos = np.arange(n) % S
+    hit = rng.random(n) < p
+    full = np.uint64((1 << W) - 1) if W < 64 else np.uint64(2**64 - 1)
+    v[hit] = (v[hit] & (~masks[pos[hit]] & full)) | bitvals[pos[hit]]
+    return v.astype(DT[W])
+
+
+def _meta(ibp, dev, W, S, masks, bitvals):
+    return ibp.PosMeta(W, S, torch.from_numpy(masks.view(np.int64)).to(dev),
+                       torch.from_numpy(bitvals.view(np.int64)).to(dev))
+
+
+@pytest.mark.parametrize("W", [16, 32, 64])
+@pytest.mark.parametrize("S", [1, 3, 32, 100, 128, 256, 1000])
+def test_pos_compress_decompress_parity(ibp, W, S):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(31 * W + S)
+    masks, bitvals = _tables(rng, S, W)
+    meta = _meta(ibp, dev, W, S, masks, bitvals)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for n in sorted({1, 63, 64, 65, max(S - 1, 1), S, S + 1, 3 * S + 7, 5000, 70_001}):
+        say(f"pos W={W} S={S} n={n}")
+        v = _data(rng, n, W, masks, bitvals, S)
+        x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+        comp = ibp.ibp_compress_pos(meta, x, err=err)
+        ref_stream, ref_off = oracle.encode_pos(v, W, masks, bitvals, S)
+        assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off), f"n={n}: offsets"
+        nb = ref_stream.size
+        got = comp.stream[:nb].cpu().numpy()
+        if not np.array_equal(got, ref_stream):
+            bad = int(np.nonzero(got != ref_stream)[0][0])
+            raise AssertionError(f"n={n}: stream differs first at byte {bad} of {nb}")
+        out = ibp.ibp_decompress_pos(meta, comp.stream, comp.offsets, n, err=err)
+        assert torch.equal(out, x), f"n={n}: round trip"
+        s2 = torch.from_numpy(ref_stream.copy()).to(dev)
+        out2 = ibp.ibp_decompress_pos(meta, s2, torch.from_numpy(ref_off.view(np.int64)).to(dev), n, err=err)
+        assert torch.equal(out2, x), f"n={n}: decode of the oracle stream"
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("W", [16, 32, 64])
+@pytest.mark.parametrize("S", [1, 5, 128, 1000])
+def test_pos_metadata_parity(ibp, W, S):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7 * W + S)
+    R = 3001
+    base = _rand(rng, R * S, W).reshape(R, S)
+    bias = _rand(rng, S, W)
+    keep = rng.random((R, S)) < 0.93
+    rows = np.where(keep, base & bias, base).astype(DT[W])
+    x = torch.from_numpy(rows.reshape(-1).view(np.uint8).copy()).to(dev)
+    for T in (0.51, 0.9, 0.95, 1.0):
+        say(f"pos metadata W={W} S={S} T={T}")
+        meta, counts = ibp.ibp_build_metadata_pos(x, W, S, T)
+        masks, bitvals, c1 = oracle.build_meta_pos(rows.reshape(-1), W, S, T)
+        assert np.array_equal(np.array(counts, np.uint64), c1)
+        assert np.array_equal(meta.mask.cpu().numpy().view(np.uint64), masks)
+        assert np.array_equal(meta.bitval.cpu().numpy().view(np.uint64), bitvals)
+
+
+def test_pos_tables_are_sanitised(ibp):
+    """Bits of Mask_i at or above W and bits of Bitval_i outside Mask_i are ignored:
+    the result equals the oracle run on the cleaned tables."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(3)
+    W, S, n = 32, 64, 20_000
+    masks, bitvals = _tables(rng, S, W)
+    v = _data(rng, n, W, masks, bitvals, S)
+    dirty_m = masks | np.uint64(0xFFFF_0000_0000_0000)
+    dirty_b = bitvals | (~masks & np.uint64(0xFFFF_FFFF))
+    meta = _meta(ibp, dev, W, S, dirty_m, dirty_b)
+    x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+    comp = ibp.ibp_compress_pos(meta, x)
+    ref_stream, ref_off = oracle.encode_pos(v, W, masks, bitvals, S)
+    assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off)
+    assert np.array_equal(comp.stream[:ref_stream.size].cpu().numpy(), ref_stream)
+    assert torch.equal(ibp.ibp_decompress_pos(meta, comp.stream, comp.offsets, n), x)
+
+
+def test_pos_corrupt_offsets_reported(ibp):
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(4)
+    W, S, n = 32, 128, 50_000
+    masks, bitvals = _tables(rng, S, W)
+    v = _data(rng, n, W, masks, bitvals, S)
+    ref_stream, ref_off = oracle.encode_pos(v, W, masks, bitvals, S)
+    bad = ref_off.copy()
+    bad[10] += 3  # segment 9 too long, segment 10 too short
+    meta = _meta(ibp, dev, W, S, masks, bitvals)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = ibp.ibp_decompress_pos(meta, torch.from_numpy(ref_stream.copy()).to(dev),
+                                 torch.from_numpy(bad.view(np.int64)).to(dev), n, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) & ibp.IBP_DEVERR_CORRUPT
+    got = out.cpu().numpy().view(np.uint32).reshape(-1)
+    # segments far from the damaged ones still decode
+    assert np.array_equal(got[:9 * S], v[:9 * S]) and np.array_equal(got[12 * S:], v[12 * S:])
