@@ -83,6 +83,11 @@ def _load():
         lib.ibpo_offsets_pos.argtypes = [_vp, _int, _u64, _uint, _vp, _vp, _u64, _vp]
         lib.ibpo_encode_pos.argtypes = [_vp, _int, _u64, _uint, _vp, _vp, _u64, _vp, _vp, _u64]
         lib.ibpo_decode_pos.argtypes = [_vp, _u64, _vp, _u64, _uint, _vp, _vp, _u64, _vp, _int]
+        lib.ibpo_zip_table.argtypes = [ctypes.c_double, _vp]
+        lib.ibpo_zip_encode.argtypes = [_vp, _u64, _vp, _vp, _vp, _vp, _vp, _u64p]
+        lib.ibpo_zip_decode.argtypes = [_vp, _vp, _vp, _u64, _vp, _u64, _vp, _vp]
+        for f in ("ibpo_zip_table", "ibpo_zip_encode", "ibpo_zip_decode"):
+            getattr(lib, f).restype = _int
         for f in ("ibpo_count_ones", "ibpo_meta_from_counts", "ibpo_build_meta", "ibpo_offsets",
                   "ibpo_encode", "ibpo_encode_segment", "ibpo_decode", "ibpo_decode_gather",
                   "ibpo_encode_slots", "ibpo_decode_slots_gather", "ibpo_build_meta_pos",
@@ -329,4 +334,50 @@ def decode_pos(stream: np.ndarray, off: np.ndarray, n: int, W: int, mask, bitval
         raise OracleError(rc, "decode_pos")
     if isb:
         return out[: n * (W // 8)].view(out_dtype)
+    return out[:n]
+
+
+# ------------------------------------------------------------------ ZipCCL exponent codec (comparison)
+
+ZIP_BLOCK = 4096
+
+
+def zip_table(sigma: float) -> np.ndarray:
+    """The 7 BF16 exponents of largest mass under N(0, sigma^2), code 1..7 order."""
+    t = np.zeros(7, np.uint8)
+    rc = _load().ibpo_zip_table(sigma, _ptr(t))
+    if rc:
+        raise OracleError(rc, "zip_table")
+    return t
+
+
+def zip_encode(x: np.ndarray, table) -> tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """(sm bytes, code planes, escape exponents, escape offsets per block) of BF16 words x."""
+    x = np.ascontiguousarray(np.asarray(x).view(np.uint16).reshape(-1))
+    t = np.ascontiguousarray(np.asarray(table, np.uint8))
+    n = x.size
+    nblk = (n + ZIP_BLOCK - 1) // ZIP_BLOCK
+    sm = np.zeros(max(n, 1), np.uint8)
+    codes = np.zeros(max(nblk * 1536, 1), np.uint8)
+    esc = np.zeros(max(n, 1), np.uint8)
+    eoff = np.zeros(nblk + 1, np.uint64)
+    ne = _u64(0)
+    rc = _load().ibpo_zip_encode(_ptr(x) if n else None, n, _ptr(t), _ptr(sm), _ptr(codes), _ptr(esc), _ptr(eoff),
+                                 ctypes.byref(ne))
+    if rc:
+        raise OracleError(rc, "zip_encode")
+    return sm[:n], codes[: nblk * 1536], esc[: ne.value], eoff
+
+
+def zip_decode(sm, codes, esc, eoff, n: int, table) -> np.ndarray:
+    sm = np.ascontiguousarray(sm, np.uint8)
+    codes = np.ascontiguousarray(codes, np.uint8)
+    esc = np.ascontiguousarray(esc, np.uint8)
+    eoff = np.ascontiguousarray(eoff, np.uint64)
+    t = np.ascontiguousarray(np.asarray(table, np.uint8))
+    out = np.zeros(max(n, 1), np.uint16)
+    rc = _load().ibpo_zip_decode(_ptr(sm) if sm.size else None, _ptr(codes) if codes.size else None,
+                                 _ptr(esc) if esc.size else None, esc.size, _ptr(eoff), n, _ptr(t), _ptr(out))
+    if rc:
+        raise OracleError(rc, "zip_decode")
     return out[:n]

@@ -14,7 +14,11 @@
  * and, from section "Integrazione del Sistema", the fixed-slot layout
  * (ibpo_encode_slots, ibpo_decode_slots_gather), plus the position-dependent
  * metadata variant (ibpo_build_meta_pos, ibpo_offsets_pos, ibpo_encode_pos,
- * ibpo_decode_pos; readings R11-R13 below).
+ * ibpo_decode_pos; readings R11-R13 below).  The comparison codec of the page
+ * "ZipCCL: Efficient Lossless Data Compression of Communication Collectives for
+ * Accelerating LLM Training" (gist.science, paper 2604.27844), section 2
+ * (Metodologia) A and B, is at the end (ibpo_zip_table, ibpo_zip_encode,
+ * ibpo_zip_decode; readings Z1-Z6).
  *
  * The page fixes the idea, not a bit layout.  Where it is silent this file takes
  * these readings (the same list, with reasons, is kept in the design notes):
@@ -545,6 +549,125 @@ int ibpo_decode_pos(const uint8_t *stream, uint64_t stream_bytes, const uint64_t
     if (off[k] > off[k + 1]) return IBPO_ECORRUPT;
     int rc = read_segment_pos(stream, off[k], off[k + 1], m, W, mask, bitval, dst, is_bytes, first);
     if (rc) return rc;
+  }
+  return IBPO_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* second codec for comparison: ZipCCL exponent coding of BF16        */
+/* (ZipCCL page, section 2 "Metodologia": A. Gaussian insight,         */
+/* B. exponent coding)                                                 */
+/* ------------------------------------------------------------------ */
+/*
+ * Readings (the page gives the idea, not a layout):
+ *   Z1 A BF16 element u (16 bits) splits into its exponent e = bits 14..7 and a
+ *      sign-mantissa byte sm = (sign << 7) | mantissa (bits 15 and 6..0).
+ *   Z2 The exponent table comes from the standard deviation sigma alone (no
+ *      histogram): under N(0, sigma^2) exponent e in 1..254 has mass
+ *      P(2^(e-127) <= |x| < 2^(e-126)), e = 0 the mass P(|x| < 2^-126), e = 255
+ *      none.  The 7 exponents of largest mass (ties: smaller e first) get codes
+ *      1..7 in decreasing order of mass.
+ *   Z3 An element whose exponent is in the table gets its code; any other gets
+ *      code 0 and its exponent goes, in element order, to the escape array.
+ *   Z4 Elements are grouped in blocks of 4096.  Block j stores its codes as three
+ *      bit planes of 4096 bits (plane p = bit p of every code, element t of the
+ *      block at plane bit t, LSB-first bytes), 1536 bytes per block, unused bits 0.
+ *   Z5 Outputs: sm[n] bytes, codes[nblk * 1536] bytes, esc[E] bytes, and
+ *      eoff[nblk + 1] = escapes before each block (eoff[nblk] = E).
+ *   Z6 Decoding: e = code ? table[code - 1] : esc[eoff[j] + rank of the element
+ *      among the block's escapes]; u = ((sm & 0x80) << 8) | (e << 7) | (sm & 0x7F).
+ */
+#define ZIP_BLOCK 4096u
+#define ZIP_PLANE_BYTES (ZIP_BLOCK / 8u)
+
+static double zip_mass(unsigned e, double sigma) {
+  /* P(a <= |x| < b) for x ~ N(0, sigma^2) = erf(b / (sigma sqrt2)) - erf(a / (sigma sqrt2)) */
+  const double s = sigma * sqrt(2.0);
+  if (e == 0) return erf(ldexp(1.0, -126) / s);
+  if (e >= 255) return 0.0;
+  return erf(ldexp(1.0, (int)e - 126) / s) - erf(ldexp(1.0, (int)e - 127) / s);
+}
+
+int ibpo_zip_table(double sigma, uint8_t table[7]) {
+  if (!(sigma > 0.0) || !table) return IBPO_EARG;
+  int used[256] = {0};
+  for (int k = 0; k < 7; ++k) {
+    int best = -1;
+    double bm = -1.0;
+    for (int e = 0; e < 256; ++e) {
+      if (used[e]) continue;
+      double m = zip_mass((unsigned)e, sigma);
+      if (m > bm) { /* strictly greater: ties keep the smaller exponent */
+        bm = m;
+        best = e;
+      }
+    }
+    used[best] = 1;
+    table[k] = (uint8_t)best;
+  }
+  return IBPO_OK;
+}
+
+static unsigned zip_code(unsigned e, const uint8_t table[7]) {
+  for (unsigned k = 0; k < 7; ++k)
+    if (table[k] == e) return k + 1;
+  return 0;
+}
+
+static int zip_table_ok(const uint8_t table[7]) {
+  for (int a = 0; a < 7; ++a)
+    for (int b = a + 1; b < 7; ++b)
+      if (table[a] == table[b]) return 0;
+  return 1;
+}
+
+/* Encode n BF16 words.  codes must hold ceil(n/4096)*1536 bytes, esc n bytes,
+ * eoff ceil(n/4096)+1 words; *n_esc receives E. */
+int ibpo_zip_encode(const uint16_t *x, uint64_t n, const uint8_t table[7], uint8_t *sm, uint8_t *codes,
+                    uint8_t *esc, uint64_t *eoff, uint64_t *n_esc) {
+  if ((n && (!x || !sm || !codes || !esc)) || !table || !eoff || !n_esc || !zip_table_ok(table)) return IBPO_EARG;
+  const uint64_t nblk = (n + ZIP_BLOCK - 1) / ZIP_BLOCK;
+  memset(codes, 0, nblk * 3 * ZIP_PLANE_BYTES);
+  uint64_t E = 0;
+  for (uint64_t j = 0; j < nblk; ++j) {
+    eoff[j] = E;
+    for (uint64_t t = 0; t < ZIP_BLOCK && j * ZIP_BLOCK + t < n; ++t) {
+      const uint64_t i = j * ZIP_BLOCK + t;
+      const unsigned u = x[i];
+      const unsigned e = (u >> 7) & 0xFFu;
+      sm[i] = (uint8_t)(((u >> 8) & 0x80u) | (u & 0x7Fu));
+      const unsigned c = zip_code(e, table);
+      for (unsigned p = 0; p < 3; ++p)
+        if ((c >> p) & 1u) codes[j * 3 * ZIP_PLANE_BYTES + p * ZIP_PLANE_BYTES + t / 8] |= (uint8_t)(1u << (t % 8));
+      if (c == 0) esc[E++] = (uint8_t)e;
+    }
+  }
+  eoff[nblk] = E;
+  *n_esc = E;
+  return IBPO_OK;
+}
+
+int ibpo_zip_decode(const uint8_t *sm, const uint8_t *codes, const uint8_t *esc, uint64_t n_esc, const uint64_t *eoff,
+                    uint64_t n, const uint8_t table[7], uint16_t *out) {
+  if ((n && (!sm || !codes || !out || !eoff)) || !table || !zip_table_ok(table)) return IBPO_EARG;
+  const uint64_t nblk = (n + ZIP_BLOCK - 1) / ZIP_BLOCK;
+  for (uint64_t j = 0; j < nblk; ++j) {
+    uint64_t k = eoff[j];
+    for (uint64_t t = 0; t < ZIP_BLOCK && j * ZIP_BLOCK + t < n; ++t) {
+      const uint64_t i = j * ZIP_BLOCK + t;
+      unsigned c = 0;
+      for (unsigned p = 0; p < 3; ++p)
+        c |= (unsigned)((codes[j * 3 * ZIP_PLANE_BYTES + p * ZIP_PLANE_BYTES + t / 8] >> (t % 8)) & 1u) << p;
+      unsigned e;
+      if (c) {
+        e = table[c - 1];
+      } else {
+        if (k >= n_esc || !esc) return IBPO_ECORRUPT;
+        e = esc[k++];
+      }
+      out[i] = (uint16_t)(((sm[i] & 0x80u) << 8) | (e << 7) | (sm[i] & 0x7Fu));
+    }
+    if (k != eoff[j + 1]) return IBPO_ECORRUPT;
   }
   return IBPO_OK;
 }

@@ -72,3 +72,15 @@ def test_golden_encode_pos():
     assert off.tolist() == g["offsets"]
     assert stream.tolist() == g["stream"]
     assert oracle.decode_pos(stream, off, x.size, W, g["mask"], g["bitval"], S).tolist() == x.tolist()
+
+
+def test_golden_zip():
+    g = _parse("zip_bf16.txt")
+    x = np.array(g["values"], np.uint16)
+    sm, codes, esc, eoff = oracle.zip_encode(x, g["table"])
+    assert sm.tolist() == g["sm"]
+    assert codes.size == 1536
+    assert (codes[0], codes[512], codes[1024]) == (g["plane0"][0], g["plane1"][0], g["plane2"][0])
+    assert not codes[1:512].any() and not codes[513:1024].any() and not codes[1025:].any()
+    assert esc.tolist() == g["esc"] and eoff.tolist() == g["eoff"]
+    assert oracle.zip_decode(sm, codes, esc, eoff, x.size, g["table"]).tolist() == g["values"]

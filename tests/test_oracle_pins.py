@@ -446,3 +446,90 @@ def test_pos_size_formula():
     stream, off2 = oracle.encode_pos(x.astype(np.uint32), W, masks, bitvals, S)
     assert np.array_equal(off, off2)
     assert np.array_equal(oracle.decode_pos(stream, off, n, W, masks, bitvals, S), x)
+
+
+# ------------------------------------------------------------------ ZipCCL exponent codec (comparison)
+
+def _bf16_exponents_of_normal(rng, sigma, n):
+    """Exponent field of N(0, sigma^2) samples as float32 (the BF16 exponent before rounding)."""
+    x = (rng.standard_normal(n) * sigma).astype(np.float32)
+    return ((x.view(np.uint32) >> 23) & 0xFF).astype(np.int64)
+
+
+@pytest.mark.parametrize("sigma", [1e-5, 1e-3, 0.02, 1.0, 37.0])
+def test_zip_table_matches_sampled_exponents(sigma):
+    """The sigma-derived table (no histogram) equals the 7 most frequent exponents of a
+    large Gaussian sample: the same set, and the same order for the leading codes."""
+    rng = np.random.default_rng(int(sigma * 1e6) % 2**32)
+    counts = np.bincount(_bf16_exponents_of_normal(rng, sigma, 4_000_000), minlength=256)
+    top = [int(e) for e in np.argsort(-counts, kind="stable")[:7]]
+    t = [int(e) for e in oracle.zip_table(sigma)]
+    assert set(t) == set(top)
+    assert t[:4] == top[:4]
+
+
+def test_zip_table_vs_scipy_cdf():
+    """Masses from scipy's normal CDF at the BF16 exponent boundaries give the same ranking."""
+    from scipy.stats import norm
+    for sigma in np.geomspace(1e-7, 1e4, 60):
+        e = np.arange(1, 255)
+        lo, hi = np.ldexp(1.0, e - 127), np.ldexp(1.0, e - 126)
+        mass = 2 * (norm.cdf(hi / sigma) - norm.cdf(lo / sigma))
+        mass = np.concatenate([[2 * norm.cdf(np.ldexp(1.0, -126) / sigma) - 1], mass, [0.0]])
+        order = sorted(range(256), key=lambda k: (-mass[k], k))[:7]
+        assert oracle.zip_table(float(sigma)).tolist() == order, sigma
+
+
+def _zip_spec(u, table):
+    """Independent numpy statement of readings Z1-Z6 for one array of BF16 words."""
+    u = u.astype(np.uint32)
+    e = (u >> 7) & 0xFF
+    sm = (((u >> 8) & 0x80) | (u & 0x7F)).astype(np.uint8)
+    lut = np.zeros(256, np.uint32)
+    for k, t in enumerate(table):
+        lut[t] = k + 1
+    c = lut[e]
+    n = u.size
+    nblk = (n + 4095) // 4096
+    planes = np.zeros((nblk, 3, 4096), np.uint8)
+    pad = np.zeros(nblk * 4096, np.uint32)
+    pad[:n] = c
+    for p in range(3):
+        planes[:, p, :] = ((pad >> p) & 1).reshape(nblk, 4096)
+    codes = np.packbits(planes.reshape(nblk, 3, 4096), axis=2, bitorder="little").reshape(-1)
+    esc = e[c == 0].astype(np.uint8)
+    per_blk = np.bincount(np.nonzero(c == 0)[0] // 4096, minlength=nblk)
+    eoff = np.concatenate([[0], np.cumsum(per_blk)]).astype(np.uint64)
+    return sm, codes, esc, eoff
+
+
+def test_zip_all_bf16_words_vs_spec():
+    """Every one of the 65,536 BF16 bit patterns, shuffled over 16 blocks plus a ragged
+    tail, encodes as the numpy statement says and decodes back."""
+    rng = np.random.default_rng(3)
+    u = np.concatenate([rng.permutation(65536), rng.integers(0, 65536, 1234)]).astype(np.uint16)
+    table = oracle.zip_table(1e-3)
+    sm, codes, esc, eoff = oracle.zip_encode(u, table)
+    rsm, rcodes, resc, reoff = _zip_spec(u, table)
+    assert np.array_equal(sm, rsm) and np.array_equal(codes, rcodes)
+    assert np.array_equal(esc, resc) and np.array_equal(eoff, reoff)
+    assert np.array_equal(oracle.zip_decode(sm, codes, esc, eoff, u.size, table), u)
+
+
+def test_zip_size_and_errors():
+    rng = np.random.default_rng(8)
+    x = (rng.standard_normal(100_003) * 1e-3).astype(np.float32)
+    u = (x.view(np.uint32) >> 16).astype(np.uint16)
+    table = oracle.zip_table(1e-3)
+    sm, codes, esc, eoff = oracle.zip_encode(u, table)
+    nblk = (u.size + 4095) // 4096
+    e = (u >> 7) & 0xFF
+    assert esc.size == int((~np.isin(e, table)).sum())
+    assert codes.size == nblk * 1536 and sm.size == u.size and eoff.size == nblk + 1
+    assert esc.size < 0.05 * u.size  # the top 7 exponents cover > 95% of N(0, sigma) data
+    with pytest.raises(oracle.OracleError):
+        oracle.zip_encode(u, [1, 2, 3, 4, 5, 6, 6])  # a repeated exponent is not a table
+    bad = eoff.copy()
+    bad[5] += 1
+    with pytest.raises(oracle.OracleError):
+        oracle.zip_decode(sm, codes, esc, bad, u.size, table)
