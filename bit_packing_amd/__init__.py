@@ -41,6 +41,8 @@ EXPORTS = (
     "ibp_compress", "ibp_decompress", "ibp_decompress_gather", "ibp_gather_raw",
     "ibp_slot_flag_words", "ibp_compress_slots", "ibp_decompress_gather_slots",
     "ibp_metadata_pos_workspace_bytes", "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos",
+    "ibp_zip_table_from_sigma", "ibp_zip_blocks", "ibp_zip_codes_bytes", "ibp_zip_workspace_bytes",
+    "ibp_zip_compress", "ibp_zip_decompress",
 )
 
 
@@ -120,9 +122,16 @@ def load_library() -> ctypes.CDLL:
         lib.ibp_build_metadata_pos.argtypes = [_vp, _u64, _u32, _u32, _dbl, _vp, _vp, _vp, _vp, _u64, _vp]
         lib.ibp_compress_pos.argtypes = [_posp, _vp, _u64, _vp, _u64, _vp, _vp, _u64, _vp, _vp]
         lib.ibp_decompress_pos.argtypes = [_posp, _vp, _u64, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_zip_table_from_sigma.argtypes = [_dbl, _vp]
+        for f in ("ibp_zip_blocks", "ibp_zip_codes_bytes", "ibp_zip_workspace_bytes"):
+            getattr(lib, f).argtypes = [_u64]
+            getattr(lib, f).restype = _u64
+        lib.ibp_zip_compress.argtypes = [_vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp, _u64, _vp, _vp]
+        lib.ibp_zip_decompress.argtypes = [_vp, _vp, _vp, _vp, _u64, _vp, _u64, _vp, _vp, _vp]
         for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",
                   "ibp_gather_raw", "ibp_compress_slots", "ibp_decompress_gather_slots",
-                  "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos"):
+                  "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos", "ibp_zip_table_from_sigma",
+                  "ibp_zip_compress", "ibp_zip_decompress"):
             getattr(lib, f).restype = _int
         _lib = lib
     return _lib
@@ -363,4 +372,62 @@ def ibp_decompress_pos(meta: PosMeta, stream_buf: torch.Tensor, offsets: torch.T
     rc = load_library().ibp_decompress_pos(ctypes.byref(st), _ptr(stream_buf), _nbytes(stream_buf), _ptr(offsets),
                                            n_chunks, _ptr(out), _ptr(err), _stream(stream))
     _check(rc, "ibp_decompress_pos")
+    return out
+
+
+# ------------------------------------------------------------------ comparison codec: BF16 exponent coding
+
+@dataclass
+class ZipCompressed:
+    """BF16 exponent coding of n words: sign-mantissa bytes, code planes, escape
+    exponents (capacity n; the first eoff[-1] are used) and per-block escape offsets."""
+    sm: torch.Tensor
+    codes: torch.Tensor
+    esc: torch.Tensor
+    eoff: torch.Tensor
+    n: int
+    table: bytes
+
+
+def ibp_zip_table_from_sigma(sigma: float) -> bytes:
+    t = (ctypes.c_uint8 * 7)()
+    _check(load_library().ibp_zip_table_from_sigma(sigma, t), "ibp_zip_table_from_sigma")
+    return bytes(t)
+
+
+def _table_buf(table) -> ctypes.Array:
+    t = bytes(table)
+    if len(t) != 7:
+        raise ValueError("a table is 7 exponents")
+    return (ctypes.c_uint8 * 7)(*t)
+
+
+def ibp_zip_compress(table, x: torch.Tensor, err: torch.Tensor | None = None, stream=None,
+                     out: ZipCompressed | None = None, workspace: torch.Tensor | None = None) -> ZipCompressed:
+    """Compress the BF16 words of x (any 2-byte dtype)."""
+    lib = load_library()
+    n = _nbytes(x) // 2
+    dev = _device(x)
+    if out is None:
+        out = ZipCompressed(torch.empty(max(n, 16), dtype=torch.uint8, device=dev),
+                            torch.empty(max(int(lib.ibp_zip_codes_bytes(n)), 16), dtype=torch.uint8, device=dev),
+                            torch.empty(max(n, 16), dtype=torch.uint8, device=dev),
+                            torch.empty(int(lib.ibp_zip_blocks(n)) + 1, dtype=torch.int64, device=dev), n, bytes(table))
+    if workspace is None:
+        workspace = torch.empty(max(int(lib.ibp_zip_workspace_bytes(n)), 8), dtype=torch.uint8, device=dev)
+    rc = lib.ibp_zip_compress(_table_buf(table), _ptr(x), n, _ptr(out.sm), _ptr(out.codes), _ptr(out.esc),
+                              _nbytes(out.esc), _ptr(out.eoff), _ptr(workspace), _nbytes(workspace), _ptr(err),
+                              _stream(stream))
+    _check(rc, "ibp_zip_compress")
+    return out
+
+
+def ibp_zip_decompress(z: ZipCompressed, out: torch.Tensor | None = None, err: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """BF16 words (as int16) of a ZipCompressed."""
+    if out is None:
+        out = torch.empty(max(z.n, 8), dtype=torch.int16, device=_device(z.sm))[: z.n]
+    rc = load_library().ibp_zip_decompress(_table_buf(z.table), _ptr(z.sm), _ptr(z.codes), _ptr(z.esc),
+                                           _nbytes(z.esc), _ptr(z.eoff), z.n, _ptr(out), _ptr(err), _stream(stream))
+    _check(rc, "ibp_zip_decompress")
     return out

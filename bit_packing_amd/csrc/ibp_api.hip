@@ -3,6 +3,7 @@
 // Every argument is checked here, on the host, before any HIP call; then the
 // launch geometry and the workspace layout are derived and the kernels in
 // ibp_meta.hip, ibp_encode.hip, ibp_decode.hip and ibp_slots.hip are enqueued on the caller's stream.
+#include <math.h>
 #include <string.h>
 
 #include "ibp.h"
@@ -485,6 +486,104 @@ IBP_API int ibp_decompress_gather_slots(const ibp_meta_t *meta, const void *slot
   a.head_blocks = (S + 127) / 128 > (row_blocks < 4 ? row_blocks : 4) ? (S + 127) / 128 : (row_blocks < 4 ? row_blocks : 4);
   a.wave_dw = (a.G * a.img_dw + 8 * a.G + (a.G & 1u) + 3) & ~3u;
   return status_of(launch_decode_slots(a, p, static_cast<hipStream_t>(hip_stream)));
+}
+
+// ------------------------------------------------------------------ comparison codec: BF16 exponent coding
+
+// Mass of BF16 exponent e under N(0, sigma^2): |x| in [2^(e-127), 2^(e-126)) for a
+// normal exponent, |x| < 2^-126 for e = 0 (zero and subnormals), none for e = 255.
+static double zip_exponent_mass(int e, double sigma) {
+  const double d = sigma * sqrt(2.0);
+  if (e == 0) return erf(ldexp(1.0, -126) / d);
+  if (e == 255) return 0.0;
+  return erf(ldexp(1.0, e - 126) / d) - erf(ldexp(1.0, e - 127) / d);
+}
+
+IBP_API int ibp_zip_table_from_sigma(double sigma, uint8_t *table_out) {
+  if (!table_out || !(sigma > 0.0) || !isfinite(sigma)) return IBP_ERR_INVALID_ARG;
+  double mass[256];
+  for (int e = 0; e < 256; ++e) mass[e] = zip_exponent_mass(e, sigma);
+  bool taken[256] = {false};
+  for (int k = 0; k < 7; ++k) {  // largest mass first; equal masses: smaller exponent first
+    int best = -1;
+    for (int e = 0; e < 256; ++e)
+      if (!taken[e] && (best < 0 || mass[e] > mass[best])) best = e;
+    taken[best] = true;
+    table_out[k] = (uint8_t)best;
+  }
+  return IBP_OK;
+}
+
+IBP_API uint64_t ibp_zip_blocks(uint64_t n) { return (n + kZipBlock - 1) / kZipBlock; }
+IBP_API uint64_t ibp_zip_codes_bytes(uint64_t n) { return ibp_zip_blocks(n) * (3 * kZipBlock / 8); }
+IBP_API uint64_t ibp_zip_workspace_bytes(uint64_t n) { return 8 + 8 * ibp_zip_blocks(n); }
+
+static bool zip_table_ok(const uint8_t *t) {
+  if (!t) return false;
+  for (int a = 0; a < 7; ++a)
+    for (int b = a + 1; b < 7; ++b)
+      if (t[a] == t[b]) return false;
+  return true;
+}
+
+IBP_API int ibp_zip_compress(const uint8_t *table, const void *d_in, uint64_t n, uint8_t *d_sm, uint8_t *d_codes,
+                             uint8_t *d_esc, uint64_t esc_capacity, uint64_t *d_eoff, void *d_workspace,
+                             uint64_t workspace_bytes, uint32_t *d_err_word, void *hip_stream) {
+  if (!zip_table_ok(table) || !d_eoff) return IBP_ERR_INVALID_ARG;
+  if (n >= (1ull << 40)) return IBP_ERR_SIZE;
+  if (n && (!d_in || !d_sm || !d_codes || !d_esc || !d_workspace)) return IBP_ERR_INVALID_ARG;
+  if (!aligned(d_in, 16) || !aligned(d_sm, 8) || !aligned(d_eoff, 8) || !aligned(d_workspace, 8))
+    return IBP_ERR_INVALID_ARG;
+  if (esc_capacity < n || workspace_bytes < ibp_zip_workspace_bytes(n)) return IBP_ERR_CAPACITY;
+  const uint64_t nblk = ibp_zip_blocks(n);
+  if (!view(d_in, 2 * n) || !view(d_sm, n) || !view(d_codes, ibp_zip_codes_bytes(n)) || !view(d_esc, n) ||
+      !view(d_eoff, 8 * (nblk + 1)) || !view(d_workspace, n ? ibp_zip_workspace_bytes(n) : 0) ||
+      !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  if (n == 0) return status_of(launch_zero(d_eoff, 1, s));
+  ZipArgs a;
+  memset(&a, 0, sizeof(a));
+  a.in = static_cast<const uint16_t *>(d_in);
+  a.sm = d_sm;
+  a.codes = d_codes;
+  a.esc = d_esc;
+  a.eoff = d_eoff;
+  a.control = static_cast<uint32_t *>(d_workspace);
+  a.status = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(d_workspace) + 8);
+  a.err = d_err_word;
+  a.n = n;
+  a.nblk = nblk;
+  for (int k = 0; k < 7; ++k) a.table[k] = table[k];
+  return status_of(launch_zip_encode(a, s));
+}
+
+IBP_API int ibp_zip_decompress(const uint8_t *table, const uint8_t *d_sm, const uint8_t *d_codes,
+                               const uint8_t *d_esc, uint64_t esc_bytes, const uint64_t *d_eoff, uint64_t n,
+                               void *d_out, uint32_t *d_err_word, void *hip_stream) {
+  if (!zip_table_ok(table) || !d_eoff) return IBP_ERR_INVALID_ARG;
+  if (n >= (1ull << 40)) return IBP_ERR_SIZE;
+  if (n && (!d_sm || !d_codes || !d_out)) return IBP_ERR_INVALID_ARG;
+  if (esc_bytes && !d_esc) return IBP_ERR_INVALID_ARG;
+  if (!aligned(d_out, 16) || !aligned(d_sm, 8) || !aligned(d_eoff, 8)) return IBP_ERR_INVALID_ARG;
+  const uint64_t nblk = ibp_zip_blocks(n);
+  if (!view(d_sm, n) || !view(d_codes, ibp_zip_codes_bytes(n)) || !view(d_esc, esc_bytes) ||
+      !view(d_eoff, 8 * (nblk + 1)) || !view(d_out, 2 * n) || !view(d_err_word, d_err_word ? 4 : 0))
+    return IBP_ERR_INVALID_ARG;
+  if (n == 0) return IBP_OK;
+  ZipArgs a;
+  memset(&a, 0, sizeof(a));
+  a.out = static_cast<uint16_t *>(d_out);
+  a.sm = const_cast<uint8_t *>(d_sm);
+  a.codes = const_cast<uint8_t *>(d_codes);
+  a.esc = const_cast<uint8_t *>(d_esc);
+  a.esc_bytes = esc_bytes;
+  a.eoff = const_cast<uint64_t *>(d_eoff);
+  a.err = d_err_word;
+  a.n = n;
+  a.nblk = nblk;
+  for (int k = 0; k < 7; ++k) a.table[k] = table[k];
+  return status_of(launch_zip_decode(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

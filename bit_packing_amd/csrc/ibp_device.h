@@ -195,6 +195,56 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with
+// Decoupled Look-back", 2016), run by one wavefront for tile t whose aggregate is
+// agg (< 2^62): it publishes the aggregate, walks back over the predecessors'
+// status words 64 at a time until one holds an inclusive prefix, publishes its own
+// inclusive prefix and returns the exclusive one.  Tiles must start in ticket
+// order (every tile waited on is already running).  Bounded: after ~2^20 polls,
+// or once another tile has aborted (control[1] != 0), it sets control[1] and
+// IBP_DEVERR_TIMEOUT and returns with timed_out set (the value is then invalid).
+__device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
+                                              uint64_t agg, uint32_t lane, bool &timed_out) {
+  uint64_t excl = 0;
+  timed_out = false;
+  if (t == 0) {
+    if (lane == 0) atomic_store_agent(&status[0], kFlagPrefix | agg);
+    return 0;
+  }
+  if (lane == 0) atomic_store_agent(&status[t], kFlagAggregate | agg);
+  int64_t base = (int64_t)t - 1;
+  uint32_t spins = 0;
+  while (true) {
+    const int64_t j = base - (int64_t)lane;
+    const uint64_t s = j >= 0 ? atomic_load_agent(&status[j]) : kFlagPrefix;
+    const uint64_t flag = s & ~kValueMask;
+    const uint64_t pm = ballot(flag == kFlagPrefix);
+    const uint64_t zm = ballot(flag == 0);
+    const uint32_t first_p = pm ? (uint32_t)__builtin_ctzll(pm) : 64u;
+    const uint64_t needed = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
+    if ((zm & needed) && !timed_out) {
+      // bounded wait: give up when another tile has aborted or after ~2^20 polls
+      bool give_up = false;
+      if ((++spins & 1023u) == 0u) give_up = atomic_load_agent32(&control[1]) != 0u;
+      if (spins > (1u << 20)) {
+        give_up = true;
+        if (lane == 0) {
+          atomic_store_agent32(&control[1], 1u);
+          if (err) atomicOr(err, IBP_DEVERR_TIMEOUT);
+        }
+      }
+      timed_out = ballot(give_up) != 0;
+      if (!timed_out) __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    excl += wave_sum64(lane <= first_p ? (s & kValueMask) : 0ull);
+    if (first_p < 64) break;
+    base -= 64;
+  }
+  if (lane == 0) atomic_store_agent(&status[t], kFlagPrefix | ((excl + agg) & kValueMask));
+  return excl;
+}
+
 }  // namespace dev
 
 // Compile-time run count for a runtime one: 1..8 exactly, 0 = loop.

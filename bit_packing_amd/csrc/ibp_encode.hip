@@ -164,43 +164,8 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
 
   // decoupled look-back
   if (wave == 0) {
-    uint64_t excl = 0;
     bool timed_out = false;
-    if (t == 0) {
-      if (lane == 0) atomic_store_agent(&a.status[0], kFlagPrefix | agg);
-    } else {
-      if (lane == 0) atomic_store_agent(&a.status[t], kFlagAggregate | agg);
-      int64_t base = (int64_t)t - 1;
-      uint32_t spins = 0;
-      while (true) {
-        const int64_t j = base - (int64_t)lane;
-        const uint64_t s = j >= 0 ? atomic_load_agent(&a.status[j]) : kFlagPrefix;
-        const uint64_t flag = s & ~kValueMask;
-        const uint64_t pm = ballot(flag == kFlagPrefix);
-        const uint64_t zm = ballot(flag == 0);
-        const uint32_t first_p = pm ? (uint32_t)__builtin_ctzll(pm) : 64u;
-        const uint64_t needed = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
-        if ((zm & needed) && !timed_out) {
-          // bounded wait: give up when another tile has aborted or after ~2^20 polls
-          bool give_up = false;
-          if ((++spins & 1023u) == 0u) give_up = atomic_load_agent32(&a.control[1]) != 0u;
-          if (spins > (1u << 20)) {
-            give_up = true;
-            if (lane == 0) {
-              atomic_store_agent32(&a.control[1], 1u);
-              if (a.err) atomicOr(a.err, IBP_DEVERR_TIMEOUT);
-            }
-          }
-          timed_out = ballot(give_up) != 0;
-          if (!timed_out) __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        excl += wave_sum64(lane <= first_p ? (s & kValueMask) : 0ull);
-        if (first_p < 64) break;
-        base -= 64;
-      }
-      if (lane == 0) atomic_store_agent(&a.status[t], kFlagPrefix | ((excl + agg) & kValueMask));
-    }
+    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, t, agg, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
       s_failed = timed_out ? 1u : 0u;

@@ -127,6 +127,25 @@ struct SlotArgs {
   uint32_t head_blocks;  // decompress: 16-byte blocks read before the header is known
 };
 
+// Comparison codec (BF16 exponent coding): elements per block.
+constexpr uint32_t kZipBlock = 4096;
+
+struct ZipArgs {
+  const uint16_t *in;  // compress: BF16 words (16-byte aligned)
+  uint16_t *out;       // decompress: BF16 words (16-byte aligned)
+  uint8_t *sm;         // sign-mantissa bytes, n (8-byte aligned)
+  uint8_t *codes;      // three 512-byte code planes per block
+  uint8_t *esc;        // escape exponents
+  uint64_t esc_bytes;  // decompress: readable escape bytes
+  uint64_t *eoff;      // nblk + 1 escape offsets
+  uint64_t *status;    // compress: look-back words, nblk
+  uint32_t *control;   // compress: [0] block ticket, [1] abort flag
+  uint32_t *err;       // optional
+  uint64_t n;
+  uint64_t nblk;
+  uint32_t table[7];   // exponents of codes 1..7, distinct
+};
+
 constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;
 
 // Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip, ibp_slots.hip).  Each returns the hipError_t of its launch(es).
@@ -137,6 +156,8 @@ hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather,
 hipError_t launch_decode_pos(const DecodeArgs &a, const CodecParams &p, hipStream_t s);
 hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s);
 hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s);
+hipError_t launch_zip_encode(const ZipArgs &a, hipStream_t s);  // ibp_zip.hip
+hipError_t launch_zip_decode(const ZipArgs &a, hipStream_t s);
 hipError_t launch_encode_slots(const SlotArgs &a, const CodecParams &p, hipStream_t s);  // ibp_slots.hip
 hipError_t launch_decode_slots(const SlotArgs &a, const CodecParams &p, hipStream_t s);
 

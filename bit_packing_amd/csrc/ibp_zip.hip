@@ -1,0 +1,223 @@
+// ibp_zip.hip -- the comparison codec: exponent coding of BF16 tensors as on the
+// page "ZipCCL: Efficient Lossless Data Compression of Communication Collectives
+// for Accelerating LLM Training", section 2 (Metodologia), A and B, on one GPU
+// and without collectives.
+//
+// A BF16 word splits into a sign-mantissa byte and its 8-bit exponent.  The 7
+// exponents of a table derived from the tensor's standard deviation get 3-bit
+// codes 1..7; any other exponent gets code 0 and is stored whole, in element
+// order, in an escape array.  Per block of 4096 elements the codes are kept as
+// three bit planes of 4096 bits; eoff[j] counts the escapes before block j.
+//
+// Both kernels run one 256-thread workgroup per block; thread t handles the two
+// groups of 8 consecutive elements [q*2048 + 8t, +8), q = 0, 1, so sign-mantissa
+// bytes, plane bytes and BF16 words move as 8-, 1- and 16-byte accesses.  The
+// escapes of a thread are ranked by a block scan of two 16-bit counts packed in
+// one word (group 0 low, group 1 high), and the block's first escape by a
+// decoupled look-back over the blocks (compression) or by eoff (decompression).
+#include "ibp_device.h"
+
+namespace ibp {
+namespace {
+
+using namespace dev;
+
+constexpr uint32_t kGroup = 8;                          // consecutive elements per thread and group
+constexpr uint32_t kHalf = kZipBlock / 2;               // elements per group pass
+constexpr uint32_t kPlane = kZipBlock / 8;              // bytes per code plane
+
+// Inclusive scan of v over the workgroup (256 threads); *total gets the sum.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t lane, uint32_t wave, uint32_t *wsum,
+                                               uint32_t *total) {
+  uint32_t x = v;
+#pragma unroll
+  for (uint32_t o = 1; o < kWave; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) wsum[wave] = x;
+  __syncthreads();
+  uint32_t pre = 0, all = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kWavesPerBlock; ++w) {
+    const uint32_t s = wsum[w];
+    if (w < wave) pre += s;
+    all += s;
+  }
+  *total = all;
+  return pre + x;
+}
+
+__global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
+  __shared__ uint8_t lut[256];  // exponent -> code
+  __shared__ uint32_t wsum[kWavesPerBlock];
+  __shared__ uint64_t s_excl;
+  __shared__ uint32_t s_tile, s_failed;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
+  if (tid == 0) s_tile = atomicAdd(&a.control[0], 1u);
+  lut[tid] = 0;
+  __syncthreads();
+  if (tid < 7) lut[a.table[tid]] = (uint8_t)(tid + 1);
+  __syncthreads();
+  const uint64_t j = s_tile;
+  if (j >= a.nblk) return;  // grid == nblk, so every ticket is a block
+  const uint64_t e0 = j * kZipBlock;
+  const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
+
+  uint32_t ex[2][kGroup / 4];  // exponents, four per word
+  uint32_t escm = 0;           // bit q*8 + k: element k of group q is an escape
+  uint32_t packed = 0;         // escape counts: group 0 low 16 bits, group 1 high
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    const uint32_t t0 = q * kHalf + kGroup * tid;
+    uint16_t u[kGroup];
+    if (t0 + kGroup <= nb) {
+      const uint4 w = *reinterpret_cast<const uint4 *>(a.in + e0 + t0);
+      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (uint32_t k = 0; k < kGroup; ++k) u[k] = (uint16_t)(ws[k / 2] >> (16 * (k % 2)));
+    } else {
+#pragma unroll
+      for (uint32_t k = 0; k < kGroup; ++k) u[k] = t0 + k < nb ? a.in[e0 + t0 + k] : (uint16_t)0;
+    }
+    uint32_t sm[2] = {0u, 0u};
+    uint32_t pb0 = 0, pb1 = 0, pb2 = 0;
+    ex[q][0] = ex[q][1] = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kGroup; ++k) {
+      const uint32_t v = u[k], e = (v >> 7) & 0xFFu;
+      const uint32_t s = ((v >> 8) & 0x80u) | (v & 0x7Fu);
+      const bool valid = t0 + k < nb;
+      const uint32_t c = valid ? lut[e] : 0u;
+      sm[k / 4] |= s << (8 * (k % 4));
+      ex[q][k / 4] |= e << (8 * (k % 4));
+      pb0 |= (c & 1u) << k;
+      pb1 |= ((c >> 1) & 1u) << k;
+      pb2 |= ((c >> 2) & 1u) << k;
+      if (valid && c == 0u) {
+        escm |= 1u << (q * kGroup + k);
+        packed += 1u << (16 * q);
+      }
+    }
+    uint8_t *smo = a.sm + e0 + t0;
+    if (t0 + kGroup <= nb) {
+      *reinterpret_cast<uint2 *>(smo) = make_uint2(sm[0], sm[1]);
+    } else {
+      for (uint32_t k = 0; t0 + k < nb; ++k) smo[k] = (uint8_t)(sm[k / 4] >> (8 * (k % 4)));
+    }
+    uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
+    cp[0] = (uint8_t)pb0;
+    cp[kPlane] = (uint8_t)pb1;
+    cp[2 * kPlane] = (uint8_t)pb2;
+  }
+  uint32_t total;
+  const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);
+  const uint32_t excl_t = incl - packed;
+  const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
+  if (wave == 0) {
+    bool timed_out = false;
+    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, j, agg, lane, timed_out);
+    if (lane == 0) {
+      s_excl = excl;
+      s_failed = timed_out ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  if (s_failed != 0u) return;  // no valid escape offset: nothing more is stored
+  const uint64_t base = s_excl;
+  if (tid == 0) {
+    a.eoff[j] = base;
+    if (j == a.nblk - 1) a.eoff[a.nblk] = base + agg;
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    uint64_t r = base + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
+#pragma unroll
+    for (uint32_t k = 0; k < kGroup; ++k)
+      if ((escm >> (q * kGroup + k)) & 1u) a.esc[r++] = (uint8_t)(ex[q][k / 4] >> (8 * (k % 4)));
+  }
+}
+
+__global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
+  __shared__ uint32_t tab[8];
+  __shared__ uint32_t wsum[kWavesPerBlock];
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
+  if (tid < 7) tab[tid + 1] = a.table[tid];
+  const uint64_t j = blockIdx.x;
+  const uint64_t e0 = j * kZipBlock;
+  const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
+  uint32_t c[2][kGroup];
+  uint32_t packed = 0;
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    const uint32_t t0 = q * kHalf + kGroup * tid;
+    const uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
+    const uint32_t pb0 = cp[0], pb1 = cp[kPlane], pb2 = cp[2 * kPlane];
+#pragma unroll
+    for (uint32_t k = 0; k < kGroup; ++k) {
+      c[q][k] = ((pb0 >> k) & 1u) | (((pb1 >> k) & 1u) << 1) | (((pb2 >> k) & 1u) << 2);
+      if (t0 + k < nb && c[q][k] == 0u) packed += 1u << (16 * q);
+    }
+  }
+  uint32_t total;
+  const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);  // also orders the tab writes
+  const uint32_t excl_t = incl - packed;
+  const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
+  const uint64_t E0 = a.eoff[j], E1 = a.eoff[j + 1];
+  if (E1 < E0 || E1 - E0 != agg || E1 > a.esc_bytes) {
+    if (tid == 0 && a.err) atomicOr(a.err, IBP_DEVERR_CORRUPT);
+    return;  // block not decoded
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    const uint32_t t0 = q * kHalf + kGroup * tid;
+    if (t0 >= nb) continue;
+    const bool full = t0 + kGroup <= nb;
+    uint32_t sm[2];
+    if (full) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(a.sm + e0 + t0);
+      sm[0] = w.x;
+      sm[1] = w.y;
+    } else {
+      sm[0] = sm[1] = 0;
+      for (uint32_t k = 0; t0 + k < nb; ++k) sm[k / 4] |= (uint32_t)a.sm[e0 + t0 + k] << (8 * (k % 4));
+    }
+    uint64_t r = E0 + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (uint32_t k = 0; k < kGroup; ++k) {
+      const uint32_t s = (sm[k / 4] >> (8 * (k % 4))) & 0xFFu;
+      uint32_t e = 0;
+      if (t0 + k < nb) e = c[q][k] ? tab[c[q][k]] : (uint32_t)a.esc[r++];
+      const uint32_t v = ((s & 0x80u) << 8) | (e << 7) | (s & 0x7Fu);
+      w[k / 2] |= v << (16 * (k % 2));
+    }
+    uint16_t *o = a.out + e0 + t0;
+    if (full) {
+      *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+    } else {
+      for (uint32_t k = 0; t0 + k < nb; ++k) o[k] = (uint16_t)(w[k / 2] >> (16 * (k % 2)));
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zip_encode(const ZipArgs &a, hipStream_t s) {
+  if (a.nblk == 0) return hipSuccess;
+  if (a.nblk > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  // clear the ticket, abort flag and status words (a kernel, not a memset node)
+  hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), a.nblk + 1, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zip_encode_kernel, dim3((uint32_t)a.nblk), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_zip_decode(const ZipArgs &a, hipStream_t s) {
+  if (a.nblk == 0) return hipSuccess;
+  if (a.nblk > 0x7FFFFFFFull) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zip_decode_kernel, dim3((uint32_t)a.nblk), dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace ibp

@@ -248,6 +248,46 @@ IBP_API int ibp_decompress_pos(const ibp_pos_meta_t *meta, const void *stream_in
                                const uint64_t *d_offsets, uint64_t n_chunks, void *d_out, uint32_t *d_err_word,
                                void *hip_stream);
 
+/*
+ * Comparison codec, not IBP: exponent coding of BF16 tensors as on the page
+ * "ZipCCL: Efficient Lossless Data Compression of Communication Collectives for
+ * Accelerating LLM Training" (section 2, Metodologia, A and B), on one GPU.
+ *   Element i (BF16 word u) -> sign-mantissa byte sm[i] = (u >> 8 & 0x80) | (u & 0x7F)
+ *   and exponent e = (u >> 7) & 0xFF.  If e == table[k] the element's code is k + 1,
+ *   otherwise 0 and e is appended to the escape array (element order).
+ *   Blocks of 4096 elements; block j keeps its codes as three planes of 512 bytes
+ *   at d_codes + j*1536 + p*512 (bit t of plane p = bit p of element t's code,
+ *   LSB-first bytes; bits past the last element are 0).  d_eoff[j] = escapes
+ *   before block j, d_eoff[nblk] = total escapes.
+ *   table: host, 7 distinct exponents (codes 1..7).
+ */
+
+/* The 7 exponents of largest mass under N(0, sigma^2) (exponent e covers
+ * 2^(e-127) <= |x| < 2^(e-126); e = 0 covers |x| < 2^-126; e = 255 none), in
+ * decreasing mass order, equal masses by smaller exponent: 7 bytes to table_out. */
+IBP_API int ibp_zip_table_from_sigma(double sigma, uint8_t *table_out);
+
+/* ceil(n / 4096); code plane bytes 1536 * blocks; compression workspace 8 + 8 * blocks. */
+IBP_API uint64_t ibp_zip_blocks(uint64_t n);
+IBP_API uint64_t ibp_zip_codes_bytes(uint64_t n);
+IBP_API uint64_t ibp_zip_workspace_bytes(uint64_t n);
+
+/* Compress n BF16 words (d_in, device, aligned to 16).  d_sm: n bytes (aligned to
+ * 8); d_codes: ibp_zip_codes_bytes(n); d_esc: esc_capacity >= n bytes; d_eoff:
+ * blocks + 1 words; d_workspace: ibp_zip_workspace_bytes(n).  One pass: each
+ * block finds its first escape by a decoupled look-back over the blocks (bounded;
+ * IBP_DEVERR_TIMEOUT on give-up).  Asynchronous. */
+IBP_API int ibp_zip_compress(const uint8_t *table, const void *d_in, uint64_t n, uint8_t *d_sm, uint8_t *d_codes,
+                             uint8_t *d_esc, uint64_t esc_capacity, uint64_t *d_eoff, void *d_workspace,
+                             uint64_t workspace_bytes, uint32_t *d_err_word, void *hip_stream);
+
+/* Decompress n BF16 words into d_out (device, aligned to 16).  esc_bytes: readable
+ * escape bytes.  A block whose escape count disagrees with d_eoff, or whose
+ * escapes lie past esc_bytes, is not decoded and sets IBP_DEVERR_CORRUPT. */
+IBP_API int ibp_zip_decompress(const uint8_t *table, const uint8_t *d_sm, const uint8_t *d_codes,
+                               const uint8_t *d_esc, uint64_t esc_bytes, const uint64_t *d_eoff, uint64_t n,
+                               void *d_out, uint32_t *d_err_word, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -132,3 +132,18 @@ def test_no_fallback_when_library_missing(ibp, monkeypatch):
     monkeypatch.setattr(ibp, "LIB_PATH", "/nonexistent/libibp.so")
     with pytest.raises(RuntimeError):
         ibp.load_library()
+
+
+def test_zip_table_matches_oracle(ibp):
+    """The library's own sigma -> exponent table (host code) equals the oracle's."""
+    import numpy as np
+
+    import oracle
+    for sigma in np.geomspace(1e-8, 1e5, 80):
+        assert list(ibp.ibp_zip_table_from_sigma(float(sigma))) == oracle.zip_table(float(sigma)).tolist(), sigma
+    lib = ibp.load_library()
+    assert lib.ibp_zip_table_from_sigma(0.0, (ctypes.c_uint8 * 7)()) == ibp.IBP_ERR_INVALID_ARG
+    assert ibp.load_library().ibp_zip_blocks(4097) == 2 and lib.ibp_zip_codes_bytes(4097) == 3072
+    assert lib.ibp_zip_workspace_bytes(4096) == 16
+    t = (ctypes.c_uint8 * 7)(1, 2, 3, 4, 5, 6, 6)  # repeated exponent
+    assert lib.ibp_zip_compress(t, FAKE, 16, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 64, None, None) == ibp.IBP_ERR_INVALID_ARG

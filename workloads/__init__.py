@@ -96,6 +96,7 @@ class Workload:
     dtype: str        # element dtype of the data
     row_elems: int    # elements per row (gather workloads), else 0
     gather: int       # ids per gather step (gather workloads), else 0
+    sigma: float = 0.0  # standard deviation of the bulk of a Gaussian tensor (0: not Gaussian)
 
     @property
     def seed(self) -> int:
@@ -110,13 +111,13 @@ WORKLOADS = {
     "dlrm": Workload(3, "dlrm", "DLRM embedding table: 10,000,000 rows x 64 fp32 ~ U(-0.05, 0.05)", 64, 0.98, 32,
                      "float32", 64, 32768),
     "llm": Workload(4, "llm", "LLM gradient buffer: 2^30 bf16 ~ N(0, 1e-3) with 0.1% N(0,1) outliers", 64, 0.97, 256,
-                    "uint16", 0, 0),
+                    "uint16", 0, 0, 1e-3),
     "ids": Workload(5, "ids", "Integer id stream: 500,000,000 int64 ~ U[0, 2^24), 5% U[0, 2^40)", 64, 0.999, 256,
                     "int64", 0, 0),
     "sparse": Workload(6, "sparse", "Sparse GNN feature cache: 1,000,000 nodes x 128 fp32, 95% zeros, rest |N(0,1)|",
                        32, 0.9, 128, "float32", 128, 65536),
     "llm16": Workload(7, "llm16", "LLM gradient buffer (the llm tensor) coded per element: 2^30 bf16, W=16", 16, 0.97,
-                      1024, "uint16", 0, 0),
+                      1024, "uint16", 0, 0, 1e-3),
 }
 
 FULL_SIZE = {"tiny": 262_144, "gnn": 1_000_000, "dlrm": 10_000_000, "llm": 1 << 30, "ids": 500_000_000,
