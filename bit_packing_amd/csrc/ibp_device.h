@@ -196,22 +196,28 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
 }
 
 // Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with
-// Decoupled Look-back", 2016), run by one wavefront for tile t whose aggregate is
-// agg (< 2^62): it publishes the aggregate, walks back over the predecessors'
-// status words 64 at a time until one holds an inclusive prefix, publishes its own
-// inclusive prefix and returns the exclusive one.  Tiles must start in ticket
-// order (every tile waited on is already running).  Bounded: after ~2^20 polls,
+// Decoupled Look-back", 2016), run by one wavefront for tile t whose aggregate
+// agg (< 2^62) lookback_publish has already published: it walks back over the
+// predecessors' status words 64 at a time until one holds an inclusive prefix,
+// publishes its own inclusive prefix and returns the exclusive one.  Tile t is workgroup t: the
+// dispatcher hands workgroups to the XCDs round-robin and starts each XCD's share
+// in increasing order, so the lowest unfinished tile always has a slot (every
+// earlier workgroup of its XCD has finished) and the wait chain makes progress.
+// (A single atomic ticket counter would also order them, but it serialises all
+// workgroups on one address, at about 12 ns each.)  Bounded: after ~2^20 polls,
 // or once another tile has aborted (control[1] != 0), it sets control[1] and
 // IBP_DEVERR_TIMEOUT and returns with timed_out set (the value is then invalid).
+// Publish tile t's aggregate agg (tile 0: its inclusive prefix) before its
+// look-back, as early as possible: one thread.
+__device__ inline void lookback_publish(uint64_t *status, uint64_t t, uint64_t agg) {
+  atomic_store_agent(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+}
+
 __device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
                                               uint64_t agg, uint32_t lane, bool &timed_out) {
   uint64_t excl = 0;
   timed_out = false;
-  if (t == 0) {
-    if (lane == 0) atomic_store_agent(&status[0], kFlagPrefix | agg);
-    return 0;
-  }
-  if (lane == 0) atomic_store_agent(&status[t], kFlagAggregate | agg);
+  if (t == 0) return 0;
   int64_t base = (int64_t)t - 1;
   uint32_t spins = 0;
   while (true) {

@@ -22,8 +22,7 @@ enum : uint32_t {
 };
 
 // One workgroup per tile of G consecutive segments (about kEncTileChunks chunks).
-//  1. take a tile ticket (tiles are numbered in start order, so every tile a
-//     tile waits for is already running);
+//  1. tile t = workgroup index (see lookback_exclusive for why the order holds);
 //  2. load the chunks (16 per thread, 64 consecutive per wavefront per pass),
 //     test the invariant bits and ballot the participation bits; clear the LDS
 //     image while the loads are in flight;
@@ -63,14 +62,10 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   uint64_t *btab = mtab + (kPos ? a.S : 0u);
   uint16_t *wpre = reinterpret_cast<uint16_t *>(btab + (kPos ? a.S : 0u));
   __shared__ uint64_t s_excl;
-  __shared__ uint32_t s_tile;
   __shared__ uint32_t s_failed;
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
-  if (tid == 0) s_tile = atomicAdd(&a.control[0], 1u);
-  __syncthreads();
-  const uint64_t t = s_tile;
-  if (t >= a.ntiles) return;  // grid == ntiles, so every ticket is a tile
+  const uint64_t t = blockIdx.x;  // grid == ntiles
 
   const uint64_t k0 = t * a.G;
   const uint64_t c0 = k0 * a.S;
@@ -162,31 +157,13 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   };
   const uint64_t agg = (uint64_t)nch * (W + 1) - (kPos ? (uint64_t)pref[kBal] : (uint64_t)pc * pref[kBal]);
 
-  // decoupled look-back
-  if (wave == 0) {
-    bool timed_out = false;
-    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, t, agg, lane, timed_out);
-    if (lane == 0) {
-      s_excl = excl;
-      s_failed = timed_out ? 1u : 0u;
-    }
-  }
-  __syncthreads();
-  const uint64_t excl = s_excl;
-  // a tile that gave up waiting has no valid start bit: it stores nothing that
-  // depends on it (its neighbours see the abort flag and give up as well)
-  if (s_failed != 0u) {
-    if (tid == 0) atomic_store_agent(&a.tails[t], kTailReady);
-    return;
-  }
+  // publish the tile's size at once, so successors can look back past it while
+  // this tile packs
+  if (tid == 0) lookback_publish(a.status, t, agg);
 
-  // 4a. segment offsets
-  for (uint32_t r = tid; r < nsegt; r += kBlock)
-    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)cost(r * a.S);
-  if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
-
-  // 4b. pack into LDS
-  const uint32_t lb0 = (uint32_t)(excl & 127u);
+  // 4. pack into LDS, from bit 0 of the image (the tile's first bit); the store
+  //    shifts the image to the tile's place in the stream
+  const uint32_t lb0 = 0u;
   const uint32_t i_lane = lane & (a.S - 1u);                   // small-S: index in segment
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
 #pragma unroll
@@ -196,9 +173,9 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     if (cb >= nch) continue;                         // uniform
     const uint32_t cl = cb + lane;
     const bool valid = cl < nch;
-    const bool h = (B[q] >> lane) & 1ull;
+    const bool h = __builtin_amdgcn_inverse_ballot_w64(B[q]);
     // saved bits of the tile chunks before this one
-    const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : pc * (uniform(pref[blk]) + count_below(B[q]));
+    const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : __umul24(pc, uniform(pref[blk]) + count_below(B[q]));
     auto payload = [&]() -> T {
       if constexpr (kPos) {
         const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
@@ -242,22 +219,64 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   }
   __syncthreads();
 
-  // 5. store: obuf dword d is stream dword (excl >> 7) * 4 + d
+  // 5. the tile's start bit: decoupled look-back over the predecessors
+  if (wave == 0) {
+    bool timed_out = false;
+    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, t, agg, lane, timed_out);
+    if (lane == 0) {
+      s_excl = excl;
+      s_failed = timed_out ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  const uint64_t excl = s_excl;
+  // a tile that gave up waiting has no valid start bit: it stores nothing that
+  // depends on it (its neighbours see the abort flag and give up as well)
+  if (s_failed != 0u) {
+    if (tid == 0) atomic_store_agent(&a.tails[t], kTailReady);
+    return;
+  }
+
+  // 6. segment offsets
+  for (uint32_t r = tid; r < nsegt; r += kBlock)
+    a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)cost(r * a.S);
+  if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
+
+  // 7. store.  Output dword d is stream dword (excl >> 7) * 4 + d, so interior
+  //    stores are 16-byte aligned; image bit j is output bit sh0 + j, sh0 = excl & 127.
+  const uint32_t sh0 = (uint32_t)(excl & 127u);
+  const uint32_t dq = sh0 >> 5, sh = sh0 & 31u;
+  const uint32_t img_end = (uint32_t)((agg + 31) >> 5);  // image dwords holding tile bits
+  auto img = [&](int32_t i) -> uint32_t { return (i >= 0 && (uint32_t)i < img_end) ? obuf[i] : 0u; };
+  auto out_dw = [&](uint32_t d) -> uint32_t {
+    const int32_t i = (int32_t)d - (int32_t)dq;
+    return sh ? (img(i) << sh) | (img(i - 1) >> (32u - sh)) : img(i);
+  };
   const bool last = t == a.ntiles - 1;
-  const uint32_t first_d = lb0 >> 5;                         // dword holding the first bit
-  const uint32_t last_d = (uint32_t)((lb0 + agg - 1) >> 5);  // dword holding the last bit
-  const bool has_head = (lb0 & 31u) != 0u;
-  const bool has_tail = ((lb0 + agg) & 31u) != 0u;
+  const uint32_t first_d = dq;                                // dword holding the first bit
+  const uint32_t last_d = (uint32_t)((sh0 + agg - 1) >> 5);   // dword holding the last bit
+  const bool has_head = sh != 0u;
+  const bool has_tail = ((sh0 + agg) & 31u) != 0u;
   const uint32_t lo = first_d + (has_head ? 1u : 0u);
   const uint32_t hi = last_d + 1u - ((has_tail && !last) ? 1u : 0u);  // [lo, hi) stored directly
   uint32_t *gdst = a.stream + ((excl >> 7) << 2);
   const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
-  for (uint32_t d = lo + tid; d < a4; d += kBlock) gdst[d] = obuf[d];
-  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kBlock)
-    *reinterpret_cast<uint4 *>(gdst + d) = *reinterpret_cast<const uint4 *>(obuf + d);
-  for (uint32_t d = e4 + tid; d < hi; d += kBlock) gdst[d] = obuf[d];
+  for (uint32_t d = lo + tid; d < a4; d += kBlock) gdst[d] = out_dw(d);
+  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kBlock) {
+    const int32_t i = (int32_t)d - (int32_t)dq;
+    const uint32_t p = img(i - 1), x0 = img(i), x1 = img(i + 1), x2 = img(i + 2), x3 = img(i + 3);
+    uint4 o;
+    if (sh) {
+      o = make_uint4((x0 << sh) | (p >> (32u - sh)), (x1 << sh) | (x0 >> (32u - sh)), (x2 << sh) | (x1 >> (32u - sh)),
+                     (x3 << sh) | (x2 >> (32u - sh)));
+    } else {
+      o = make_uint4(x0, x1, x2, x3);
+    }
+    *reinterpret_cast<uint4 *>(gdst + d) = o;
+  }
+  for (uint32_t d = e4 + tid; d < hi; d += kBlock) gdst[d] = out_dw(d);
   if (tid == 0) {
-    if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | obuf[last_d]);
+    if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | out_dw(last_d));
     if (has_head) {
       uint64_t prev = 0;
       uint32_t spins = 0;
@@ -272,7 +291,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      gdst[first_d] = obuf[first_d] | (uint32_t)prev;
+      gdst[first_d] = out_dw(first_d) | (uint32_t)prev;
     }
   }
 }
@@ -331,7 +350,7 @@ hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s) {
 hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s) {
   if (a.ntiles == 0) return hipSuccess;
   if (a.ntiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  // clear the ticket, abort flag, status and hand-over words (a kernel, not a
+  // clear the control words, status and hand-over words (a kernel, not a
   // memset node, so the sequence stays valid inside a captured graph)
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;

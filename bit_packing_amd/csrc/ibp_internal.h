@@ -63,7 +63,7 @@ struct EncodeArgs {
   uint64_t *off;       // nseg + 1 bit offsets
   uint64_t *status;    // ntiles look-back words
   uint64_t *tails;     // ntiles hand-over words (last partial dword of a tile)
-  uint32_t *control;   // [0] tile ticket, [1] abort flag
+  uint32_t *control;   // [0] unused, [1] abort flag
   uint32_t *err;       // optional
   const uint64_t *pmask;    // position-dependent metadata: Mask_i, i < S (device), else null
   const uint64_t *pbitval;  // Bitval_i, i < S
@@ -139,7 +139,7 @@ struct ZipArgs {
   uint64_t esc_bytes;  // decompress: readable escape bytes
   uint64_t *eoff;      // nblk + 1 escape offsets
   uint64_t *status;    // compress: look-back words, nblk
-  uint32_t *control;   // compress: [0] block ticket, [1] abort flag
+  uint32_t *control;   // compress: [0] unused, [1] abort flag
   uint32_t *err;       // optional
   uint64_t n;
   uint64_t nblk;

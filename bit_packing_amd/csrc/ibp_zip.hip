@@ -52,15 +52,13 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   __shared__ uint8_t lut[256];  // exponent -> code
   __shared__ uint32_t wsum[kWavesPerBlock];
   __shared__ uint64_t s_excl;
-  __shared__ uint32_t s_tile, s_failed;
+  __shared__ uint32_t s_failed;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
-  if (tid == 0) s_tile = atomicAdd(&a.control[0], 1u);
   lut[tid] = 0;
   __syncthreads();
   if (tid < 7) lut[a.table[tid]] = (uint8_t)(tid + 1);
   __syncthreads();
-  const uint64_t j = s_tile;
-  if (j >= a.nblk) return;  // grid == nblk, so every ticket is a block
+  const uint64_t j = blockIdx.x;  // grid == nblk; the look-back relies on workgroup order
   const uint64_t e0 = j * kZipBlock;
   const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
 
@@ -114,6 +112,7 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);
   const uint32_t excl_t = incl - packed;
   const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
+  if (tid == 0) lookback_publish(a.status, j, agg);
   if (wave == 0) {
     bool timed_out = false;
     const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, j, agg, lane, timed_out);
@@ -206,7 +205,7 @@ __global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
 hipError_t launch_zip_encode(const ZipArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipSuccess;
   if (a.nblk > 0x7FFFFFFFull) return hipErrorInvalidValue;
-  // clear the ticket, abort flag and status words (a kernel, not a memset node)
+  // clear the control words and status words (a kernel, not a memset node)
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), a.nblk + 1, s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(zip_encode_kernel, dim3((uint32_t)a.nblk), dim3(kBlock), 0, s, a);
