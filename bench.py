@@ -418,7 +418,15 @@ def main() -> int:
     torch.cuda.synchronize()
     errword = int(err.item())
 
-    # a plain device copy of known size: its counter readings calibrate FETCH_SIZE / WRITE_SIZE
+    # reference ceiling for kernels that read and write HBM: a plain 256 MiB device copy
+    ref_a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    ref_b = torch.empty_like(ref_a)
+    _, dc_ms = timer.run(lambda i: ref_b.copy_(ref_a), 10)
+    extra["device_copy_reference"] = {"GBps": 2 * (256 << 20) / dc_ms / 1e6,
+                                      "fraction_of_peak": 2 * (256 << 20) / dc_ms / 1e6 / HBM_PEAK_GBPS}
+    del ref_a, ref_b
+    # a plain device copy of known size (the last one of the run): its counter readings
+    # calibrate FETCH_SIZE / WRITE_SIZE
     cal = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     cal2 = torch.empty_like(cal)
     cal2.copy_(cal)

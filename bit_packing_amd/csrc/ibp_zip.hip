@@ -63,6 +63,8 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
 
   uint32_t ex[2][kGroup / 4];  // exponents, four per word
+  uint32_t smw[2][2];          // sign-mantissa bytes, four per word
+  uint32_t pbv[2][3];          // plane bytes
   uint32_t escm = 0;           // bit q*8 + k: element k of group q is an escape
   uint32_t packed = 0;         // escape counts: group 0 low 16 bits, group 1 high
 #pragma unroll
@@ -78,41 +80,47 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
 #pragma unroll
       for (uint32_t k = 0; k < kGroup; ++k) u[k] = t0 + k < nb ? a.in[e0 + t0 + k] : (uint16_t)0;
     }
-    uint32_t sm[2] = {0u, 0u};
-    uint32_t pb0 = 0, pb1 = 0, pb2 = 0;
+    smw[q][0] = smw[q][1] = 0;
+    pbv[q][0] = pbv[q][1] = pbv[q][2] = 0;
     ex[q][0] = ex[q][1] = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kGroup; ++k) {
       const uint32_t v = u[k], e = (v >> 7) & 0xFFu;
-      const uint32_t s = ((v >> 8) & 0x80u) | (v & 0x7Fu);
+      const uint32_t sbyte = ((v >> 8) & 0x80u) | (v & 0x7Fu);
       const bool valid = t0 + k < nb;
       const uint32_t c = valid ? lut[e] : 0u;
-      sm[k / 4] |= s << (8 * (k % 4));
+      smw[q][k / 4] |= sbyte << (8 * (k % 4));
       ex[q][k / 4] |= e << (8 * (k % 4));
-      pb0 |= (c & 1u) << k;
-      pb1 |= ((c >> 1) & 1u) << k;
-      pb2 |= ((c >> 2) & 1u) << k;
+      pbv[q][0] |= (c & 1u) << k;
+      pbv[q][1] |= ((c >> 1) & 1u) << k;
+      pbv[q][2] |= ((c >> 2) & 1u) << k;
       if (valid && c == 0u) {
         escm |= 1u << (q * kGroup + k);
         packed += 1u << (16 * q);
       }
     }
-    uint8_t *smo = a.sm + e0 + t0;
-    if (t0 + kGroup <= nb) {
-      *reinterpret_cast<uint2 *>(smo) = make_uint2(sm[0], sm[1]);
-    } else {
-      for (uint32_t k = 0; t0 + k < nb; ++k) smo[k] = (uint8_t)(sm[k / 4] >> (8 * (k % 4)));
-    }
-    uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
-    cp[0] = (uint8_t)pb0;
-    cp[kPlane] = (uint8_t)pb1;
-    cp[2 * kPlane] = (uint8_t)pb2;
   }
+  // the block's escape count first, published at once for the successors' look-back
   uint32_t total;
   const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);
   const uint32_t excl_t = incl - packed;
   const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
   if (tid == 0) lookback_publish(a.status, j, agg);
+  // then the sign-mantissa bytes and code planes, which need no offset
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    const uint32_t t0 = q * kHalf + kGroup * tid;
+    uint8_t *smo = a.sm + e0 + t0;
+    if (t0 + kGroup <= nb) {
+      *reinterpret_cast<uint2 *>(smo) = make_uint2(smw[q][0], smw[q][1]);
+    } else {
+      for (uint32_t k = 0; t0 + k < nb; ++k) smo[k] = (uint8_t)(smw[q][k / 4] >> (8 * (k % 4)));
+    }
+    uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
+    cp[0] = (uint8_t)pbv[q][0];
+    cp[kPlane] = (uint8_t)pbv[q][1];
+    cp[2 * kPlane] = (uint8_t)pbv[q][2];
+  }
   if (wave == 0) {
     bool timed_out = false;
     const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, j, agg, lane, timed_out);
@@ -145,16 +153,34 @@ __global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
   const uint64_t j = blockIdx.x;
   const uint64_t e0 = j * kZipBlock;
   const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
+  // every load that does not depend on the escape ranks is issued first
+  const uint64_t E0 = a.eoff[j], E1 = a.eoff[j + 1];
+  uint32_t pb[2][3];
+  uint32_t sm[2][2];
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    const uint32_t t0 = q * kHalf + kGroup * tid;
+    const uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
+    pb[q][0] = cp[0];
+    pb[q][1] = cp[kPlane];
+    pb[q][2] = cp[2 * kPlane];
+    sm[q][0] = sm[q][1] = 0;
+    if (t0 + kGroup <= nb) {
+      const uint2 w = *reinterpret_cast<const uint2 *>(a.sm + e0 + t0);
+      sm[q][0] = w.x;
+      sm[q][1] = w.y;
+    } else {
+      for (uint32_t k = 0; t0 + k < nb; ++k) sm[q][k / 4] |= (uint32_t)a.sm[e0 + t0 + k] << (8 * (k % 4));
+    }
+  }
   uint32_t c[2][kGroup];
   uint32_t packed = 0;
 #pragma unroll
   for (uint32_t q = 0; q < 2; ++q) {
     const uint32_t t0 = q * kHalf + kGroup * tid;
-    const uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
-    const uint32_t pb0 = cp[0], pb1 = cp[kPlane], pb2 = cp[2 * kPlane];
 #pragma unroll
     for (uint32_t k = 0; k < kGroup; ++k) {
-      c[q][k] = ((pb0 >> k) & 1u) | (((pb1 >> k) & 1u) << 1) | (((pb2 >> k) & 1u) << 2);
+      c[q][k] = ((pb[q][0] >> k) & 1u) | (((pb[q][1] >> k) & 1u) << 1) | (((pb[q][2] >> k) & 1u) << 2);
       if (t0 + k < nb && c[q][k] == 0u) packed += 1u << (16 * q);
     }
   }
@@ -162,37 +188,36 @@ __global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
   const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);  // also orders the tab writes
   const uint32_t excl_t = incl - packed;
   const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
-  const uint64_t E0 = a.eoff[j], E1 = a.eoff[j + 1];
   if (E1 < E0 || E1 - E0 != agg || E1 > a.esc_bytes) {
     if (tid == 0 && a.err) atomicOr(a.err, IBP_DEVERR_CORRUPT);
     return;  // block not decoded
+  }
+  // this thread's escape exponents (consecutive in the escape array per group)
+  uint32_t ex[2][kGroup];
+#pragma unroll
+  for (uint32_t q = 0; q < 2; ++q) {
+    const uint32_t t0 = q * kHalf + kGroup * tid;
+    uint64_t r = E0 + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
+#pragma unroll
+    for (uint32_t k = 0; k < kGroup; ++k) {
+      ex[q][k] = 0;
+      if (t0 + k < nb && c[q][k] == 0u) ex[q][k] = a.esc[r++];
+    }
   }
 #pragma unroll
   for (uint32_t q = 0; q < 2; ++q) {
     const uint32_t t0 = q * kHalf + kGroup * tid;
     if (t0 >= nb) continue;
-    const bool full = t0 + kGroup <= nb;
-    uint32_t sm[2];
-    if (full) {
-      const uint2 w = *reinterpret_cast<const uint2 *>(a.sm + e0 + t0);
-      sm[0] = w.x;
-      sm[1] = w.y;
-    } else {
-      sm[0] = sm[1] = 0;
-      for (uint32_t k = 0; t0 + k < nb; ++k) sm[k / 4] |= (uint32_t)a.sm[e0 + t0 + k] << (8 * (k % 4));
-    }
-    uint64_t r = E0 + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
     uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (uint32_t k = 0; k < kGroup; ++k) {
-      const uint32_t s = (sm[k / 4] >> (8 * (k % 4))) & 0xFFu;
-      uint32_t e = 0;
-      if (t0 + k < nb) e = c[q][k] ? tab[c[q][k]] : (uint32_t)a.esc[r++];
+      const uint32_t s = (sm[q][k / 4] >> (8 * (k % 4))) & 0xFFu;
+      const uint32_t e = c[q][k] ? tab[c[q][k]] : ex[q][k];
       const uint32_t v = ((s & 0x80u) << 8) | (e << 7) | (s & 0x7Fu);
       w[k / 2] |= v << (16 * (k % 2));
     }
     uint16_t *o = a.out + e0 + t0;
-    if (full) {
+    if (t0 + kGroup <= nb) {
       *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
     } else {
       for (uint32_t k = 0; t0 + k < nb; ++k) o[k] = (uint16_t)(w[k / 2] >> (16 * (k % 2)));
