@@ -18,6 +18,7 @@ constexpr uint32_t kEncTileChunks = 4096;
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
 constexpr uint32_t kDecMaxUnits = 128;
+constexpr uint32_t kGatherMaxRows = 8;   // rows per wavefront of a gather from HBM
 // Metadata count kernel: at most this many workgroups (one per CU) write partial counts.
 constexpr uint32_t kMetaMaxBlocks = 256;
 
