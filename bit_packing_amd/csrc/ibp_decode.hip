@@ -272,12 +272,7 @@ __global__ void __launch_bounds__(kBlock) decode_pos_kernel(DecodeArgs a, CodecP
     const uint64_t mi = ok ? mtab[i] : 0ull;
     const uint32_t pci = popc(mi);
     const uint32_t sv = h ? pci : 0u;
-    uint32_t x = sv;  // inclusive scan of the savings over the pass
-#pragma unroll
-    for (uint32_t o = 1; o < kWave; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, kWave);
-      if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(sv);  // inclusive scan of the savings over the pass
     const uint32_t start = lane >= i ? lane - i : 0u;  // the segment's first lane in this pass
     const uint32_t xs = __shfl(x, start == 0u ? 0u : start - 1u, kWave);
     const uint32_t before = start == 0u ? 0u : xs;

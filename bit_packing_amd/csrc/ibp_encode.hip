@@ -113,12 +113,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
       B[q] = ballot(h);
       // saved bits: an inclusive wave scan over the block's 64 chunks
       const uint32_t sv = h ? popc(m) : 0u;
-      uint32_t x = sv;
-#pragma unroll
-      for (uint32_t o = 1; o < kWave; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, kWave);
-        if (lane >= o) x += y;
-      }
+      const uint32_t x = wave_incl_scan(sv);
       svx[q] = x - sv;
       wpre[cl] = (uint16_t)x;
       if (lane == kWave - 1) bal[q * kWavesPerBlock + wave] = x;  // the block's saved bits
@@ -131,12 +126,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   // 3. compressed chunks before each 64-chunk block
   if (wave == 0) {
     const uint32_t c = kPos ? (uint32_t)bal[lane] : popc(bal[lane]);
-    uint32_t x = c;
-#pragma unroll
-    for (uint32_t o = 1; o < kWave; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o, kWave);
-      if (lane >= o) x += y;
-    }
+    const uint32_t x = wave_incl_scan(c);
     pref[lane] = x - c;
     if (lane == kWave - 1) pref[kBal] = x;
   }

@@ -29,12 +29,7 @@ constexpr uint32_t kPlane = kZipBlock / 8;              // bytes per code plane
 // Inclusive scan of v over the workgroup (256 threads); *total gets the sum.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t lane, uint32_t wave, uint32_t *wsum,
                                                uint32_t *total) {
-  uint32_t x = v;
-#pragma unroll
-  for (uint32_t o = 1; o < kWave; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
+  const uint32_t x = wave_incl_scan(v);
   if (lane == kWave - 1) wsum[wave] = x;
   __syncthreads();
   uint32_t pre = 0, all = 0;
