@@ -176,6 +176,32 @@ __device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint64_t x
   if (w2) atomicOr(&s[d + 2], w2);
 }
 
+// The same with one zero test for the whole field instead of one per dword: a
+// lane whose field is 0 issues no atomic (sparse data packs many short fields
+// into one dword, where atomics to the same address serialise), any other lane
+// ORs every dword the field can touch, parts that are 0 included (q + 32 bits,
+// q + 64 for a 64-bit field, must lie inside the array).  ubfe(x, 32 - sh, sh) is
+// x >> (32 - sh), and 0 for sh == 0.
+__device__ __forceinline__ void lds_or_bits(uint32_t *s, uint32_t q, uint32_t x) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  if (x) {
+    atomicOr(&s[d], x << sh);
+    atomicOr(&s[d + 1], __builtin_amdgcn_ubfe(x, 32u - sh, sh));
+  }
+}
+
+__device__ __forceinline__ void lds_or_bits(uint32_t *s, uint32_t q, uint16_t x) { lds_or_bits(s, q, (uint32_t)x); }
+
+__device__ __forceinline__ void lds_or_bits(uint32_t *s, uint32_t q, uint64_t x) {
+  const uint32_t d = q >> 5, sh = q & 31u;
+  const uint32_t x0 = (uint32_t)x, x1 = (uint32_t)(x >> 32);
+  if (x) {
+    atomicOr(&s[d], x0 << sh);
+    atomicOr(&s[d + 1], (x1 << sh) | __builtin_amdgcn_ubfe(x0, 32u - sh, sh));
+    atomicOr(&s[d + 2], __builtin_amdgcn_ubfe(x1, 32u - sh, sh));
+  }
+}
+
 // ------------------------------------------------------------------ global memory
 
 __device__ __forceinline__ uint4 load16(const uint8_t *src, uint64_t blk) {

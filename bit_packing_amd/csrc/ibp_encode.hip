@@ -77,10 +77,15 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
 
   // 2. chunks, participation bits; clear the image meanwhile
   T v[kQ];
+  if (nch == kEncTileChunks) {  // every tile but possibly the last: no bounds tests
 #pragma unroll
-  for (uint32_t q = 0; q < kQ; ++q) {
-    const uint32_t cl = q * kBlock + tid;
-    v[q] = cl < nch ? in[cl] : (T)0;
+    for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kBlock + tid];
+  } else {
+#pragma unroll
+    for (uint32_t q = 0; q < kQ; ++q) {
+      const uint32_t cl = q * kBlock + tid;
+      v[q] = cl < nch ? in[cl] : (T)0;
+    }
   }
   for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kBlock)
     *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
@@ -152,8 +157,18 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   if (tid == 0) lookback_publish(a.status, t, agg);
 
   // 4. pack into LDS, from bit 0 of the image (the tile's first bit); the store
-  //    shifts the image to the tile's place in the stream
-  const uint32_t lb0 = 0u;
+  //    shifts the image to the tile's place in the stream.  Segment s0's header
+  //    starts at image bit s0 (W + 1) - (bits saved before s0); its payloads
+  //    follow the m header bits, so chunk cl's payload starts at
+  //    s0 + m + cl W - (bits saved by the tile chunks before cl).
+  const uint32_t lane_bits = lane * W;
+  const uint32_t my_pref = pref[lane];  // lane b: the value for 64-chunk block b
+  auto pref_at = [&](uint32_t b) -> uint32_t {  // b wave-uniform
+    return (uint32_t)__builtin_amdgcn_readlane((int)my_pref, (int)b);
+  };
+  auto seg_start = [&](uint32_t c) -> uint32_t {  // first chunk of the segment holding tile chunk c
+    return a.s_log2 != kNotPow2 ? (c >> a.s_log2) << a.s_log2 : (c / a.S) * a.S;
+  };
   const uint32_t i_lane = lane & (a.S - 1u);                   // small-S: index in segment
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
 #pragma unroll
@@ -164,47 +179,66 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     const uint32_t cl = cb + lane;
     const bool valid = cl < nch;
     const bool h = __builtin_amdgcn_inverse_ballot_w64(B[q]);
-    // saved bits of the tile chunks before this one
-    const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : __umul24(pc, uniform(pref[blk]) + count_below(B[q]));
     auto payload = [&]() -> T {
       if constexpr (kPos) {
-        const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
-        return h ? extract_var<T>(v[q], ~mtab[ip[q]] & full) : v[q];
+        return h ? extract_var<T>(v[q], ~mtab[ip[q]] & low_lanes(W)) : v[q];
       } else {
         return h ? extract_free<T, NR>(v[q], p.runs) : v[q];
       }
     };
-    uint32_t i, s0, gs;
     if constexpr (kMode == kModeLargeS) {
-      s0 = (cb / a.S) * a.S;  // uniform: the block lies in one segment
-      i = cl - s0;
-      gs = kPos ? uniform(pref[s0 >> 6]) : pc * uniform(pref[s0 >> 6]);
-      const uint32_t m = min(a.S, nch - s0);
-      const uint32_t segbase = lb0 + s0 * (W + 1) - gs;
-      if (lane == 0) lds_or_field(obuf, segbase + (cb - s0), B[q]);  // 64 header bits
-      const uint32_t pos = segbase + m + i * W - (c_cl - gs);
-      if (valid) lds_or_field(obuf, pos, payload());
-    } else if constexpr (kMode == kModeSmallS) {
-      s0 = cb + (lane & ~(a.S - 1u));
-      i = i_lane;
-      gs = kPos ? cost(min(s0, nch - 1u)) : pc * (uniform(pref[blk]) + popc(B[q] & seg_below));
-      const uint32_t m = min(a.S, nch - min(s0, nch));
-      const uint32_t segbase = lb0 + s0 * (W + 1) - gs;
-      if (valid && i == 0) lds_or_field(obuf, segbase, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
-      const uint32_t pos = segbase + m + i * W - (c_cl - gs);
-      if (valid) lds_or_field(obuf, pos, payload());
-    } else {
-      const uint32_t r = cl / a.S;
-      s0 = r * a.S;
-      i = cl - s0;
-      if (valid) {
-        gs = cost(s0);
+      // the block lies inside one segment: everything but the lane's own count is uniform
+      if constexpr (kPos) {
+        // position metadata: header written here, saved-bit prefixes read from LDS
+        const uint32_t s0 = (cb / a.S) * a.S;
+        const uint32_t gs = uniform(pref[s0 >> 6]);
         const uint32_t m = min(a.S, nch - s0);
-        const uint32_t segbase = lb0 + s0 * (W + 1) - gs;
-        if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
-        const uint32_t pos = segbase + m + i * W - (c_cl - gs);
-        lds_or_field(obuf, pos, payload());
+        const uint32_t segbase = s0 * (W + 1) - gs;
+        if (lane == 0) lds_or_field(obuf, segbase + (cb - s0), B[q]);  // 64 header bits
+        const uint32_t c_cl = uniform(pref[blk]) + svx[q];
+        if (valid) lds_or_field(obuf, segbase + m + (cl - s0) * W - (c_cl - gs), payload());
+      } else {
+        const uint32_t s0 = seg_start(cb);
+        const uint32_t m = min(a.S, nch - s0);
+        const uint32_t saved = __umul24(pc, pref_at(blk) + count_below(B[q]));
+        const uint32_t pos = (s0 + m + cb * W) + lane_bits - saved;
+        lds_or_bits(obuf, valid ? pos : 0u, payload());  // invalid lanes hold 0
       }
+    } else if constexpr (kMode == kModeSmallS) {
+      const uint32_t s0 = cb + (lane & ~(a.S - 1u));
+      const uint32_t m = min(a.S, nch - min(s0, nch));
+      if constexpr (kPos) {
+        const uint32_t gs = cost(min(s0, nch - 1u));
+        const uint32_t segbase = s0 * (W + 1) - gs;
+        if (valid && i_lane == 0) lds_or_field(obuf, segbase, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
+        const uint32_t c_cl = uniform(pref[blk]) + svx[q];
+        if (valid) lds_or_field(obuf, segbase + m + i_lane * W - (c_cl - gs), payload());
+      } else {
+        const uint32_t gs = pc * (pref_at(blk) + popc(B[q] & seg_below));
+        if (valid && i_lane == 0) lds_or_bits(obuf, s0 * (W + 1) - gs, (uint32_t)((B[q] >> lane) & low_lanes(m)));
+        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(blk) + count_below(B[q]));
+        lds_or_bits(obuf, valid ? pos : 0u, payload());
+      }
+    } else {
+      if (valid) {
+        const uint32_t s0 = seg_start(cl);
+        const uint32_t i = cl - s0;
+        const uint32_t gs = cost(s0);
+        const uint32_t m = min(a.S, nch - s0);
+        const uint32_t segbase = s0 * (W + 1) - gs;
+        if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
+        const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : __umul24(pc, uniform(pref[blk]) + count_below(B[q]));
+        lds_or_field(obuf, segbase + m + i * W - (c_cl - gs), payload());
+      }
+    }
+  }
+  if constexpr (kMode == kModeLargeS && !kPos) {
+    // the headers: lane q of each wavefront ORs in block q * kWavesPerBlock + wave's
+    // 64 participation bits
+    const uint32_t blk = lane * kWavesPerBlock + wave, cb = blk * kWave;
+    if (lane < kQ && cb < nch) {
+      const uint32_t s0 = seg_start(cb);
+      lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6], bal[blk]);
     }
   }
   __syncthreads();
@@ -252,15 +286,21 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   uint32_t *gdst = a.stream + ((excl >> 7) << 2);
   const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
   for (uint32_t d = lo + tid; d < a4; d += kBlock) gdst[d] = out_dw(d);
+  // interior: output dwords [d, d + 4) are image bits from 32 d - sh0 on, i.e. from
+  // bit t = 128 - sh0 of the eight image dwords [d - 4, d + 4) (two aligned 16-byte
+  // LDS reads; the image is zero past its last bit and a4 >= 4 unless sh0 == 0)
+  const uint32_t t_sh = 128u - sh0, jt = t_sh >> 5, st = t_sh & 31u;
+  auto al = [&](uint32_t hi, uint32_t lo) -> uint32_t { return __builtin_amdgcn_alignbit(hi, lo, st); };
   for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kBlock) {
-    const int32_t i = (int32_t)d - (int32_t)dq;
-    const uint32_t p = img(i - 1), x0 = img(i), x1 = img(i + 1), x2 = img(i + 2), x3 = img(i + 3);
+    const uint4 A = *reinterpret_cast<const uint4 *>(obuf + ((max(d, 4u) - 4u) & ~3u));
+    const uint4 C = *reinterpret_cast<const uint4 *>(obuf + d);
     uint4 o;
-    if (sh) {
-      o = make_uint4((x0 << sh) | (p >> (32u - sh)), (x1 << sh) | (x0 >> (32u - sh)), (x2 << sh) | (x1 >> (32u - sh)),
-                     (x3 << sh) | (x2 >> (32u - sh)));
-    } else {
-      o = make_uint4(x0, x1, x2, x3);
+    switch (jt) {  // uniform
+      case 0: o = make_uint4(al(A.y, A.x), al(A.z, A.y), al(A.w, A.z), al(C.x, A.w)); break;
+      case 1: o = make_uint4(al(A.z, A.y), al(A.w, A.z), al(C.x, A.w), al(C.y, C.x)); break;
+      case 2: o = make_uint4(al(A.w, A.z), al(C.x, A.w), al(C.y, C.x), al(C.z, C.y)); break;
+      case 3: o = make_uint4(al(C.x, A.w), al(C.y, C.x), al(C.z, C.y), al(C.w, C.z)); break;
+      default: o = C; break;  // sh0 == 0
     }
     *reinterpret_cast<uint4 *>(gdst + d) = o;
   }
