@@ -339,10 +339,14 @@ static int decode_common(const CodecParams &p, const uint64_t *pmask, const uint
   a.S = S;
   a.s_log2 = log2_if_pow2(S);
   // Rows read over PCIe go one per wavefront: more independent read streams keep
-  // more host reads in flight.  From HBM a wavefront takes about 512 chunks, and a
-  // gather at most 8 rows (short rows: more wavefronts, shorter chains per wavefront).
-  a.G = (gather && host_stream) ? 1u : dec_units_per_tile(S);
-  if (gather && a.G > kGatherMaxRows) a.G = kGatherMaxRows;
+  // more host reads in flight.  From HBM a wavefront takes about 512 chunks of a
+  // contiguous stream, and about 1024 chunks, at most kGatherMaxRows rows, of a
+  // gather (its dependent id -> offset -> row reads favour one wave generation).
+  if (gather)
+    a.G = host_stream ? 1u : (S >= 2 * kDecTileChunks / kGatherMaxRows ? (S >= 2 * kDecTileChunks ? 1u : 2 * kDecTileChunks / S)
+                                                                       : kGatherMaxRows);
+  else
+    a.G = dec_units_per_tile(S);
   const uint32_t tile_chunks = a.G * S;
   if (gather) {
     a.slot_dw = ((S * (p.W + 1) + 127) / 128 + 1) * 4;

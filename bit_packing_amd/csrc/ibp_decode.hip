@@ -138,9 +138,45 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
       my_whole = my_first >= whole ? 0u : (uint32_t)min((uint64_t)unb[r], whole - my_first);
     }
     wave_lds_sync();
-    // b. stage every row into its slot: whole blocks first, four loads in flight per
-    //    lane before any LDS write
-    if (a.S >= kWave) {
+    // b. stage every row into its slot: whole blocks first, all loads in flight
+    //    before any LDS write
+    if (a.S >= kWave && a.slot_dw <= 4u * kWave) {
+      // a row's blocks fit one 16-byte load per lane: one load instruction per row,
+      // with the row's base address scalar
+      static_assert(kGatherMaxRows == 8, "one named register per row");
+      auto fetch = [&](uint32_t r, uint4 &t) {
+        if (r < nu) {  // uniform
+          const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
+          const uint64_t f_r = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_first >> 32), (int)r) << 32) |
+                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_first, (int)r);
+          if (lane < n_r) t = *reinterpret_cast<const uint4 *>(a.stream + f_r * 16u + (lane << 4));
+        }
+      };
+      auto put = [&](uint32_t r, const uint4 &t) {
+        if (r < nu) {
+          const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
+          if (lane < n_r) *reinterpret_cast<uint4 *>(stg + r * a.slot_dw + 4u * lane) = t;
+        }
+      };
+      uint4 t0, t1, t2, t3, t4, t5, t6, t7;
+      fetch(0, t0);
+      fetch(1, t1);
+      fetch(2, t2);
+      fetch(3, t3);
+      fetch(4, t4);
+      fetch(5, t5);
+      fetch(6, t6);
+      fetch(7, t7);
+      put(0, t0);
+      put(1, t1);
+      put(2, t2);
+      put(3, t3);
+      put(4, t4);
+      put(5, t5);
+      put(6, t6);
+      put(7, t7);
+    } else if (a.S >= kWave) {
+      // four loads in flight per lane before any LDS write
       // one load instruction per (row, 64 blocks): the row's base address is scalar
       uint32_t r = 0, j0 = 0;
       auto item = [&](uint4 &t, uint32_t &d) {
@@ -214,7 +250,9 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
 
   // c. decode
   T *out = static_cast<T *>(a.out) + chunk0;
-  if constexpr (kMode == kModeLargeS)
+  if constexpr (kMode == kModeLargeS && kGather)
+    err |= decode_rows<T, NR>(a, p, stg, lbeg, lend, nu, out, lane);
+  else if constexpr (kMode == kModeLargeS)
     err |= decode_large_s<T, NR>(a, p, stg, lbeg, lend, nu, nch, out, lane);
   else if constexpr (kMode == kModeSmallS)
     err |= decode_small_s<T, kGather, NR>(a, p, stg, lbeg, lend, nch, out, lane);
