@@ -250,14 +250,18 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
 
   // c. decode
   T *out = static_cast<T *>(a.out) + chunk0;
-  if constexpr (kMode == kModeLargeS && kGather)
-    err |= decode_rows<T, NR>(a, p, stg, lbeg, lend, nu, out, lane);
-  else if constexpr (kMode == kModeLargeS)
-    err |= decode_large_s<T, NR>(a, p, stg, lbeg, lend, nu, nch, out, lane);
-  else if constexpr (kMode == kModeSmallS)
+  if constexpr (kMode == kModeLargeS) {
+    // gathered rows are whole segments, and so is every segment of a contiguous tile
+    // but possibly the stream's last
+    if (kGather || nch == nu * a.S)
+      err |= decode_rows<T, NR>(a, p, stg, lbeg, lend, nu, out, lane);
+    else
+      err |= decode_large_s<T, NR>(a, p, stg, lbeg, lend, nu, nch, out, lane);
+  } else if constexpr (kMode == kModeSmallS) {
     err |= decode_small_s<T, kGather, NR>(a, p, stg, lbeg, lend, nch, out, lane);
-  else
+  } else {
     err |= decode_general<T, kGather>(a, p, stg, lbeg, lend, gseg, nch, out, lane);
+  }
   if (err && a.err) atomicOr(a.err, err);
 }
 
