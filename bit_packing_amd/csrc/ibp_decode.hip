@@ -140,33 +140,50 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
     wave_lds_sync();
     // b. stage every row into its slot: whole blocks first, all loads in flight
     //    before any LDS write
-    if (a.S >= kWave && a.slot_dw <= 4u * kWave) {
-      // a row's blocks fit one 16-byte load per lane: one load instruction per row,
-      // with the row's base address scalar
+    if (a.S >= kWave && a.slot_dw <= 4u * kWave && whole > 0) {
+      // a row's blocks fit one 16-byte load per lane: one load instruction per row
+      // (row base address scalar), all kGatherMaxRows of them unconditional, so the
+      // compiler can wait for each row's load alone.  Lanes past a row's whole
+      // blocks, and rows past the tile, read a block that exists and write it to
+      // the 16 spare bytes after the slots.
       static_assert(kGatherMaxRows == 8, "one named register per row");
-      auto fetch = [&](uint32_t r, uint4 &t) {
-        if (r < nu) {  // uniform
-          const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
-          const uint64_t f_r = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_first >> 32), (int)r) << 32) |
-                               (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_first, (int)r);
-          if (lane < n_r) t = *reinterpret_cast<const uint4 *>(a.stream + f_r * 16u + (lane << 4));
-        }
+      const uint32_t spare = a.G * a.slot_dw;
+      auto fetch = [&](uint32_t r) -> uint4 {
+        const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
+        const uint64_t f_r = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(my_first >> 32), (int)r) << 32) |
+                             (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)my_first, (int)r);
+        const uint64_t blk = min(f_r + min(lane, n_r ? n_r - 1u : 0u), whole - 1u);
+        return *reinterpret_cast<const uint4 *>(a.stream + blk * 16u);
       };
       auto put = [&](uint32_t r, const uint4 &t) {
-        if (r < nu) {
-          const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
-          if (lane < n_r) *reinterpret_cast<uint4 *>(stg + r * a.slot_dw + 4u * lane) = t;
-        }
+        const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
+        *reinterpret_cast<uint4 *>(stg + (lane < n_r ? r * a.slot_dw + 4u * lane : spare)) = t;
       };
-      uint4 t0, t1, t2, t3, t4, t5, t6, t7;
-      fetch(0, t0);
-      fetch(1, t1);
-      fetch(2, t2);
-      fetch(3, t3);
-      fetch(4, t4);
-      fetch(5, t5);
-      fetch(6, t6);
-      fetch(7, t7);
+      const uint4 t0 = fetch(0), t1 = fetch(1), t2 = fetch(2), t3 = fetch(3);
+      const uint4 t4 = fetch(4), t5 = fetch(5), t6 = fetch(6), t7 = fetch(7);
+      if constexpr (kMode == kModeLargeS) {
+        if (!ballot(tail_row)) {
+          // decode each row as soon as its own blocks have arrived, while the
+          // later rows' loads are still in flight
+          T *out = static_cast<T *>(a.out) + chunk0;
+          auto row = [&](uint32_t r, const uint4 &t) {
+            put(r, t);
+            wave_lds_sync();
+            if (r < nu)
+              err |= decode_row<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S, lane);
+          };
+          row(0, t0);
+          row(1, t1);
+          row(2, t2);
+          row(3, t3);
+          row(4, t4);
+          row(5, t5);
+          row(6, t6);
+          row(7, t7);
+          if (err && a.err) atomicOr(a.err, err);
+          return;
+        }
+      }
       put(0, t0);
       put(1, t1);
       put(2, t2);

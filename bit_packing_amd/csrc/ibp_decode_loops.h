@@ -57,34 +57,39 @@ __device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const Co
   return err;
 }
 
-// Gather with S a multiple of 64: every row is a whole segment of S chunks, so
-// every pass is full and the per-pass bookkeeping reduces to two running bit
-// positions: hp, the header bit of the pass's first chunk, and base, the payload
-// bit it would have if every earlier chunk of the row were raw.
+// A whole segment of S chunks (S a multiple of 64) whose bits are local bits
+// [lb, le): every pass is full, so the per-pass bookkeeping reduces to two
+// running bit positions: hp, the header bit of the pass's first chunk, and base,
+// the payload bit it would have if every earlier chunk of the segment were raw.
+template <typename T, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
+                                               uint32_t le, T *o, uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  if (lb == kBad) return 0u;
+  const uint32_t pc = p.pc;
+  const T bitval = (T)p.bitval;
+  const uint32_t lane_bits = lane * W;
+  o += lane;
+  uint32_t hp = lb, base = lb + S;
+  for (uint32_t q = 0; q < S; q += kWave) {
+    const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
+    const uint32_t pos = base + lane_bits - __umul24(pc, count_below(H));
+    const T x = lds_field<T>(stg, pos);
+    o[q] = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
+    base += kWave * W - pc * popc(H);
+    hp += kWave;
+  }
+  return base != le ? IBP_DEVERR_CORRUPT : 0u;
+}
+
+// Units that are all whole segments of S chunks, S a multiple of 64.
 template <typename T, uint32_t NR>
 __device__ __forceinline__ uint32_t decode_rows(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
                                                 const uint32_t *lbeg, const uint32_t *lend, uint32_t nu, T *out,
                                                 uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  const uint32_t pc = p.pc, S = a.S;
-  const T bitval = (T)p.bitval;
-  const uint32_t lane_bits = lane * W;
   uint32_t err = 0;
-  for (uint32_t r = 0; r < nu; ++r) {
-    const uint32_t lb = uniform(lbeg[r]);
-    if (lb == kBad) continue;
-    T *o = out + (uint64_t)r * S + lane;
-    uint32_t hp = lb, base = lb + S;
-    for (uint32_t q = 0; q < S; q += kWave) {
-      const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
-      const uint32_t pos = base + lane_bits - __umul24(pc, count_below(H));
-      const T x = lds_field<T>(stg, pos);
-      o[q] = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
-      base += kWave * W - pc * popc(H);
-      hp += kWave;
-    }
-    if (base != uniform(lend[r])) err |= IBP_DEVERR_CORRUPT;
-  }
+  for (uint32_t r = 0; r < nu; ++r)
+    err |= decode_row<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S, lane);
   return err;
 }
 
