@@ -23,6 +23,8 @@
 //  - S dividing 64: a pass holds 64/S whole segments; a ballot of the
 //    participation bits, masked to the lane's segment;
 //  - any other S: a ballot plus a per-segment carry kept in LDS.
+#include <type_traits>
+
 #include "ibp_decode_loops.h"
 
 namespace ibp {
@@ -282,6 +284,36 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
   if (err && a.err) atomicOr(a.err, err);
 }
 
+// Position metadata, a whole segment of S chunks (S a multiple of 64) at local
+// bits [lb, le): chunk i = q + lane of pass q saves popcount(Mask_i) bits when it
+// matches, so its payload bit is base + lane W minus the savings of the chunks
+// before it in the pass (an inclusive wave scan, less its own); base then drops by
+// the pass's total, the scan's last lane.
+template <typename T>
+__device__ __forceinline__ uint32_t decode_pos_row(uint32_t S, const uint64_t *mtab, const uint64_t *btab,
+                                                   const uint32_t *stg, uint32_t lb, uint32_t le, T *o,
+                                                   uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  using U = typename std::conditional<(W > 32), uint64_t, uint32_t>::type;
+  constexpr U kFull = W >= 64 ? ~(U)0 : (U)((1ull << (W & 63)) - 1ull);
+  if (lb == kBad) return 0u;
+  const uint32_t lane_bits = lane * W;
+  o += lane;
+  uint32_t hp = lb, base = lb + S;
+  for (uint32_t q = 0; q < S; q += kWave) {
+    const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
+    const bool h = __builtin_amdgcn_inverse_ballot_w64(H);
+    const U m = (U)mtab[q + lane];
+    const uint32_t sv = h ? popc_u(m) : 0u;
+    const uint32_t x = wave_incl_scan(sv);
+    const T xv = lds_field<T>(stg, base + lane_bits - (x - sv));
+    o[q] = h ? (T)(deposit_runs<U>((U)xv, ~m & kFull) | (U)btab[q + lane]) : xv;
+    base += kWave * W - (uint32_t)__builtin_amdgcn_readlane((int)x, kWave - 1);
+    hp += kWave;
+  }
+  return base != le ? IBP_DEVERR_CORRUPT : 0u;
+}
+
 // Contiguous decompression with position-dependent metadata: chunk position i
 // of a segment has its own Mask_i / Bitval_i (device tables, copied to LDS).  The
 // tile is staged as in decode_kernel.  Per pass of 64 tile chunks a lane's payload
@@ -315,10 +347,19 @@ __global__ void __launch_bounds__(kBlock) decode_pos_kernel(DecodeArgs a, CodecP
   const uint32_t nch = (uint32_t)min((uint64_t)nu * a.S, a.n_chunks - chunk0);
   uint32_t err = 0;
   if (!stage_tile<W>(a, u0, nu, nch, stg, lbeg, lend, lane, err)) return;
+  T *out = static_cast<T *>(a.out) + chunk0;
+  if (a.S % kWave == 0 && nch == nu * a.S) {
+    // whole segments, S a multiple of 64: every pass lies inside one segment
+    wave_lds_sync();
+    for (uint32_t r = 0; r < nu; ++r)
+      err |= decode_pos_row<T>(a.S, mtab, btab, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S,
+                               lane);
+    if (err && a.err) atomicOr(a.err, err);
+    return;
+  }
   for (uint32_t r = lane; r < nu; r += kWave) carry[r] = 0;
   wave_lds_sync();
 
-  T *out = static_cast<T *>(a.out) + chunk0;
   for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
     const uint32_t cl = p0 + lane;
     const bool valid = cl < nch;

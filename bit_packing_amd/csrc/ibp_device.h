@@ -127,6 +127,41 @@ template <typename T> __device__ __forceinline__ T deposit_var(T x, uint64_t F) 
   return (T)out;
 }
 
+// The same, one step per run with all-integer-width operations on U (uint32_t
+// for W <= 32, uint64_t for W = 64): R = F & ~(F + lowest set bit) is F's lowest
+// run of consecutive set positions.  Shift counts are masked to the width, which
+// only matters for a run covering all of U, after which F is 0 and the loop ends.
+template <typename U> __device__ __forceinline__ uint32_t ctz_u(U v) {
+  return sizeof(U) > 4 ? (uint32_t)__builtin_ctzll((uint64_t)v) : (uint32_t)__builtin_ctz((uint32_t)v);
+}
+template <typename U> __device__ __forceinline__ uint32_t popc_u(U v) {
+  return sizeof(U) > 4 ? (uint32_t)__builtin_popcountll((uint64_t)v) : (uint32_t)__builtin_popcount((uint32_t)v);
+}
+
+template <typename U> __device__ __forceinline__ U deposit_runs(U x, U F) {
+  constexpr uint32_t kMask = sizeof(U) * 8 - 1;
+  U out = 0;
+  while (F) {
+    const U R = F & ~(F + (F & (U)(0 - F)));
+    out |= (x << ctz_u(F)) & R;
+    x >>= popc_u(R) & kMask;
+    F ^= R;
+  }
+  return out;
+}
+
+template <typename U> __device__ __forceinline__ U extract_runs(U v, U F) {
+  U out = 0;
+  uint32_t k = 0;
+  while (F) {
+    const U R = F & ~(F + (F & (U)(0 - F)));
+    out |= ((v & R) >> ctz_u(F)) << k;
+    k += popc_u(R);
+    F ^= R;
+  }
+  return out;
+}
+
 // ------------------------------------------------------------------ LDS bit fields
 
 __device__ __forceinline__ uint32_t lds_bit(const uint32_t *s, uint32_t q) {
