@@ -8,6 +8,8 @@
 // workgroup sizes its tile, obtains the tile's starting bit through a decoupled
 // look-back over its predecessors (Merrill & Garland, "Single-pass Parallel
 // Prefix Scan with Decoupled Look-back", 2016), and packs the tile in LDS.
+#include <type_traits>
+
 #include "ibp_device.h"
 
 namespace ibp {
@@ -181,7 +183,8 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     const bool h = __builtin_amdgcn_inverse_ballot_w64(B[q]);
     auto payload = [&]() -> T {
       if constexpr (kPos) {
-        return h ? extract_var<T>(v[q], ~mtab[ip[q]] & low_lanes(W)) : v[q];
+        using U = typename std::conditional<(W > 32), uint64_t, uint32_t>::type;
+        return h ? (T)extract_runs<U>((U)v[q], (U)(~mtab[ip[q]] & low_lanes(W))) : v[q];
       } else {
         return h ? extract_free<T, NR>(v[q], p.runs) : v[q];
       }
