@@ -49,11 +49,11 @@ enum : uint32_t {
 // scan per 64-chunk block plus a scan over the blocks), and the extraction walks
 // the runs of each lane's own free positions.
 template <typename T, uint32_t kMode, uint32_t NR, bool kPos>
-__global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParams p) {
+__global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
-  constexpr uint32_t kQ = kEncTileChunks / kBlock;   // passes of 256 chunks
-  constexpr uint32_t kBal = kEncTileChunks / kWave;  // 64-chunk blocks per tile
-  static_assert(kBal == kWave, "one ballot word per lane of the prefix scan");
+  constexpr uint32_t kQ = kEncTileChunks / kEncBlock;  // passes of kEncBlock chunks
+  constexpr uint32_t kBal = kEncTileChunks / kWave;    // 64-chunk blocks per tile
+  static_assert(kBal <= kWave, "one ballot word per lane of the prefix scan");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   uint32_t *obuf = smem;
   uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // kBal words
@@ -81,26 +81,26 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   T v[kQ];
   if (nch == kEncTileChunks) {  // every tile but possibly the last: no bounds tests
 #pragma unroll
-    for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kBlock + tid];
+    for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kEncBlock + tid];
   } else {
 #pragma unroll
     for (uint32_t q = 0; q < kQ; ++q) {
-      const uint32_t cl = q * kBlock + tid;
+      const uint32_t cl = q * kEncBlock + tid;
       v[q] = cl < nch ? in[cl] : (T)0;
     }
   }
-  for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kBlock)
+  for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kEncBlock)
     *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
-  uint32_t ip[kQ];   // kPos: position of chunk q * kBlock + tid in its segment (tiles start on a segment)
+  uint32_t ip[kQ];   // kPos: position of chunk q * kEncBlock + tid in its segment (tiles start on a segment)
   uint32_t svx[kQ];  // kPos: saved bits of the earlier chunks of its 64-chunk block
   if constexpr (kPos) {
     const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
-    for (uint32_t i = tid; i < a.S; i += kBlock) {
+    for (uint32_t i = tid; i < a.S; i += kEncBlock) {
       const uint64_t m = a.pmask[i] & full;
       mtab[i] = m;
       btab[i] = a.pbitval[i] & m;
     }
-    const uint32_t step = kBlock % a.S;
+    const uint32_t step = kEncBlock % a.S;
     uint32_t i0 = tid % a.S;
 #pragma unroll
     for (uint32_t q = 0; q < kQ; ++q) {
@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
-    const uint32_t cl = q * kBlock + tid;
+    const uint32_t cl = q * kEncBlock + tid;
     if constexpr (kPos) {
       const uint64_t m = mtab[ip[q]];
       const bool h = cl < nch && ((v[q] ^ (T)btab[ip[q]]) & (T)m) == 0;
@@ -123,18 +123,18 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
       const uint32_t x = wave_incl_scan(sv);
       svx[q] = x - sv;
       wpre[cl] = (uint16_t)x;
-      if (lane == kWave - 1) bal[q * kWavesPerBlock + wave] = x;  // the block's saved bits
+      if (lane == kWave - 1) bal[q * kEncWaves + wave] = x;  // the block's saved bits
     } else {
       B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
-      if (lane == 0) bal[q * kWavesPerBlock + wave] = B[q];
+      if (lane == 0) bal[q * kEncWaves + wave] = B[q];
     }
   }
   __syncthreads();
   // 3. compressed chunks before each 64-chunk block
   if (wave == 0) {
-    const uint32_t c = kPos ? (uint32_t)bal[lane] : popc(bal[lane]);
+    const uint32_t c = lane < kBal ? (kPos ? (uint32_t)bal[lane] : popc(bal[lane])) : 0u;
     const uint32_t x = wave_incl_scan(c);
-    pref[lane] = x - c;
+    if (lane < kBal) pref[lane] = x - c;
     if (lane == kWave - 1) pref[kBal] = x;
   }
   __syncthreads();
@@ -164,7 +164,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   //    follow the m header bits, so chunk cl's payload starts at
   //    s0 + m + cl W - (bits saved by the tile chunks before cl).
   const uint32_t lane_bits = lane * W;
-  const uint32_t my_pref = pref[lane];  // lane b: the value for 64-chunk block b
+  const uint32_t my_pref = lane <= kBal ? pref[lane] : 0u;  // lane b: the value for 64-chunk block b
   auto pref_at = [&](uint32_t b) -> uint32_t {  // b wave-uniform
     return (uint32_t)__builtin_amdgcn_readlane((int)my_pref, (int)b);
   };
@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
-    const uint32_t blk = q * kWavesPerBlock + wave;  // this wavefront's 64-chunk block
+    const uint32_t blk = q * kEncWaves + wave;  // this wavefront's 64-chunk block
     const uint32_t cb = blk * kWave;                 // its first tile chunk
     if (cb >= nch) continue;                         // uniform
     const uint32_t cl = cb + lane;
@@ -236,9 +236,9 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     }
   }
   if constexpr (kMode == kModeLargeS && !kPos) {
-    // the headers: lane q of each wavefront ORs in block q * kWavesPerBlock + wave's
+    // the headers: lane q of each wavefront ORs in block q * kEncWaves + wave's
     // 64 participation bits
-    const uint32_t blk = lane * kWavesPerBlock + wave, cb = blk * kWave;
+    const uint32_t blk = lane * kEncWaves + wave, cb = blk * kWave;
     if (lane < kQ && cb < nch) {
       const uint32_t s0 = seg_start(cb);
       lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6], bal[blk]);
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   }
 
   // 6. segment offsets
-  for (uint32_t r = tid; r < nsegt; r += kBlock)
+  for (uint32_t r = tid; r < nsegt; r += kEncBlock)
     a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)cost(r * a.S);
   if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
 
@@ -288,13 +288,13 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
   const uint32_t hi = last_d + 1u - ((has_tail && !last) ? 1u : 0u);  // [lo, hi) stored directly
   uint32_t *gdst = a.stream + ((excl >> 7) << 2);
   const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
-  for (uint32_t d = lo + tid; d < a4; d += kBlock) gdst[d] = out_dw(d);
+  for (uint32_t d = lo + tid; d < a4; d += kEncBlock) gdst[d] = out_dw(d);
   // interior: output dwords [d, d + 4) are image bits from 32 d - sh0 on, i.e. from
   // bit t = 128 - sh0 of the eight image dwords [d - 4, d + 4) (two aligned 16-byte
   // LDS reads; the image is zero past its last bit and a4 >= 4 unless sh0 == 0)
   const uint32_t t_sh = 128u - sh0, jt = t_sh >> 5, st = t_sh & 31u;
   auto al = [&](uint32_t hi, uint32_t lo) -> uint32_t { return __builtin_amdgcn_alignbit(hi, lo, st); };
-  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kBlock) {
+  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kEncBlock) {
     const uint4 A = *reinterpret_cast<const uint4 *>(obuf + ((max(d, 4u) - 4u) & ~3u));
     const uint4 C = *reinterpret_cast<const uint4 *>(obuf + d);
     uint4 o;
@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a, CodecParam
     }
     *reinterpret_cast<uint4 *>(gdst + d) = o;
   }
-  for (uint32_t d = e4 + tid; d < hi; d += kBlock) gdst[d] = out_dw(d);
+  for (uint32_t d = e4 + tid; d < hi; d += kEncBlock) gdst[d] = out_dw(d);
   if (tid == 0) {
     if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | out_dw(last_d));
     if (has_head) {
@@ -340,7 +340,7 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos>), dim3((uint32_t)a.ntiles), dim3(kBlock), shmem, s, a, p);
+  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos>), dim3((uint32_t)a.ntiles), dim3(kEncBlock), shmem, s, a, p);
   return hipGetLastError();
 }
 

@@ -12,8 +12,13 @@ constexpr uint32_t kBlock = 256;        // threads per workgroup for every kerne
 constexpr uint32_t kWavesPerBlock = kBlock / kWave;
 constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-bit chunk
 
-// Compression tile: a workgroup sizes, offsets and packs about this many chunks.
-constexpr uint32_t kEncTileChunks = 4096;
+// Compression: a workgroup of kEncBlock threads sizes, offsets and packs a tile
+// of about kEncTileChunks chunks (16 per thread).  Measured on the five
+// workloads: 128- and 64-thread workgroups (2048- and 1024-chunk tiles) were
+// 10-50% slower, their per-tile costs spread over fewer chunks.
+constexpr uint32_t kEncBlock = 256;
+constexpr uint32_t kEncWaves = kEncBlock / kWave;
+constexpr uint32_t kEncTileChunks = kEncBlock * 16;
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
