@@ -140,11 +140,26 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   }
 }
 
+// Bits 0..3 of x spread to bit 0 of bytes 0..3 (bit k -> bit 8k): the shifted
+// copies x, x << 7, x << 14, x << 21 do not overlap, so the product has no carries.
+__device__ __forceinline__ uint32_t spread4(uint32_t x) { return __umul24(x & 0xFu, 0x00204081u) & 0x01010101u; }
+
+// Bytes i of the result: 0 if byte i of x is 0, else 0x80 (bytes of x at most 0x7F).
+__device__ __forceinline__ uint32_t nonzero_bytes(uint32_t x) { return (x + 0x7F7F7F7Fu) & 0x80808080u; }
+
+// BF16 words of two elements from their sign-mantissa and exponent bytes placed
+// in the low bytes of the 16-bit halves of sp and ep.
+__device__ __forceinline__ uint32_t bf16_pair(uint32_t sp, uint32_t ep) {
+  return ((sp << 8) & 0x80008000u) | (ep << 7) | (sp & 0x007F007Fu);
+}
+
 __global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
-  __shared__ uint32_t tab[8];
   __shared__ uint32_t wsum[kWavesPerBlock];
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
-  if (tid < 7) tab[tid + 1] = a.table[tid];
+  // exponent of code c in byte c of (thi:tlo); byte 0 (escape) is 0
+  const uint32_t tlo = ((uint32_t)a.table[0] << 8) | ((uint32_t)a.table[1] << 16) | ((uint32_t)a.table[2] << 24);
+  const uint32_t thi = (uint32_t)a.table[3] | ((uint32_t)a.table[4] << 8) | ((uint32_t)a.table[5] << 16) |
+                       ((uint32_t)a.table[6] << 24);
   const uint64_t j = blockIdx.x;
   const uint64_t e0 = j * kZipBlock;
   const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
@@ -168,53 +183,60 @@ __global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
       for (uint32_t k = 0; t0 + k < nb; ++k) sm[q][k / 4] |= (uint32_t)a.sm[e0 + t0 + k] << (8 * (k % 4));
     }
   }
-  uint32_t c[2][kGroup];
+  // codes of elements 4h..4h+3 of group q as the bytes of cb[q][h], and the escapes
+  // (code 0 of an element inside the block) as 0x80 bytes of esc[q][h]
+  uint32_t cb[2][2], esc[2][2];
   uint32_t packed = 0;
 #pragma unroll
   for (uint32_t q = 0; q < 2; ++q) {
     const uint32_t t0 = q * kHalf + kGroup * tid;
+    const uint32_t valid = nb > t0 ? min(nb - t0, kGroup) : 0u;  // elements of the group inside the block
+    uint32_t n = 0;
 #pragma unroll
-    for (uint32_t k = 0; k < kGroup; ++k) {
-      c[q][k] = ((pb[q][0] >> k) & 1u) | (((pb[q][1] >> k) & 1u) << 1) | (((pb[q][2] >> k) & 1u) << 2);
-      if (t0 + k < nb && c[q][k] == 0u) packed += 1u << (16 * q);
+    for (uint32_t h = 0; h < 2; ++h) {
+      cb[q][h] = spread4(pb[q][0] >> (4 * h)) | (spread4(pb[q][1] >> (4 * h)) << 1) |
+                 (spread4(pb[q][2] >> (4 * h)) << 2);
+      const uint32_t vh = valid > 4 * h ? min(valid - 4 * h, 4u) : 0u;  // valid elements of this word
+      const uint32_t in_block = vh >= 4 ? 0xFFFFFFFFu : ((1u << (8 * vh)) - 1u);
+      esc[q][h] = ~nonzero_bytes(cb[q][h]) & 0x80808080u & in_block;
+      n += __builtin_popcount(esc[q][h]);
     }
+    packed += n << (16 * q);
   }
   uint32_t total;
-  const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);  // also orders the tab writes
+  const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);
   const uint32_t excl_t = incl - packed;
   const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
   if (E1 < E0 || E1 - E0 != agg || E1 > a.esc_bytes) {
     if (tid == 0 && a.err) atomicOr(a.err, IBP_DEVERR_CORRUPT);
     return;  // block not decoded
   }
-  // this thread's escape exponents (consecutive in the escape array per group)
-  uint32_t ex[2][kGroup];
-#pragma unroll
-  for (uint32_t q = 0; q < 2; ++q) {
-    const uint32_t t0 = q * kHalf + kGroup * tid;
-    uint64_t r = E0 + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
-#pragma unroll
-    for (uint32_t k = 0; k < kGroup; ++k) {
-      ex[q][k] = 0;
-      if (t0 + k < nb && c[q][k] == 0u) ex[q][k] = a.esc[r++];
-    }
-  }
 #pragma unroll
   for (uint32_t q = 0; q < 2; ++q) {
     const uint32_t t0 = q * kHalf + kGroup * tid;
     if (t0 >= nb) continue;
-    uint32_t w[4] = {0u, 0u, 0u, 0u};
+    // exponents: table bytes by code, then this thread's escapes (consecutive in the
+    // escape array per group) in element order
+    uint32_t ex[2];
+    uint64_t r = E0 + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
 #pragma unroll
-    for (uint32_t k = 0; k < kGroup; ++k) {
-      const uint32_t s = (sm[q][k / 4] >> (8 * (k % 4))) & 0xFFu;
-      const uint32_t e = c[q][k] ? tab[c[q][k]] : ex[q][k];
-      const uint32_t v = ((s & 0x80u) << 8) | (e << 7) | (s & 0x7Fu);
-      w[k / 2] |= v << (16 * (k % 2));
+    for (uint32_t h = 0; h < 2; ++h) {
+      ex[h] = __builtin_amdgcn_perm(thi, tlo, cb[q][h]);
+      for (uint32_t m = esc[q][h]; m; m &= m - 1u) {
+        const uint32_t sh = (uint32_t)__builtin_ctz(m) - 7u;  // 8 * (byte index)
+        ex[h] |= (uint32_t)a.esc[r++] << sh;
+      }
     }
+    // pairs of elements: sign-mantissa and exponent bytes moved to the 16-bit halves
+    const uint32_t w0 = bf16_pair(__builtin_amdgcn_perm(0u, sm[q][0], 0x0C010C00u), __builtin_amdgcn_perm(0u, ex[0], 0x0C010C00u));
+    const uint32_t w1 = bf16_pair(__builtin_amdgcn_perm(0u, sm[q][0], 0x0C030C02u), __builtin_amdgcn_perm(0u, ex[0], 0x0C030C02u));
+    const uint32_t w2 = bf16_pair(__builtin_amdgcn_perm(0u, sm[q][1], 0x0C010C00u), __builtin_amdgcn_perm(0u, ex[1], 0x0C010C00u));
+    const uint32_t w3 = bf16_pair(__builtin_amdgcn_perm(0u, sm[q][1], 0x0C030C02u), __builtin_amdgcn_perm(0u, ex[1], 0x0C030C02u));
     uint16_t *o = a.out + e0 + t0;
     if (t0 + kGroup <= nb) {
-      *reinterpret_cast<uint4 *>(o) = make_uint4(w[0], w[1], w[2], w[3]);
+      *reinterpret_cast<uint4 *>(o) = make_uint4(w0, w1, w2, w3);
     } else {
+      const uint32_t w[4] = {w0, w1, w2, w3};
       for (uint32_t k = 0; t0 + k < nb; ++k) o[k] = (uint16_t)(w[k / 2] >> (16 * (k % 2)));
     }
   }
