@@ -9,12 +9,13 @@
 // order, in an escape array.  Per block of 4096 elements the codes are kept as
 // three bit planes of 4096 bits; eoff[j] counts the escapes before block j.
 //
-// Both kernels run one 256-thread workgroup per block; thread t handles the two
-// groups of 8 consecutive elements [q*2048 + 8t, +8), q = 0, 1, so sign-mantissa
-// bytes, plane bytes and BF16 words move as 8-, 1- and 16-byte accesses.  The
-// escapes of a thread are ranked by a block scan of two 16-bit counts packed in
-// one word (group 0 low, group 1 high), and the block's first escape by a
-// decoupled look-back over the blocks (compression) or by eoff (decompression).
+// A 256-thread workgroup decodes one block, and compresses kZipWG consecutive
+// blocks; in every block thread t handles the two groups of 8 consecutive
+// elements [q*2048 + 8t, +8), q = 0, 1, so sign-mantissa bytes, plane bytes and
+// BF16 words move as 8-, 1- and 16-byte accesses.  The escapes of a thread are
+// ranked by a block scan of two 16-bit counts packed in one word (group 0 low,
+// group 1 high), and the first escape of the compressor's workgroup by a
+// decoupled look-back over the workgroups (the decompressor reads eoff).
 #include "ibp_device.h"
 
 namespace ibp {
@@ -25,6 +26,7 @@ using namespace dev;
 constexpr uint32_t kGroup = 8;                          // consecutive elements per thread and group
 constexpr uint32_t kHalf = kZipBlock / 2;               // elements per group pass
 constexpr uint32_t kPlane = kZipBlock / 8;              // bytes per code plane
+constexpr uint32_t kZipWG = 4;                          // blocks per compressor workgroup
 
 // Inclusive scan of v over the workgroup (256 threads); *total gets the sum.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t lane, uint32_t wave, uint32_t *wsum,
@@ -44,81 +46,124 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t lane, uint32
 }
 
 __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
-  __shared__ uint8_t lut[256];  // exponent -> code
-  __shared__ uint32_t wsum[kWavesPerBlock];
+  // exponent -> code c as plane bits (c & 1, c >> 1 & 1, c >> 2 & 1 at bits 0, 8,
+  // 16), or bit 24 for an exponent outside the table (an escape): OR-ing
+  // lut[e_k] << k over the 8 elements of a group leaves the group's three plane
+  // bytes in bytes 0..2 and its escape mask in byte 3
+  __shared__ uint32_t lut[256];
+  __shared__ uint32_t wsum[kZipWG][kWavesPerBlock];
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_failed;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
-  lut[tid] = 0;
+  lut[tid] = 1u << 24;
   __syncthreads();
-  if (tid < 7) lut[a.table[tid]] = (uint8_t)(tid + 1);
+  if (tid < 7) {
+    const uint32_t c = tid + 1;
+    lut[a.table[tid]] = (c & 1u) | ((c >> 1) & 1u) << 8 | ((c >> 2) & 1u) << 16;
+  }
   __syncthreads();
-  const uint64_t j = blockIdx.x;  // grid == nblk; the look-back relies on workgroup order
-  const uint64_t e0 = j * kZipBlock;
-  const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
+  // workgroup g compresses blocks [j0, j0 + nbw); grid == workgroups, the
+  // look-back over workgroups relies on their order
+  const uint64_t g = blockIdx.x;
+  const uint64_t j0 = g * kZipWG;
+  const uint32_t nbw = (uint32_t)min((uint64_t)kZipWG, a.nblk - j0);
 
-  uint32_t ex[2][kGroup / 4];  // exponents, four per word
-  uint32_t smw[2][2];          // sign-mantissa bytes, four per word
-  uint32_t pbv[2][3];          // plane bytes
-  uint32_t escm = 0;           // bit q*8 + k: element k of group q is an escape
-  uint32_t packed = 0;         // escape counts: group 0 low 16 bits, group 1 high
+  // 1. every block's BF16 words first
+  uint32_t ws[kZipWG][2][4];
 #pragma unroll
-  for (uint32_t q = 0; q < 2; ++q) {
-    const uint32_t t0 = q * kHalf + kGroup * tid;
-    uint16_t u[kGroup];
-    if (t0 + kGroup <= nb) {
-      const uint4 w = *reinterpret_cast<const uint4 *>(a.in + e0 + t0);
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  for (uint32_t b = 0; b < kZipWG; ++b) {
+    const uint64_t e0 = (j0 + b) * kZipBlock;
+    const uint32_t nb = b < nbw ? (uint32_t)min((uint64_t)kZipBlock, a.n - e0) : 0u;
 #pragma unroll
-      for (uint32_t k = 0; k < kGroup; ++k) u[k] = (uint16_t)(ws[k / 2] >> (16 * (k % 2)));
-    } else {
+    for (uint32_t q = 0; q < 2; ++q) {
+      const uint32_t t0 = q * kHalf + kGroup * tid;
+      if (t0 + kGroup <= nb) {
+        const uint4 w = *reinterpret_cast<const uint4 *>(a.in + e0 + t0);
+        ws[b][q][0] = w.x;
+        ws[b][q][1] = w.y;
+        ws[b][q][2] = w.z;
+        ws[b][q][3] = w.w;
+      } else {
 #pragma unroll
-      for (uint32_t k = 0; k < kGroup; ++k) u[k] = t0 + k < nb ? a.in[e0 + t0 + k] : (uint16_t)0;
-    }
-    smw[q][0] = smw[q][1] = 0;
-    pbv[q][0] = pbv[q][1] = pbv[q][2] = 0;
-    ex[q][0] = ex[q][1] = 0;
-#pragma unroll
-    for (uint32_t k = 0; k < kGroup; ++k) {
-      const uint32_t v = u[k], e = (v >> 7) & 0xFFu;
-      const uint32_t sbyte = ((v >> 8) & 0x80u) | (v & 0x7Fu);
-      const bool valid = t0 + k < nb;
-      const uint32_t c = valid ? lut[e] : 0u;
-      smw[q][k / 4] |= sbyte << (8 * (k % 4));
-      ex[q][k / 4] |= e << (8 * (k % 4));
-      pbv[q][0] |= (c & 1u) << k;
-      pbv[q][1] |= ((c >> 1) & 1u) << k;
-      pbv[q][2] |= ((c >> 2) & 1u) << k;
-      if (valid && c == 0u) {
-        escm |= 1u << (q * kGroup + k);
-        packed += 1u << (16 * q);
+        for (uint32_t k = 0; k < kGroup / 2; ++k) {
+          const uint32_t lo = t0 + 2 * k < nb ? a.in[e0 + t0 + 2 * k] : 0u;
+          const uint32_t hi = t0 + 2 * k + 1 < nb ? a.in[e0 + t0 + 2 * k + 1] : 0u;
+          ws[b][q][k] = lo | (hi << 16);
+        }
       }
     }
   }
-  // the block's escape count first, published at once for the successors' look-back
-  uint32_t total;
-  const uint32_t incl = block_scan(packed, lane, wave, wsum, &total);
-  const uint32_t excl_t = incl - packed;
-  const uint32_t tot0 = total & 0xFFFFu, agg = tot0 + (total >> 16);
-  if (tid == 0) lookback_publish(a.status, j, agg);
-  // then the sign-mantissa bytes and code planes, which need no offset
+  // 2. per block: sign-mantissa and exponent bytes, codes, escape ranks (a block
+  //    scan of the two groups' counts packed in one word, group 0 low)
+  uint32_t smw[kZipWG][2][2], ex[kZipWG][2][2], acc[kZipWG][2];
+  uint32_t escm[kZipWG];       // bit q*8 + k: element k of group q is an escape
+  uint32_t rank[kZipWG][2];    // escapes of the workgroup before this thread's group q
+  uint32_t btot[kZipWG];       // escapes per block
+  uint32_t wtot = 0;           // escapes of the workgroup
 #pragma unroll
-  for (uint32_t q = 0; q < 2; ++q) {
-    const uint32_t t0 = q * kHalf + kGroup * tid;
-    uint8_t *smo = a.sm + e0 + t0;
-    if (t0 + kGroup <= nb) {
-      *reinterpret_cast<uint2 *>(smo) = make_uint2(smw[q][0], smw[q][1]);
-    } else {
-      for (uint32_t k = 0; t0 + k < nb; ++k) smo[k] = (uint8_t)(smw[q][k / 4] >> (8 * (k % 4)));
+  for (uint32_t b = 0; b < kZipWG; ++b) {
+    const uint32_t nb = b < nbw ? (uint32_t)min((uint64_t)kZipBlock, a.n - (j0 + b) * kZipBlock) : 0u;
+    uint32_t packed = 0;
+    escm[b] = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+      const uint32_t t0 = q * kHalf + kGroup * tid;
+      // two elements per word: sign-mantissa byte (sign at bit 7) and exponent in
+      // the low byte of each 16-bit half, then four of them gathered into one word
+      uint32_t sp[4], ep[4];
+#pragma unroll
+      for (uint32_t k = 0; k < 4; ++k) {
+        sp[k] = (ws[b][q][k] & 0x007F007Fu) | ((ws[b][q][k] >> 8) & 0x00800080u);
+        ep[k] = (ws[b][q][k] >> 7) & 0x00FF00FFu;
+      }
+      smw[b][q][0] = __builtin_amdgcn_perm(sp[1], sp[0], 0x06040200u);
+      smw[b][q][1] = __builtin_amdgcn_perm(sp[3], sp[2], 0x06040200u);
+      ex[b][q][0] = __builtin_amdgcn_perm(ep[1], ep[0], 0x06040200u);
+      ex[b][q][1] = __builtin_amdgcn_perm(ep[3], ep[2], 0x06040200u);
+      uint32_t c = 0;
+#pragma unroll
+      for (uint32_t k = 0; k < kGroup; ++k) c |= lut[(ex[b][q][k / 4] >> (8 * (k % 4))) & 0xFFu] << k;
+      const uint32_t valid = nb > t0 ? min(nb - t0, kGroup) : 0u;  // elements of the group inside the block
+      const uint32_t em = (c >> 24) & ((1u << valid) - 1u);
+      acc[b][q] = c & (((1u << valid) - 1u) * 0x010101u);  // elements past nb have code 0
+      escm[b] |= em << (q * kGroup);
+      packed += (uint32_t)__builtin_popcount(em) << (16 * q);
     }
-    uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
-    cp[0] = (uint8_t)pbv[q][0];
-    cp[kPlane] = (uint8_t)pbv[q][1];
-    cp[2 * kPlane] = (uint8_t)pbv[q][2];
+    uint32_t total = 0;
+    const uint32_t incl = block_scan(packed, lane, wave, wsum[b], &total);
+    const uint32_t excl_t = incl - packed;
+    const uint32_t tot0 = total & 0xFFFFu;
+    rank[b][0] = wtot + (excl_t & 0xFFFFu);
+    rank[b][1] = wtot + tot0 + (excl_t >> 16);
+    btot[b] = tot0 + (total >> 16);
+    wtot += btot[b];
+  }
+  // the workgroup's escape count first, published at once for the successors'
+  // look-back; then the sign-mantissa bytes and code planes, which need no offset
+  if (tid == 0) lookback_publish(a.status, g, wtot);
+#pragma unroll
+  for (uint32_t b = 0; b < kZipWG; ++b) {
+    if (b >= nbw) continue;
+    const uint64_t j = j0 + b, e0 = j * kZipBlock;
+    const uint32_t nb = (uint32_t)min((uint64_t)kZipBlock, a.n - e0);
+#pragma unroll
+    for (uint32_t q = 0; q < 2; ++q) {
+      const uint32_t t0 = q * kHalf + kGroup * tid;
+      uint8_t *smo = a.sm + e0 + t0;
+      if (t0 + kGroup <= nb) {
+        *reinterpret_cast<uint2 *>(smo) = make_uint2(smw[b][q][0], smw[b][q][1]);
+      } else {
+        for (uint32_t k = 0; t0 + k < nb; ++k) smo[k] = (uint8_t)(smw[b][q][k / 4] >> (8 * (k % 4)));
+      }
+      uint8_t *cp = a.codes + j * (3 * kPlane) + q * (kHalf / 8) + tid;
+      cp[0] = (uint8_t)acc[b][q];
+      cp[kPlane] = (uint8_t)(acc[b][q] >> 8);
+      cp[2 * kPlane] = (uint8_t)(acc[b][q] >> 16);
+    }
   }
   if (wave == 0) {
     bool timed_out = false;
-    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, j, agg, lane, timed_out);
+    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, g, wtot, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
       s_failed = timed_out ? 1u : 0u;
@@ -128,15 +173,23 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   if (s_failed != 0u) return;  // no valid escape offset: nothing more is stored
   const uint64_t base = s_excl;
   if (tid == 0) {
-    a.eoff[j] = base;
-    if (j == a.nblk - 1) a.eoff[a.nblk] = base + agg;
+    uint64_t o = base;
+    for (uint32_t b = 0; b < nbw; ++b) {
+      a.eoff[j0 + b] = o;
+      o += btot[b];
+    }
+    if (j0 + nbw == a.nblk) a.eoff[a.nblk] = o;
   }
 #pragma unroll
-  for (uint32_t q = 0; q < 2; ++q) {
-    uint64_t r = base + (q == 0 ? (excl_t & 0xFFFFu) : tot0 + (excl_t >> 16));
+  for (uint32_t b = 0; b < kZipWG; ++b) {
 #pragma unroll
-    for (uint32_t k = 0; k < kGroup; ++k)
-      if ((escm >> (q * kGroup + k)) & 1u) a.esc[r++] = (uint8_t)(ex[q][k / 4] >> (8 * (k % 4)));
+    for (uint32_t q = 0; q < 2; ++q) {
+      uint64_t r = base + rank[b][q];
+      for (uint32_t m = (escm[b] >> (q * kGroup)) & 0xFFu; m; m &= m - 1u) {
+        const uint32_t k = (uint32_t)__builtin_ctz(m);
+        a.esc[r++] = (uint8_t)(ex[b][q][k / 4] >> (8 * (k % 4)));
+      }
+    }
   }
 }
 
@@ -250,7 +303,7 @@ hipError_t launch_zip_encode(const ZipArgs &a, hipStream_t s) {
   // clear the control words and status words (a kernel, not a memset node)
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), a.nblk + 1, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(zip_encode_kernel, dim3((uint32_t)a.nblk), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(zip_encode_kernel, dim3((uint32_t)((a.nblk + kZipWG - 1) / kZipWG)), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

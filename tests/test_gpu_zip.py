@@ -53,7 +53,7 @@ def test_zip_parity(ibp, sigma):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(int(sigma * 1e5))
     table = oracle.zip_table(sigma)
-    for n in (1, 7, 8, 9, 4095, 4096, 4097, 2048 * 3 + 5, 100_003, (1 << 20) + 13):
+    for n in (1, 7, 8, 9, 4095, 4096, 4097, 2048 * 3 + 5, 3 * 4096 - 5, 4 * 4096, 4 * 4096 + 100, 100_003, (1 << 20) + 13):
         say(f"zip sigma={sigma} n={n}")
         _check(ibp, dev, _bf16(rng, n, sigma), table, f"n={n}")
 
