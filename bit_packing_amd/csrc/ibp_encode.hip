@@ -23,7 +23,7 @@ enum : uint32_t {
   kModeLargeS = 2,   // S % 64 == 0: each 64-chunk block lies inside one segment
 };
 
-// One workgroup per tile of G consecutive segments (about kEncTileChunks chunks).
+// One workgroup per tile of G consecutive segments (about 16 chunks per thread).
 //  1. tile t = workgroup index (see lookback_exclusive for why the order holds);
 //  2. load the chunks (16 per thread, 64 consecutive per wavefront per pass),
 //     test the invariant bits and ballot the participation bits; clear the LDS
@@ -49,11 +49,15 @@ enum : uint32_t {
 // scan per 64-chunk block plus a scan over the blocks), and the extraction walks
 // the runs of each lane's own free positions.
 template <typename T, uint32_t kMode, uint32_t NR, bool kPos>
-__global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecParams p) {
+__global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock) encode_kernel(EncodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
-  constexpr uint32_t kQ = kEncTileChunks / kEncBlock;  // passes of kEncBlock chunks
-  constexpr uint32_t kBal = kEncTileChunks / kWave;    // 64-chunk blocks per tile
-  static_assert(kBal <= kWave, "one ballot word per lane of the prefix scan");
+  constexpr uint32_t kThreads = kPos ? kEncBlockPos : kEncBlock;
+  constexpr uint32_t kWaves = kThreads / kWave;
+  constexpr uint32_t kTile = enc_tile_chunks(kPos);
+  constexpr uint32_t kQ = kTile / kThreads;  // passes of kThreads chunks
+  constexpr uint32_t kBal = kTile / kWave;   // 64-chunk blocks per tile
+  constexpr uint32_t kPer = (kBal + kWave - 1) / kWave;  // 64-chunk blocks per lane of the prefix scan
+  static_assert(kBal <= kWave || kBal == kPer * kWave, "whole blocks per lane of the prefix scan");
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   uint32_t *obuf = smem;
   uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // kBal words
@@ -79,28 +83,28 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
 
   // 2. chunks, participation bits; clear the image meanwhile
   T v[kQ];
-  if (nch == kEncTileChunks) {  // every tile but possibly the last: no bounds tests
+  if (nch == kTile) {  // every tile but possibly the last: no bounds tests
 #pragma unroll
-    for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kEncBlock + tid];
+    for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kThreads + tid];
   } else {
 #pragma unroll
     for (uint32_t q = 0; q < kQ; ++q) {
-      const uint32_t cl = q * kEncBlock + tid;
+      const uint32_t cl = q * kThreads + tid;
       v[q] = cl < nch ? in[cl] : (T)0;
     }
   }
-  for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kEncBlock)
+  for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kThreads)
     *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
-  uint32_t ip[kQ];   // kPos: position of chunk q * kEncBlock + tid in its segment (tiles start on a segment)
+  uint32_t ip[kQ];   // kPos: position of chunk q * kThreads + tid in its segment (tiles start on a segment)
   uint32_t svx[kQ];  // kPos: saved bits of the earlier chunks of its 64-chunk block
   if constexpr (kPos) {
     const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
-    for (uint32_t i = tid; i < a.S; i += kEncBlock) {
+    for (uint32_t i = tid; i < a.S; i += kThreads) {
       const uint64_t m = a.pmask[i] & full;
       mtab[i] = m;
       btab[i] = a.pbitval[i] & m;
     }
-    const uint32_t step = kEncBlock % a.S;
+    const uint32_t step = kThreads % a.S;
     uint32_t i0 = tid % a.S;
 #pragma unroll
     for (uint32_t q = 0; q < kQ; ++q) {
@@ -113,7 +117,7 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
   uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
-    const uint32_t cl = q * kEncBlock + tid;
+    const uint32_t cl = q * kThreads + tid;
     if constexpr (kPos) {
       const uint64_t m = mtab[ip[q]];
       const bool h = cl < nch && ((v[q] ^ (T)btab[ip[q]]) & (T)m) == 0;
@@ -123,18 +127,30 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
       const uint32_t x = wave_incl_scan(sv);
       svx[q] = x - sv;
       wpre[cl] = (uint16_t)x;
-      if (lane == kWave - 1) bal[q * kEncWaves + wave] = x;  // the block's saved bits
+      if (lane == kWave - 1) bal[q * kWaves + wave] = x;  // the block's saved bits
     } else {
       B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
-      if (lane == 0) bal[q * kEncWaves + wave] = B[q];
+      if (lane == 0) bal[q * kWaves + wave] = B[q];
     }
   }
   __syncthreads();
   // 3. compressed chunks before each 64-chunk block
   if (wave == 0) {
-    const uint32_t c = lane < kBal ? (kPos ? (uint32_t)bal[lane] : popc(bal[lane])) : 0u;
-    const uint32_t x = wave_incl_scan(c);
-    if (lane < kBal) pref[lane] = x - c;
+    // lane l sums blocks [kPer l, kPer l + kPer)
+    uint32_t cs[kPer], c = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+      const uint32_t b = kPer * lane + k;
+      cs[k] = b < kBal ? (kPos ? (uint32_t)bal[b] : popc(bal[b])) : 0u;
+      c += cs[k];
+    }
+    uint32_t x = wave_incl_scan(c) - c;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k) {
+      const uint32_t b = kPer * lane + k;
+      if (b < kBal) pref[b] = x;
+      x += cs[k];
+    }
     if (lane == kWave - 1) pref[kBal] = x;
   }
   __syncthreads();
@@ -164,9 +180,16 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
   //    follow the m header bits, so chunk cl's payload starts at
   //    s0 + m + cl W - (bits saved by the tile chunks before cl).
   const uint32_t lane_bits = lane * W;
-  const uint32_t my_pref = lane <= kBal ? pref[lane] : 0u;  // lane b: the value for 64-chunk block b
+  // lane l holds the values of 64-chunk blocks l, 64 + l, ...
+  uint32_t my_pref[kPer];
+#pragma unroll
+  for (uint32_t k = 0; k < kPer; ++k) my_pref[k] = kWave * k + lane <= kBal ? pref[kWave * k + lane] : 0u;
   auto pref_at = [&](uint32_t b) -> uint32_t {  // b wave-uniform
-    return (uint32_t)__builtin_amdgcn_readlane((int)my_pref, (int)b);
+    uint32_t v = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kPer; ++k)
+      if ((b >> 6) == k) v = (uint32_t)__builtin_amdgcn_readlane((int)my_pref[k], (int)(b & 63u));
+    return v;
   };
   auto seg_start = [&](uint32_t c) -> uint32_t {  // first chunk of the segment holding tile chunk c
     return a.s_log2 != kNotPow2 ? (c >> a.s_log2) << a.s_log2 : (c / a.S) * a.S;
@@ -175,7 +198,7 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
 #pragma unroll
   for (uint32_t q = 0; q < kQ; ++q) {
-    const uint32_t blk = q * kEncWaves + wave;  // this wavefront's 64-chunk block
+    const uint32_t blk = q * kWaves + wave;  // this wavefront's 64-chunk block
     const uint32_t cb = blk * kWave;                 // its first tile chunk
     if (cb >= nch) continue;                         // uniform
     const uint32_t cl = cb + lane;
@@ -236,9 +259,9 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
     }
   }
   if constexpr (kMode == kModeLargeS && !kPos) {
-    // the headers: lane q of each wavefront ORs in block q * kEncWaves + wave's
+    // the headers: lane q of each wavefront ORs in block q * kWaves + wave's
     // 64 participation bits
-    const uint32_t blk = lane * kEncWaves + wave, cb = blk * kWave;
+    const uint32_t blk = lane * kWaves + wave, cb = blk * kWave;
     if (lane < kQ && cb < nch) {
       const uint32_t s0 = seg_start(cb);
       lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6], bal[blk]);
@@ -265,7 +288,7 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
   }
 
   // 6. segment offsets
-  for (uint32_t r = tid; r < nsegt; r += kEncBlock)
+  for (uint32_t r = tid; r < nsegt; r += kThreads)
     a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)cost(r * a.S);
   if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
 
@@ -288,13 +311,13 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
   const uint32_t hi = last_d + 1u - ((has_tail && !last) ? 1u : 0u);  // [lo, hi) stored directly
   uint32_t *gdst = a.stream + ((excl >> 7) << 2);
   const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
-  for (uint32_t d = lo + tid; d < a4; d += kEncBlock) gdst[d] = out_dw(d);
+  for (uint32_t d = lo + tid; d < a4; d += kThreads) gdst[d] = out_dw(d);
   // interior: output dwords [d, d + 4) are image bits from 32 d - sh0 on, i.e. from
   // bit t = 128 - sh0 of the eight image dwords [d - 4, d + 4) (two aligned 16-byte
   // LDS reads; the image is zero past its last bit and a4 >= 4 unless sh0 == 0)
   const uint32_t t_sh = 128u - sh0, jt = t_sh >> 5, st = t_sh & 31u;
   auto al = [&](uint32_t hi, uint32_t lo) -> uint32_t { return __builtin_amdgcn_alignbit(hi, lo, st); };
-  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kEncBlock) {
+  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kThreads) {
     const uint4 A = *reinterpret_cast<const uint4 *>(obuf + ((max(d, 4u) - 4u) & ~3u));
     const uint4 C = *reinterpret_cast<const uint4 *>(obuf + d);
     uint4 o;
@@ -307,7 +330,7 @@ __global__ void __launch_bounds__(kEncBlock) encode_kernel(EncodeArgs a, CodecPa
     }
     *reinterpret_cast<uint4 *>(gdst + d) = o;
   }
-  for (uint32_t d = e4 + tid; d < hi; d += kEncBlock) gdst[d] = out_dw(d);
+  for (uint32_t d = e4 + tid; d < hi; d += kThreads) gdst[d] = out_dw(d);
   if (tid == 0) {
     if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | out_dw(last_d));
     if (has_head) {
@@ -340,7 +363,8 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos>), dim3((uint32_t)a.ntiles), dim3(kEncBlock), shmem, s, a, p);
+  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos>), dim3((uint32_t)a.ntiles), dim3(kPos ? kEncBlockPos : kEncBlock),
+                     shmem, s, a, p);
   return hipGetLastError();
 }
 
@@ -388,11 +412,12 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
   // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
-  size_t shmem = (size_t)a.obuf_dw * 4 + (kEncTileChunks / kWave) * 8 + ((kEncTileChunks / kWave) + 2) * 4;
+  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr);
+  size_t shmem = (size_t)a.obuf_dw * 4 + (tile / kWave) * 8 + ((tile / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   if (a.pmask) {
     // position tables and per-chunk saved-bit prefixes
-    shmem += (size_t)a.S * 16 + (size_t)kEncTileChunks * 2;
+    shmem += (size_t)a.S * 16 + (size_t)tile * 2;
     if (p.W == 16) return launch_encode_pos_w<uint16_t>(a, p, shmem, s);
     return p.W == 32 ? launch_encode_pos_w<uint32_t>(a, p, shmem, s) : launch_encode_pos_w<uint64_t>(a, p, shmem, s);
   }

@@ -13,12 +13,15 @@ constexpr uint32_t kWavesPerBlock = kBlock / kWave;
 constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-bit chunk
 
 // Compression: a workgroup of kEncBlock threads sizes, offsets and packs a tile
-// of about kEncTileChunks chunks (16 per thread).  Measured on the five
-// workloads: 128- and 64-thread workgroups (2048- and 1024-chunk tiles) were
-// 10-50% slower, their per-tile costs spread over fewer chunks.
-constexpr uint32_t kEncBlock = 256;
-constexpr uint32_t kEncWaves = kEncBlock / kWave;
-constexpr uint32_t kEncTileChunks = kEncBlock * 16;
+// of 16 chunks per thread; with position-dependent metadata, whose tables and
+// per-chunk prefixes also live in LDS, kEncBlockPos threads.  Measured on the
+// workloads: 512 threads beat 256 by 3-10% with one Mask (1024 did not), while
+// position metadata is fastest at 256 (its LDS per workgroup doubles with the
+// tile); 128 and 64 threads were 10-50% slower, their per-tile costs spread over
+// fewer chunks.
+constexpr uint32_t kEncBlock = 512;
+constexpr uint32_t kEncBlockPos = 256;
+constexpr uint32_t enc_tile_chunks(bool pos) { return 16u * (pos ? kEncBlockPos : kEncBlock); }
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;

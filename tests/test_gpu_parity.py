@@ -2,7 +2,8 @@
 
 Tolerance is 0 everywhere: the codec is lossless, so counts, Mask, Bitval, the
 offset table, every stream byte below ceil(total/8) and the round trip must
-agree exactly.  Sizes span several compression tiles (4096 chunks) and
+agree exactly.  Sizes span several compression tiles (8192 chunks, 4096 with
+position metadata) and
 decompression tiles (512 chunks per wavefront) plus ragged tails.
 """
 import numpy as np
