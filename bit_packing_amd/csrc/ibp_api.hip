@@ -345,11 +345,20 @@ static int decode_common(const CodecParams &p, const uint64_t *pmask, const uint
   // more host reads in flight.  From HBM a wavefront takes about 512 chunks of a
   // contiguous stream, and about 1024 chunks, at most kGatherMaxRows rows, of a
   // gather (its dependent id -> offset -> row reads favour one wave generation).
-  if (gather)
+  // A contiguous stream with one Mask takes 512 chunks per wavefront; from 2^24
+  // chunks on, 512 * 64 / W (the same ~4 KB of staging at every W), which spreads
+  // the per-tile setup over more chunks (sparse W = 32 data: 197 -> 159 us per
+  // 128M chunks; W = 16: 969 -> 865 us per 1G chunks), while smaller inputs keep
+  // more wavefronts.
+  if (gather) {
     a.G = host_stream ? 1u : (S >= 2 * kDecTileChunks / kGatherMaxRows ? (S >= 2 * kDecTileChunks ? 1u : 2 * kDecTileChunks / S)
                                                                        : kGatherMaxRows);
-  else
+  } else if (pmask) {
     a.G = dec_units_per_tile(S);
+  } else {
+    const uint32_t tile = n_chunks >= (1ull << 24) ? kDecTileChunks * (64u / p.W) : kDecTileChunks;
+    a.G = S >= tile ? 1u : (tile / S > kDecMaxUnits ? kDecMaxUnits : tile / S);
+  }
   const uint32_t tile_chunks = a.G * S;
   if (gather) {
     a.slot_dw = ((S * (p.W + 1) + 127) / 128 + 1) * 4;
