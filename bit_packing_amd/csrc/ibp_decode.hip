@@ -172,7 +172,8 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
             put(r, t);
             wave_lds_sync();
             if (r < nu)
-              err |= decode_row<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S, lane);
+              err |= decode_segment<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S,
+                                           lane);
           };
           row(0, t0);
           row(1, t1);

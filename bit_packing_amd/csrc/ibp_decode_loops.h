@@ -10,6 +10,8 @@
 // (a ballot plus a per-unit carry kept in gseg).
 #pragma once
 
+#include <type_traits>
+
 #include "ibp_device.h"
 
 namespace ibp {
@@ -82,6 +84,52 @@ __device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S,
   return base != le ? IBP_DEVERR_CORRUPT : 0u;
 }
 
+// The same for W <= 32 and S a multiple of 128, two chunks per lane: lane l takes
+// chunks 2l and 2l + 1 of each 128-chunk pass and reads their two participation
+// bits itself; the compressed chunks before chunk 2l are those below lane l in
+// the ballot of the even chunks plus those in the ballot of the odd ones, and
+// the two ballots' popcounts give the pass's total.  The pair is stored as one
+// 2W-bit word, so o must be 2W/8-byte aligned.
+template <typename T, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
+                                                uint32_t le, T *o, uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  static_assert(W <= 32, "two chunks per lane up to W = 32");
+  using P = typename std::conditional<(W == 32), uint64_t, uint32_t>::type;  // a pair of chunks
+  if (lb == kBad) return 0u;
+  const uint32_t pc = p.pc;
+  const T bitval = (T)p.bitval;
+  const uint32_t lane_bits = lane * 2u * W;
+  P *op = reinterpret_cast<P *>(o) + lane;
+  uint32_t hp = lb + 2u * lane, base = lb + S;  // hp: this lane's first participation bit
+  for (uint32_t q = 0; q < S; q += 2 * kWave) {
+    const uint32_t b2 = lds_field<uint32_t>(stg, hp) & 3u;
+    const bool h0 = (b2 & 1u) != 0u, h1 = b2 > 1u;
+    const uint64_t E = ballot(h0), O = ballot(h1);
+    const uint32_t pos0 = base + lane_bits - __umul24(pc, count_below(E) + count_below(O));
+    const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
+    const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
+    const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | bitval) : x0;
+    const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | bitval) : x1;
+    op[q / 2] = (P)v0 | ((P)v1 << W);
+    base += 2u * kWave * W - pc * (popc(E) + popc(O));
+    hp += 2u * kWave;
+  }
+  return base != le ? IBP_DEVERR_CORRUPT : 0u;
+}
+
+// One whole segment: two chunks per lane where that applies (W <= 32, S a multiple
+// of 128, o aligned for the pair stores), else one.
+template <typename T, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_segment(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
+                                                   uint32_t le, T *o, uint32_t lane) {
+  if constexpr (sizeof(T) <= 4) {
+    if (S % (2u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & (2u * sizeof(T) - 1u)) == 0u)
+      return decode_row2<T, NR>(p, S, stg, lb, le, o, lane);
+  }
+  return decode_row<T, NR>(p, S, stg, lb, le, o, lane);
+}
+
 // Units that are all whole segments of S chunks, S a multiple of 64.
 template <typename T, uint32_t NR>
 __device__ __forceinline__ uint32_t decode_rows(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
@@ -89,7 +137,7 @@ __device__ __forceinline__ uint32_t decode_rows(const DecodeArgs &a, const Codec
                                                 uint32_t lane) {
   uint32_t err = 0;
   for (uint32_t r = 0; r < nu; ++r)
-    err |= decode_row<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S, lane);
+    err |= decode_segment<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S, lane);
   return err;
 }
 
