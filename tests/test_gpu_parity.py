@@ -98,6 +98,38 @@ def test_compress_decompress_parity(ibp, W, S):
             _run_case(ibp, dev, _data(rng, n, W, mask, bitval, p), W, S, mask, bitval, f"{name}-{n}")
 
 
+@pytest.mark.parametrize("W", [16, 32])
+@pytest.mark.parametrize("S", [128, 256])
+def test_decode_into_unaligned_output(ibp, W, S):
+    """Outputs that start one chunk past an aligned address: the decoders store a
+    pair of W <= 32 chunks as one word only when the output allows it, else one
+    chunk per lane; both the contiguous decode and the HBM gather are checked."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(W * 31 + S)
+    cb = W // 8
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for name, mask, bitval in _masks(rng, W):
+        for n in (20 * S, 20 * S + 5):
+            say(f"unaligned output {name} W={W} S={S} n={n}")
+            v = _data(rng, n, W, mask, bitval, 0.9)
+            meta = ibp.make_meta(W, mask, bitval)
+            x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+            comp = ibp.ibp_compress(meta, x, S, err=err)
+            big = torch.zeros(n * cb + 16, dtype=torch.uint8, device=dev)
+            out = big[cb: cb + n * cb]
+            ibp.ibp_decompress(meta, comp.stream, comp.offsets, n, S, out=out, err=err)
+            assert torch.equal(out, x), f"{name} n={n}: contiguous decode into an unaligned output"
+            ids_np = rng.integers(0, n // S, 300).astype(np.int64)
+            big2 = torch.zeros(ids_np.size * S * cb + 16, dtype=torch.uint8, device=dev)
+            out2 = big2[cb: cb + ids_np.size * S * cb]
+            ibp.ibp_decompress_gather(meta, comp.stream, comp.offsets, S, torch.from_numpy(ids_np).to(dev),
+                                      out=out2, err=err, n_segments=n // S)
+            want = v[: (n // S) * S].reshape(-1, S)[ids_np].reshape(-1)
+            assert np.array_equal(out2.cpu().numpy().view(v.dtype), want), f"{name} n={n}: gather into an unaligned output"
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+
+
 @pytest.mark.parametrize("W", [16, 32, 64])
 def test_all_invariant_and_raw_streams(ibp, W):
     """Minimum size (all chunks equal Bitval on a full Mask) and +1 bit per chunk (Mask = 0)."""
