@@ -8,9 +8,10 @@
 // rows for the gather):
 //  a. read the units' bit ranges from the offset table and check them, so that
 //     no read leaves the stream and no LDS write leaves the tile's staging area;
-//  b. stage the compressed bits in LDS with 16-byte loads, all issued before any
-//     LDS write (the contiguous tile is one range; a gather stages each row in
-//     its own slot);
+//  b. stage the compressed bits in LDS with 16-byte loads: the contiguous tile is
+//     one range, all its loads issued before any LDS write; a gather stages each
+//     row in its own slot, and when a row's blocks fit one load per lane each row
+//     is staged and decoded as soon as its own load lands;
 //  c. per pass of 64 chunks, find each lane's payload offset from the
 //     participation bits: every chunk before it in its segment costs W bits,
 //     minus popcount(Mask) for each compressed one, so the offset is a prefix
@@ -19,7 +20,10 @@
 //     take it raw; store 64 consecutive chunks.
 // The prefix count has three forms, chosen by the host from S:
 //  - S a multiple of 64: a pass lies inside one segment, whose 64 participation
-//    bits are one broadcast 64-bit LDS read;
+//    bits are one broadcast 64-bit LDS read; for W <= 32 and S a multiple of 128
+//    a lane takes two chunks of a 128-chunk pass instead (its own two
+//    participation bits, the ballots of the even and the odd chunks) and stores
+//    them as one word;
 //  - S dividing 64: a pass holds 64/S whole segments; a ballot of the
 //    participation bits, masked to the lane's segment;
 //  - any other S: a ballot plus a per-segment carry kept in LDS.

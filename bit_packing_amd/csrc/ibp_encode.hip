@@ -30,15 +30,18 @@ enum : uint32_t {
 //     image while the loads are in flight;
 //  3. a wave-wide scan of the ballot popcounts gives the number of compressed
 //     chunks before every 64-chunk block, hence every segment's size and the
-//     tile's; publish it, then wavefront 0 walks back over the predecessors'
-//     status words 64 at a time (decoupled look-back) to get the tile's first bit;
-//  4. write the segment offsets; assemble the tile's bits in LDS with atomic ORs
-//     (headers as whole ballot fields, payloads = parallel bit extract or the raw
-//     chunk); bit 0 of the image is the first bit of the 16-byte block holding the
-//     tile's first bit, so interior stores are 16-byte aligned;
-//  5. store the whole dwords; the dword shared with the previous tile is written
-//     by this tile after OR-ing in the bits the previous tile handed over, and the
-//     dword shared with the next tile is handed over instead of written.
+//     tile's, which is published at once for the successors' look-back;
+//  4. assemble the tile's bits with atomic ORs in an LDS image that starts at the
+//     tile's own first bit (payloads = parallel bit extract or the raw chunk;
+//     the headers of S >= 64 segments as whole 64-bit ballots, once per tile);
+//  5. wavefront 0 walks back over the predecessors' status words 64 at a time
+//     (decoupled look-back) to get the tile's first bit;
+//  6. write the segment offsets;
+//  7. store the image shifted to the first bit's place in its 16-byte block
+//     (interior 16-byte stores from two aligned LDS reads); the dword shared with
+//     the previous tile is written by this tile after OR-ing in the bits the
+//     previous tile handed over, and the dword shared with the next tile is
+//     handed over instead of written.
 // The per-chunk prefix count has the decoder's three forms (S a multiple of 64,
 // S dividing 64, any S).
 //
