@@ -39,10 +39,15 @@ KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: // comments, trailing blanks and empty lines
+    do not count, so a comment edit leaves committed counter summaries valid."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
