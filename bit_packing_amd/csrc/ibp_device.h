@@ -95,23 +95,8 @@ template <typename T, uint32_t NR> __device__ __forceinline__ T deposit_free(T x
   return out;
 }
 
-// Bit extract / deposit for a per-lane free-position mask F: one step per run of
+// Bit deposit for a per-lane free-position mask F: one step per run of
 // consecutive free positions (runs differ between lanes, so the loop is per lane).
-template <typename T> __device__ __forceinline__ T extract_var(T v, uint64_t F) {
-  uint64_t out = 0;
-  uint32_t k = 0;
-  while (F) {
-    const uint32_t lo = (uint32_t)__builtin_ctzll(F);
-    const uint64_t rest = ~(F >> lo);
-    const uint32_t len = rest ? (uint32_t)__builtin_ctzll(rest) : 64u - lo;
-    const uint64_t run = low_lanes(len);
-    out |= (((uint64_t)v >> lo) & run) << k;
-    k += len;
-    F &= ~(run << lo);
-  }
-  return (T)out;
-}
-
 template <typename T> __device__ __forceinline__ T deposit_var(T x, uint64_t F) {
   uint64_t out = 0;
   uint32_t k = 0;
