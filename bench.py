@@ -35,7 +35,7 @@ HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD published
 PCIE_PEAK_GBPS = 64.0      # PCIe 5.0 x16, one direction, published link rate
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in
                   ("ibp_device.h", "ibp_decode_loops.h", "ibp_internal.h", "ibp_meta.hip", "ibp_encode.hip",
-                   "ibp_decode.hip", "ibp_slots.hip", "ibp_zip.hip")]
+                   "ibp_decode.hip", "ibp_decode_pos.hip", "ibp_slots.hip", "ibp_zip.hip")]
 
 
 def kernel_source_hash() -> str:

@@ -9,7 +9,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("ibp_meta.hip", "ibp_encode.hip", "ibp_decode.hip", "ibp_slots.hip", "ibp_zip.hip", "ibp_api.hip")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("ibp_meta.hip", "ibp_encode.hip", "ibp_decode.hip", "ibp_decode_pos.hip", "ibp_slots.hip", "ibp_zip.hip", "ibp_api.hip")]
 LIB = os.path.join(HERE, "libibp.so")
 
 HIPCC_FLAGS = [

@@ -36,57 +36,6 @@ namespace {
 
 using namespace dev;
 
-// Stage the 16-byte blocks [blk0, blk0 + nb) of src into LDS at dst.  Whole
-// blocks are loaded four per lane before any is written (up to 256 loads in
-// flight per wavefront); the block holding the end of a source whose length is
-// not a multiple of 16 is read byte by byte afterwards.
-__device__ __forceinline__ void stage_range(const uint8_t *src, uint64_t nbytes, uint64_t blk0, uint32_t nb,
-                                            uint32_t *dst, uint32_t lane) {
-  const uint64_t whole = nbytes >> 4;
-  const uint32_t nf = blk0 >= whole ? 0u : (uint32_t)min((uint64_t)nb, whole - blk0);
-  for (uint32_t j0 = 0; j0 < nf; j0 += 4 * kWave) {
-    uint4 t[4];
-#pragma unroll
-    for (uint32_t u = 0; u < 4; ++u) {
-      const uint32_t j = j0 + u * kWave + lane;
-      if (j < nf) t[u] = load16(src, blk0 + j);
-    }
-#pragma unroll
-    for (uint32_t u = 0; u < 4; ++u) {
-      const uint32_t j = j0 + u * kWave + lane;
-      if (j < nf) *reinterpret_cast<uint4 *>(dst + 4 * j) = t[u];
-    }
-  }
-  for (uint32_t j = nf + lane; j < nb; j += kWave)
-    *reinterpret_cast<uint4 *>(dst + 4 * j) = load16_tail(src, nbytes, blk0 + j);
-}
-
-// Contiguous decode, steps a and b for the tile of segments [u0, u0 + nu): check
-// its bit range and every segment's, fill lbeg/lend (kBad for a bad segment), and
-// stage the range into LDS.  Returns false (after flagging the error) when the
-// tile's range itself is unusable.
-template <uint32_t W>
-__device__ __forceinline__ bool stage_tile(const DecodeArgs &a, uint64_t u0, uint32_t nu, uint32_t nch, uint32_t *stg,
-                                           uint32_t *lbeg, uint32_t *lend, uint32_t lane, uint32_t &err) {
-  const uint64_t A = a.off[u0], B = a.off[u0 + nu];
-  const bool tile_ok = A <= B && B - A <= (uint64_t)nch * (W + 1) && B <= a.stream_bytes * 8u;
-  if (!tile_ok) {
-    if (lane == 0 && a.err) atomicOr(a.err, IBP_DEVERR_CORRUPT);
-    return false;
-  }
-  const uint64_t base = A & ~127ull;
-  for (uint32_t r = lane; r < nu; r += kWave) {
-    const uint64_t x = a.off[u0 + r], y = a.off[u0 + r + 1];
-    const uint64_t m = min((uint64_t)a.S, a.n_chunks - (u0 + r) * a.S);
-    const bool good = A <= x && x <= y && y <= B && y - x >= m && y - x <= m * (W + 1);
-    lbeg[r] = good ? (uint32_t)(x - base) : kBad;
-    lend[r] = good ? (uint32_t)(y - base) : kBad;
-    if (!good) err |= IBP_DEVERR_CORRUPT;
-  }
-  stage_range(a.stream, a.stream_bytes, A >> 7, (uint32_t)(((B + 127u) >> 7) - (A >> 7)), stg, lane);
-  return true;
-}
-
 template <typename T, bool kGather, uint32_t kMode, uint32_t NR>
 __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
@@ -289,114 +238,6 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
   if (err && a.err) atomicOr(a.err, err);
 }
 
-// Position metadata, a whole segment of S chunks (S a multiple of 64) at local
-// bits [lb, le): chunk i = q + lane of pass q saves popcount(Mask_i) bits when it
-// matches, so its payload bit is base + lane W minus the savings of the chunks
-// before it in the pass (an inclusive wave scan, less its own); base then drops by
-// the pass's total, the scan's last lane.
-template <typename T>
-__device__ __forceinline__ uint32_t decode_pos_row(uint32_t S, const uint64_t *mtab, const uint64_t *btab,
-                                                   const uint32_t *stg, uint32_t lb, uint32_t le, T *o,
-                                                   uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  using U = typename std::conditional<(W > 32), uint64_t, uint32_t>::type;
-  constexpr U kFull = W >= 64 ? ~(U)0 : (U)((1ull << (W & 63)) - 1ull);
-  if (lb == kBad) return 0u;
-  const uint32_t lane_bits = lane * W;
-  o += lane;
-  uint32_t hp = lb, base = lb + S;
-  for (uint32_t q = 0; q < S; q += kWave) {
-    const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
-    const bool h = __builtin_amdgcn_inverse_ballot_w64(H);
-    const U m = (U)mtab[q + lane];
-    const uint32_t sv = h ? popc_u(m) : 0u;
-    const uint32_t x = wave_incl_scan(sv);
-    const T xv = lds_field<T>(stg, base + lane_bits - (x - sv));
-    o[q] = h ? (T)(deposit_runs<U>((U)xv, ~m & kFull) | (U)btab[q + lane]) : xv;
-    base += kWave * W - (uint32_t)__builtin_amdgcn_readlane((int)x, kWave - 1);
-    hp += kWave;
-  }
-  return base != le ? IBP_DEVERR_CORRUPT : 0u;
-}
-
-// Contiguous decompression with position-dependent metadata: chunk position i
-// of a segment has its own Mask_i / Bitval_i (device tables, copied to LDS).  The
-// tile is staged as in decode_kernel.  Per pass of 64 tile chunks a lane's payload
-// offset is its segment's payload start + i W minus the bits saved by the earlier
-// matching chunks of the segment, popcount(Mask_j) each: an inclusive wave scan
-// of the savings, less the part before the segment's first lane in the pass, plus
-// a per-segment carry from earlier passes (LDS).  The deposit walks the runs of
-// the lane's own free positions.
-template <typename T>
-__global__ void __launch_bounds__(kBlock) decode_pos_kernel(DecodeArgs a, CodecParams p) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  constexpr uint64_t kFull = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
-  extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
-  uint64_t *mtab = reinterpret_cast<uint64_t *>(smem);
-  uint64_t *btab = mtab + a.S;
-  for (uint32_t i = threadIdx.x; i < a.S; i += kBlock) {
-    const uint64_t m = a.pmask[i] & kFull;
-    mtab[i] = m;
-    btab[i] = a.pbitval[i] & m;
-  }
-  __syncthreads();
-  const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWave);
-  const uint64_t u0 = ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * a.G;
-  if (u0 >= a.n_units) return;
-  const uint32_t nu = (uint32_t)min((uint64_t)a.G, a.n_units - u0);
-  uint32_t *stg = smem + 4u * a.S + (uint64_t)wave * a.wave_dw;
-  uint32_t *lbeg = stg + a.stage_dw;
-  uint32_t *lend = lbeg + a.G;
-  uint32_t *carry = lend + a.G;  // saved bits of each segment in earlier passes
-  const uint64_t chunk0 = u0 * a.S;
-  const uint32_t nch = (uint32_t)min((uint64_t)nu * a.S, a.n_chunks - chunk0);
-  uint32_t err = 0;
-  if (!stage_tile<W>(a, u0, nu, nch, stg, lbeg, lend, lane, err)) return;
-  T *out = static_cast<T *>(a.out) + chunk0;
-  if (a.S % kWave == 0 && nch == nu * a.S) {
-    // whole segments, S a multiple of 64: every pass lies inside one segment
-    wave_lds_sync();
-    for (uint32_t r = 0; r < nu; ++r)
-      err |= decode_pos_row<T>(a.S, mtab, btab, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S,
-                               lane);
-    if (err && a.err) atomicOr(a.err, err);
-    return;
-  }
-  for (uint32_t r = lane; r < nu; r += kWave) carry[r] = 0;
-  wave_lds_sync();
-
-  for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
-    const uint32_t cl = p0 + lane;
-    const bool valid = cl < nch;
-    const uint32_t r = valid ? (a.s_log2 != kNotPow2 ? cl >> a.s_log2 : cl / a.S) : 0u;
-    const uint32_t i = cl - r * a.S;
-    const uint32_t lb = valid ? lbeg[r] : kBad;
-    const bool ok = lb != kBad;
-    const uint32_t m = min(a.S, nch - r * a.S);
-    const bool h = ok && lds_bit(stg, lb + i);
-    const uint64_t mi = ok ? mtab[i] : 0ull;
-    const uint32_t pci = popc(mi);
-    const uint32_t sv = h ? pci : 0u;
-    const uint32_t x = wave_incl_scan(sv);  // inclusive scan of the savings over the pass
-    const uint32_t start = lane >= i ? lane - i : 0u;  // the segment's first lane in this pass
-    const uint32_t xs = __shfl(x, start == 0u ? 0u : start - 1u, kWave);
-    const uint32_t before = start == 0u ? 0u : xs;
-    const uint32_t c = ok ? carry[r] : 0u;
-    const uint32_t pos = ok ? lb + m + i * W - (c + x - sv - before) : 0u;
-    const T xv = lds_field<T>(stg, pos);
-    const T v = h ? (T)(deposit_var<T>(xv, ~mi & kFull) | (T)btab[i]) : xv;
-    if (ok) {
-      out[cl] = v;
-      if (i == m - 1 && pos + (h ? W - pci : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
-    }
-    wave_lds_sync();
-    // the last lane of a segment that continues into the next pass keeps its carry
-    if (ok && lane == kWave - 1 && i != m - 1) carry[r] = c + x - before;
-    wave_lds_sync();
-  }
-  if (err && a.err) atomicOr(a.err, err);
-}
-
 // Uncompressed gather baseline: row j = row ids[j], 16 bytes per lane.
 __global__ void __launch_bounds__(kBlock) raw_gather_kernel(RawGatherArgs a) {
   const uint64_t total = a.n_ids * a.row_blocks;
@@ -461,19 +302,6 @@ hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather,
   if (p.W == 16) return gather ? go_mode<uint16_t, true>(a, p, l) : go_mode<uint16_t, false>(a, p, l);
   if (p.W == 32) return gather ? go_mode<uint32_t, true>(a, p, l) : go_mode<uint32_t, false>(a, p, l);
   return gather ? go_mode<uint64_t, true>(a, p, l) : go_mode<uint64_t, false>(a, p, l);
-}
-
-hipError_t launch_decode_pos(const DecodeArgs &a, const CodecParams &p, hipStream_t s) {
-  if (a.n_units == 0) return hipSuccess;
-  const uint64_t tiles = (a.n_units + a.G - 1) / a.G;
-  const uint64_t blocks = (tiles + kWavesPerBlock - 1) / kWavesPerBlock;
-  if (blocks > 0x7FFFFFFFull || !a.pmask || !a.pbitval) return hipErrorInvalidValue;
-  const size_t shmem = (size_t)a.S * 16 + (size_t)a.wave_dw * 4 * kWavesPerBlock;
-  const dim3 grid((uint32_t)blocks);
-  if (p.W == 16) hipLaunchKernelGGL(decode_pos_kernel<uint16_t>, grid, dim3(kBlock), shmem, s, a, p);
-  else if (p.W == 32) hipLaunchKernelGGL(decode_pos_kernel<uint32_t>, grid, dim3(kBlock), shmem, s, a, p);
-  else hipLaunchKernelGGL(decode_pos_kernel<uint64_t>, grid, dim3(kBlock), shmem, s, a, p);
-  return hipGetLastError();
 }
 
 hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s) {

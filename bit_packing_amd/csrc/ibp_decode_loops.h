@@ -25,6 +25,57 @@ enum : uint32_t {
   kModeLargeS = 2,   // S % 64 == 0: each pass lies inside one segment
 };
 
+// Stage the 16-byte blocks [blk0, blk0 + nb) of src into LDS at dst.  Whole
+// blocks are loaded four per lane before any is written (up to 256 loads in
+// flight per wavefront); the block holding the end of a source whose length is
+// not a multiple of 16 is read byte by byte afterwards.
+__device__ __forceinline__ void stage_range(const uint8_t *src, uint64_t nbytes, uint64_t blk0, uint32_t nb,
+                                            uint32_t *dst, uint32_t lane) {
+  const uint64_t whole = nbytes >> 4;
+  const uint32_t nf = blk0 >= whole ? 0u : (uint32_t)min((uint64_t)nb, whole - blk0);
+  for (uint32_t j0 = 0; j0 < nf; j0 += 4 * kWave) {
+    uint4 t[4];
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const uint32_t j = j0 + u * kWave + lane;
+      if (j < nf) t[u] = load16(src, blk0 + j);
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < 4; ++u) {
+      const uint32_t j = j0 + u * kWave + lane;
+      if (j < nf) *reinterpret_cast<uint4 *>(dst + 4 * j) = t[u];
+    }
+  }
+  for (uint32_t j = nf + lane; j < nb; j += kWave)
+    *reinterpret_cast<uint4 *>(dst + 4 * j) = load16_tail(src, nbytes, blk0 + j);
+}
+
+// Contiguous decode, steps a and b for the tile of segments [u0, u0 + nu): check
+// its bit range and every segment's, fill lbeg/lend (kBad for a bad segment), and
+// stage the range into LDS.  Returns false (after flagging the error) when the
+// tile's range itself is unusable.
+template <uint32_t W>
+__device__ __forceinline__ bool stage_tile(const DecodeArgs &a, uint64_t u0, uint32_t nu, uint32_t nch, uint32_t *stg,
+                                           uint32_t *lbeg, uint32_t *lend, uint32_t lane, uint32_t &err) {
+  const uint64_t A = a.off[u0], B = a.off[u0 + nu];
+  const bool tile_ok = A <= B && B - A <= (uint64_t)nch * (W + 1) && B <= a.stream_bytes * 8u;
+  if (!tile_ok) {
+    if (lane == 0 && a.err) atomicOr(a.err, IBP_DEVERR_CORRUPT);
+    return false;
+  }
+  const uint64_t base = A & ~127ull;
+  for (uint32_t r = lane; r < nu; r += kWave) {
+    const uint64_t x = a.off[u0 + r], y = a.off[u0 + r + 1];
+    const uint64_t m = min((uint64_t)a.S, a.n_chunks - (u0 + r) * a.S);
+    const bool good = A <= x && x <= y && y <= B && y - x >= m && y - x <= m * (W + 1);
+    lbeg[r] = good ? (uint32_t)(x - base) : kBad;
+    lend[r] = good ? (uint32_t)(y - base) : kBad;
+    if (!good) err |= IBP_DEVERR_CORRUPT;
+  }
+  stage_range(a.stream, a.stream_bytes, A >> 7, (uint32_t)(((B + 127u) >> 7) - (A >> 7)), stg, lane);
+  return true;
+}
+
 // S a multiple of 64: the segments of the tile one after another, 64 chunks per pass.
 template <typename T, uint32_t NR>
 __device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,

@@ -56,7 +56,7 @@ def _meta(ibp, dev, W, S, masks, bitvals):
 
 
 @pytest.mark.parametrize("W", [16, 32, 64])
-@pytest.mark.parametrize("S", [1, 3, 32, 100, 128, 256, 1000])
+@pytest.mark.parametrize("S", [1, 3, 32, 64, 100, 128, 192, 256, 1000, 1024])
 def test_pos_compress_decompress_parity(ibp, W, S):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(31 * W + S)
@@ -82,6 +82,51 @@ def test_pos_compress_decompress_parity(ibp, W, S):
         assert torch.equal(out2, x), f"n={n}: decode of the oracle stream"
         torch.cuda.synchronize()
         assert int(err.item()) == 0
+
+
+def _data_rows(rng, n, W, masks, bitvals, S, p):
+    """As _data, row by row (fast for large n): chunk j has position j % S."""
+    dt = DT[W]
+    v = rng.integers(0, np.iinfo(dt).max, size=n, dtype=dt, endpoint=True)
+    rows = n // S
+    body = v[: rows * S].reshape(rows, S)
+    hit = rng.random((rows, S)) < p
+    m, b = masks.astype(dt), bitvals.astype(dt)
+    body[...] = np.where(hit, (body & ~m[None, :]) | b[None, :], body)
+    return v
+
+
+# n above what four times the resident workgroups cover in one sweep (the grid is
+# capped there and each workgroup loops over tiles), for the paths: W = 16 pairs
+# with shift steps, W = 32 any S, W = 64 one chunk per lane; the smaller cases add
+# the W = 16 one-per-lane and W = 32 pair paths and a W = 64 S of one tile per wave.
+@pytest.mark.parametrize("W,S,n", [(16, 1024, (1 << 25) + 77), (32, 100, 20_000_077), (64, 256, (1 << 24) + 77),
+                                   (16, 64, 1_000_077), (32, 256, 1_000_077), (64, 1000, 1_000_077)])
+def test_pos_decode_many_tiles(ibp, W, S, n):
+    """Large inputs (each workgroup loops over many tiles): the decode of the
+    oracle's stream equals the input, and so does a decode into an output one
+    chunk past an aligned address."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(5 * W + S)
+    masks, bitvals = _tables(rng, S, W)
+    meta = _meta(ibp, dev, W, S, masks, bitvals)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    say(f"pos many tiles W={W} S={S} n={n}")
+    v = _data_rows(rng, n, W, masks, bitvals, S, 0.8)
+    ref_stream, ref_off = oracle.encode_pos(v, W, masks, bitvals, S)
+    x = torch.from_numpy(v.view(np.uint8)).to(dev)
+    s_d = torch.from_numpy(ref_stream).to(dev)
+    o_d = torch.from_numpy(ref_off.view(np.int64)).to(dev)
+    out = ibp.ibp_decompress_pos(meta, s_d, o_d, n, err=err)
+    assert torch.equal(out, x), "decode of the oracle stream"
+    del out
+    cb = W // 8
+    big = torch.zeros(n * cb + 16, dtype=torch.uint8, device=dev)
+    out2 = big[cb: cb + n * cb]
+    ibp.ibp_decompress_pos(meta, s_d, o_d, n, out=out2, err=err)
+    assert torch.equal(out2, x), "decode into an unaligned output"
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
 
 
 @pytest.mark.parametrize("W", [16, 32, 64])
