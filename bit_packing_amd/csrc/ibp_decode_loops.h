@@ -140,7 +140,10 @@ __device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S,
 // bits itself; the compressed chunks before chunk 2l are those below lane l in
 // the ballot of the even chunks plus those in the ballot of the odd ones, and
 // the two ballots' popcounts give the pass's total.  The pair is stored as one
-// 2W-bit word, so o must be 2W/8-byte aligned.
+// 2W-bit word, so o must be 2W/8-byte aligned.  For W = 16 both chunks lie in
+// the 32 bits from chunk 2l's payload, read once; the second sits 16 - pc bits up
+// when the first is compressed, and the deposit runs on the pair word with each
+// run's mask in both halves (a run never crosses a half).
 template <typename T, uint32_t NR>
 __device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
                                                 uint32_t le, T *o, uint32_t lane) {
@@ -158,11 +161,26 @@ __device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S
     const bool h0 = (b2 & 1u) != 0u, h1 = b2 > 1u;
     const uint64_t E = ballot(h0), O = ballot(h1);
     const uint32_t pos0 = base + lane_bits - __umul24(pc, count_below(E) + count_below(O));
-    const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
-    const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
-    const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | bitval) : x0;
-    const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | bitval) : x1;
-    op[q / 2] = (P)v0 | ((P)v1 << W);
+    if constexpr (W == 16) {
+      const uint32_t w = lds_field<uint32_t>(stg, pos0);
+      const uint32_t x = (w & 0xFFFFu) | ((w << (h0 ? pc : 0u)) & 0xFFFF0000u);
+      uint32_t d = (uint32_t)bitval * 0x10001u;
+      if constexpr (NR == 0) {
+        for (uint32_t r = 0; r < p.runs.n; ++r)
+          d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
+      } else {
+#pragma unroll
+        for (uint32_t r = 0; r < NR; ++r) d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
+      }
+      const uint32_t sel = (h0 ? 0x0000FFFFu : 0u) | (h1 ? 0xFFFF0000u : 0u);
+      op[q / 2] = (P)((sel & d) | (~sel & x));
+    } else {
+      const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
+      const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
+      const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | bitval) : x0;
+      const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | bitval) : x1;
+      op[q / 2] = (P)v0 | ((P)v1 << W);
+    }
     base += 2u * kWave * W - pc * (popc(E) + popc(O));
     hp += 2u * kWave;
   }

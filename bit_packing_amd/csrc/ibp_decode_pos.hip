@@ -267,9 +267,10 @@ __device__ __forceinline__ uint32_t pos_row2(uint32_t S, const uint4 *tab, uint3
       const uint32_t s0 = h0 ? (e1.z & 0xFFFFu) : 0u, s1 = h1 ? (e1.z >> 16) : 0u;
       const uint32_t s = s0 + s1;
       const uint32_t incl = wave_incl_scan(s);
-      const uint32_t pos0 = base + 2u * lane * W - (incl - s), pos1 = pos0 + W - s0;
-      const uint32_t x = __builtin_amdgcn_perm(lds_field<uint32_t>(stg, pos1), lds_field<uint32_t>(stg, pos0),
-                                               0x05040100u);  // low halves: chunk 2l, chunk 2l + 1
+      // both chunks lie in the 32 bits from chunk 2l's payload; the second sits
+      // 16 - popcount(Mask) bits up when the first matches
+      const uint32_t w = lds_field<uint32_t>(stg, base + 2u * lane * W - (incl - s));
+      const uint32_t x = bfi(0xFFFFu, w, w << s0);
       const uint32_t sel = (h0 ? 0x0000FFFFu : 0u) | (h1 ? 0xFFFF0000u : 0u);
       op[q / 2] = (P)bfi(sel, kShift ? expand16x2(x, tab[i >> 1], e1) : bfi(e1.x, x, e1.y), x);
       base += 2u * kWave * W - last_lane(incl);
