@@ -66,14 +66,14 @@ uint32_t meta_blocks(uint64_t n) {
   return (uint32_t)(want < 1 ? 1 : (want > kMetaMaxBlocks ? kMetaMaxBlocks : want));
 }
 
-uint32_t enc_segs_per_tile(uint32_t S, bool pos) {
-  const uint32_t tile = enc_tile_chunks(pos);
+uint32_t enc_segs_per_tile(uint32_t S, bool pos, bool pair = false) {
+  const uint32_t tile = enc_tile_chunks(pos, pair);
   return S >= tile ? 1u : tile / S;
 }
 
-uint64_t enc_tiles(uint64_t n_chunks, uint32_t S, bool pos) {
+uint64_t enc_tiles(uint64_t n_chunks, uint32_t S, bool pos, bool pair = false) {
   const uint64_t nseg = (n_chunks + S - 1) / S;
-  const uint32_t G = enc_segs_per_tile(S, pos);
+  const uint32_t G = enc_segs_per_tile(S, pos, pair);
   return (nseg + G - 1) / G;
 }
 
@@ -228,14 +228,17 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   a.off = d_offsets;
   a.control = static_cast<uint32_t *>(d_workspace);
   a.status = reinterpret_cast<uint64_t *>(static_cast<uint8_t *>(d_workspace) + 8);
-  a.ntiles = enc_tiles(n, S, pmask != nullptr);
+  // W = 16 with one Mask reads chunk pairs as 32-bit words when the segments are
+  // whole 64-chunk blocks and the input allows it
+  a.pair = (p.W == 16 && !pmask && S % kWave == 0 && aligned(d_in, 4)) ? 1u : 0u;
+  a.ntiles = enc_tiles(n, S, pmask != nullptr, a.pair != 0u);
   a.tails = a.status + a.ntiles;
   a.err = d_err_word;
   a.n_chunks = n;
   a.nseg = nseg;
   a.S = S;
   a.s_log2 = log2_if_pow2(S);
-  a.G = enc_segs_per_tile(S, pmask != nullptr);
+  a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u);
   a.tile_chunks = a.G * S;
   a.obuf_dw = ((127 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;  // image from the 16-byte block of the first bit
   return status_of(launch_encode(a, p, s));

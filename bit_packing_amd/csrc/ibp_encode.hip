@@ -23,7 +23,8 @@ enum : uint32_t {
   kModeLargeS = 2,   // S % 64 == 0: each 64-chunk block lies inside one segment
 };
 
-// One workgroup per tile of G consecutive segments (about 16 chunks per thread).
+// One workgroup per tile of G consecutive segments (about 16 chunks per thread,
+// 32 in the W = 16 pair form).
 //  1. tile t = workgroup index (see lookback_exclusive for why the order holds);
 //  2. load the chunks (16 per thread, 64 consecutive per wavefront per pass),
 //     test the invariant bits and ballot the participation bits; clear the LDS
@@ -45,22 +46,49 @@ enum : uint32_t {
 // The per-chunk prefix count has the decoder's three forms (S a multiple of 64,
 // S dividing 64, any S).
 //
+// kPair (W = 16, one Mask, S a multiple of 64, input 4-byte aligned): a lane
+// takes two consecutive chunks as one 32-bit word per pass (128 chunks per
+// wavefront), tests both, and ballots the even and the odd chunks.  A 64-chunk
+// block's word holds its 32 even chunks' bits low and its 32 odd chunks' bits
+// high (its popcount, all the prefix counts need, is the same) and is interleaved
+// into stream order only where the header is written.  The free
+// bits of both chunks are extracted together on the pair word (each run's mask
+// in both halves: a run never crosses a half), and the two payloads go into LDS
+// as one field of at most 32 bits, half the LDS atomics of one chunk per lane.
+//
 // kPos: position-dependent metadata.  Chunk position i of a segment has its own
 // Mask_i / Bitval_i (tables in device memory, copied to LDS), so a matching chunk
 // saves popcount(Mask_i) bits instead of a constant: the count of compressed
 // chunks times popcount(Mask) becomes a prefix sum of per-chunk savings (a wave
 // scan per 64-chunk block plus a scan over the blocks), and the extraction walks
 // the runs of each lane's own free positions.
-template <typename T, uint32_t kMode, uint32_t NR, bool kPos>
-__global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock) encode_kernel(EncodeArgs a, CodecParams p) {
+// Bits 0..31 of e at the even positions of the result, of o at the odd ones.
+__device__ __forceinline__ uint64_t interleave32(uint32_t e, uint32_t o) {
+  auto spread = [](uint64_t x) {
+    x = (x | (x << 16)) & 0x0000FFFF0000FFFFull;
+    x = (x | (x << 8)) & 0x00FF00FF00FF00FFull;
+    x = (x | (x << 4)) & 0x0F0F0F0F0F0F0F0Full;
+    x = (x | (x << 2)) & 0x3333333333333333ull;
+    return (x | (x << 1)) & 0x5555555555555555ull;
+  };
+  return spread(e) | (spread(o) << 1);
+}
+
+// The pair form asks for 8 wavefronts per SIMD (its 16 unrolled passes otherwise
+// take enough scalar registers to allow only 7: 1.28 -> 1.11 ms per 2^30 chunks).
+template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false>
+__global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock, kPair ? 8 : 1)
+    encode_kernel(EncodeArgs a, CodecParams p) {
+  static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = kPos ? kEncBlockPos : kEncBlock;
   constexpr uint32_t kWaves = kThreads / kWave;
-  constexpr uint32_t kTile = enc_tile_chunks(kPos);
+  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair);
   constexpr uint32_t kQ = kTile / kThreads;  // passes of kThreads chunks
   constexpr uint32_t kBal = kTile / kWave;   // 64-chunk blocks per tile
   constexpr uint32_t kPer = (kBal + kWave - 1) / kWave;  // 64-chunk blocks per lane of the prefix scan
   static_assert(kBal <= kWave || kBal == kPer * kWave, "whole blocks per lane of the prefix scan");
+  constexpr uint32_t kQP = kPair ? kQ / 2 : 1;  // kPair: passes of kThreads chunk pairs
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   uint32_t *obuf = smem;
   uint64_t *bal = reinterpret_cast<uint64_t *>(smem + a.obuf_dw);  // kBal words
@@ -86,7 +114,20 @@ __global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock) encode_kernel
 
   // 2. chunks, participation bits; clear the image meanwhile
   T v[kQ];
-  if (nch == kTile) {  // every tile but possibly the last: no bounds tests
+  uint32_t v2[kQP];  // kPair: chunks 2 (q kThreads + tid) and the next one
+  if constexpr (kPair) {
+    const uint32_t *in2 = reinterpret_cast<const uint32_t *>(in);
+    if (nch == kTile) {
+#pragma unroll
+      for (uint32_t q = 0; q < kQP; ++q) v2[q] = in2[q * kThreads + tid];
+    } else {
+#pragma unroll
+      for (uint32_t q = 0; q < kQP; ++q) {
+        const uint32_t c = 2u * (q * kThreads + tid);
+        v2[q] = c + 1u < nch ? in2[c / 2u] : (c < nch ? (uint32_t)in[c] : 0u);
+      }
+    }
+  } else if (nch == kTile) {  // every tile but possibly the last: no bounds tests
 #pragma unroll
     for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kThreads + tid];
   } else {
@@ -118,8 +159,29 @@ __global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock) encode_kernel
     __syncthreads();
   }
   uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
+  // kPair: participation of the even and of the odd chunk of pass q's pair (taken
+  // again when packing rather than held in scalar registers across the barriers)
+  auto even_odd = [&](uint32_t q, bool &h0, bool &h1) {
+    const uint32_t c = 2u * (q * kThreads + tid);
+    const uint32_t m32 = (uint32_t)mask, b32 = (uint32_t)bitval;
+    h0 = c < nch && (((v2[q] & 0xFFFFu) ^ b32) & m32) == 0u;
+    h1 = c + 1u < nch && (((v2[q] >> 16) ^ b32) & m32) == 0u;
+  };
+  if constexpr (kPair) {
 #pragma unroll
-  for (uint32_t q = 0; q < kQ; ++q) {
+    for (uint32_t q = 0; q < kQP; ++q) {
+      bool h0, h1;
+      even_odd(q, h0, h1);
+      const uint64_t E = ballot(h0), O = ballot(h1);
+      if (lane == 0) {  // the span's two 64-chunk blocks: lanes 0-31, lanes 32-63
+        const uint32_t b = 2u * (q * kWaves + wave);
+        bal[b] = (E & 0xFFFFFFFFull) | (O << 32);
+        bal[b + 1] = (E >> 32) | (O & 0xFFFFFFFF00000000ull);
+      }
+    }
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < (kPair ? 0u : kQ); ++q) {
     const uint32_t cl = q * kThreads + tid;
     if constexpr (kPos) {
       const uint64_t m = mtab[ip[q]];
@@ -199,8 +261,36 @@ __global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock) encode_kernel
   };
   const uint32_t i_lane = lane & (a.S - 1u);                   // small-S: index in segment
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
+  if constexpr (kPair) {
 #pragma unroll
-  for (uint32_t q = 0; q < kQ; ++q) {
+    for (uint32_t q = 0; q < kQP; ++q) {
+      const uint32_t blk = 2u * (q * kWaves + wave);  // first of the span's two 64-chunk blocks
+      const uint32_t cb = blk * kWave;
+      if (cb >= nch) continue;  // uniform
+      const uint32_t c = cb + 2u * lane;
+      // the two blocks may lie in different segments (S = 64)
+      const uint32_t s_lo = seg_start(cb), s_hi = seg_start(min(cb + kWave, nch - 1u));
+      const uint32_t s0 = lane < 32u ? s_lo : s_hi;
+      const uint32_t m = min(a.S, nch - s0);
+      bool h0, h1;
+      even_odd(q, h0, h1);
+      const uint32_t saved = __umul24(pc, pref_at(blk) + count_below(ballot(h0)) + count_below(ballot(h1)));
+      const uint32_t pos = s0 + m + c * W - saved;
+      const uint32_t x = v2[q];
+      uint32_t ext = 0;
+      if constexpr (NR == 0) {
+        for (uint32_t r = 0; r < p.runs.n; ++r) ext |= (x >> p.runs.shift[r]) & ((uint32_t)p.runs.pmask[r] * 0x10001u);
+      } else {
+#pragma unroll
+        for (uint32_t r = 0; r < NR; ++r) ext |= (x >> p.runs.shift[r]) & ((uint32_t)p.runs.pmask[r] * 0x10001u);
+      }
+      const uint32_t a0 = h0 ? (ext & 0xFFFFu) : (x & 0xFFFFu), a1 = h1 ? (ext >> 16) : (x >> 16);
+      const uint32_t field = a0 | (a1 << (h0 ? W - pc : W));
+      lds_or_bits(obuf, c < nch ? pos : 0u, c < nch ? field : 0u);  // lanes past the tile hold 0
+    }
+  }
+#pragma unroll
+  for (uint32_t q = 0; q < (kPair ? 0u : kQ); ++q) {
     const uint32_t blk = q * kWaves + wave;  // this wavefront's 64-chunk block
     const uint32_t cb = blk * kWave;                 // its first tile chunk
     if (cb >= nch) continue;                         // uniform
@@ -267,7 +357,8 @@ __global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock) encode_kernel
     const uint32_t blk = lane * kWaves + wave, cb = blk * kWave;
     if (lane < kQ && cb < nch) {
       const uint32_t s0 = seg_start(cb);
-      lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6], bal[blk]);
+      const uint64_t hdr = kPair ? interleave32((uint32_t)bal[blk], (uint32_t)(bal[blk] >> 32)) : bal[blk];
+      lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6], hdr);
     }
   }
   __syncthreads();
@@ -364,10 +455,10 @@ __global__ void __launch_bounds__(kBlock) zero_kernel(uint64_t *p, uint64_t n) {
 
 static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; }
 
-template <typename T, uint32_t M, uint32_t NR, bool kPos = false>
+template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos>), dim3((uint32_t)a.ntiles), dim3(kPos ? kEncBlockPos : kEncBlock),
-                     shmem, s, a, p);
+  hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos, kPair>), dim3((uint32_t)a.ntiles),
+                     dim3(kPos ? kEncBlockPos : kEncBlock), shmem, s, a, p);
   return hipGetLastError();
 }
 
@@ -378,23 +469,26 @@ static hipError_t launch_encode_pos_w(const EncodeArgs &a, const CodecParams &p,
   return launch_encode_t<T, kModeGeneral, 0, true>(a, p, shmem, s);
 }
 
-template <typename T, uint32_t M>
+template <typename T, uint32_t M, bool kPair = false>
 static hipError_t launch_encode_runs(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
   switch (runs_bucket(p.runs.n)) {
-    case 1: return launch_encode_t<T, M, 1>(a, p, shmem, s);
-    case 2: return launch_encode_t<T, M, 2>(a, p, shmem, s);
-    case 3: return launch_encode_t<T, M, 3>(a, p, shmem, s);
-    case 4: return launch_encode_t<T, M, 4>(a, p, shmem, s);
-    case 5: return launch_encode_t<T, M, 5>(a, p, shmem, s);
-    case 6: return launch_encode_t<T, M, 6>(a, p, shmem, s);
-    case 7: return launch_encode_t<T, M, 7>(a, p, shmem, s);
-    case 8: return launch_encode_t<T, M, 8>(a, p, shmem, s);
-    default: return launch_encode_t<T, M, 0>(a, p, shmem, s);
+    case 1: return launch_encode_t<T, M, 1, false, kPair>(a, p, shmem, s);
+    case 2: return launch_encode_t<T, M, 2, false, kPair>(a, p, shmem, s);
+    case 3: return launch_encode_t<T, M, 3, false, kPair>(a, p, shmem, s);
+    case 4: return launch_encode_t<T, M, 4, false, kPair>(a, p, shmem, s);
+    case 5: return launch_encode_t<T, M, 5, false, kPair>(a, p, shmem, s);
+    case 6: return launch_encode_t<T, M, 6, false, kPair>(a, p, shmem, s);
+    case 7: return launch_encode_t<T, M, 7, false, kPair>(a, p, shmem, s);
+    case 8: return launch_encode_t<T, M, 8, false, kPair>(a, p, shmem, s);
+    default: return launch_encode_t<T, M, 0, false, kPair>(a, p, shmem, s);
   }
 }
 
 template <typename T>
 static hipError_t launch_encode_w(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (a.pair) return launch_encode_runs<T, kModeLargeS, true>(a, p, shmem, s);
+  }
   if (a.S % kWave == 0) return launch_encode_runs<T, kModeLargeS>(a, p, shmem, s);
   if (kWave % a.S == 0) return launch_encode_runs<T, kModeSmallS>(a, p, shmem, s);
   return launch_encode_t<T, kModeGeneral, 0>(a, p, shmem, s);
@@ -415,7 +509,7 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
   // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
-  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr);
+  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u);
   size_t shmem = (size_t)a.obuf_dw * 4 + (tile / kWave) * 8 + ((tile / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   if (a.pmask) {

@@ -18,10 +18,13 @@ constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-
 // workloads: 512 threads beat 256 by 3-10% with one Mask (1024 did not), while
 // position metadata is fastest at 256 (its LDS per workgroup doubles with the
 // tile); 128 and 64 threads were 10-50% slower, their per-tile costs spread over
-// fewer chunks.
+// fewer chunks.  The W = 16 pair form (two chunks per lane) takes 32 chunks per
+// thread, so a tile still moves 32 KB of input.
 constexpr uint32_t kEncBlock = 512;
 constexpr uint32_t kEncBlockPos = 256;
-constexpr uint32_t enc_tile_chunks(bool pos) { return 16u * (pos ? kEncBlockPos : kEncBlock); }
+constexpr uint32_t enc_tile_chunks(bool pos, bool pair = false) {
+  return (pair ? 32u : 16u) * (pos ? kEncBlockPos : kEncBlock);
+}
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
@@ -84,6 +87,7 @@ struct EncodeArgs {
   uint32_t G;          // segments per tile
   uint32_t tile_chunks;
   uint32_t obuf_dw;    // LDS dwords for the packed tile
+  uint32_t pair;       // 1: W = 16 chunk pairs (one Mask, S a multiple of 64, input 4-byte aligned)
 };
 
 struct DecodeArgs {

@@ -87,7 +87,7 @@ def _run_case(ibp, dev, v, W, S, mask, bitval, tag):
 
 
 @pytest.mark.parametrize("W", [16, 32, 64])
-@pytest.mark.parametrize("S", [1, 3, 32, 100, 128, 256, 1000, 1024])
+@pytest.mark.parametrize("S", [1, 3, 32, 64, 100, 128, 192, 256, 1000, 1024])
 def test_compress_decompress_parity(ibp, W, S):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(W * 10007 + S)
@@ -278,6 +278,31 @@ def test_host_argument_checks(ibp):
     rc = lib.ibp_decompress(ibp.ctypes.byref(meta), stream.data_ptr(), 1 << 40, off.data_ptr(), 128, 128,
                             torch.empty(512, dtype=torch.uint8, device=dev).data_ptr(), None, None)
     assert rc == ibp.IBP_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("S", [64, 128])
+def test_compress_w16_input_two_bytes_past_alignment(ibp, S):
+    """W = 16 input that starts 2 bytes past a 4-byte boundary (the compressor reads
+    chunk pairs as 32-bit words only from 4-byte aligned inputs): the same stream
+    and offsets as the oracle, and as the compression of an aligned copy."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(S + 16)
+    W = 16
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    for name, mask, bitval in _masks(rng, W):
+        n = 20_000 * (S // 64) + 7
+        say(f"w16 input +2 bytes {name} S={S} n={n}")
+        v = _data(rng, n, W, mask, bitval, 0.9)
+        meta = ibp.make_meta(W, mask, bitval)
+        big = torch.zeros(2 * n + 8, dtype=torch.uint8, device=dev)
+        x = big[2: 2 + 2 * n]
+        x.copy_(torch.from_numpy(v.view(np.uint8).copy()).to(dev))
+        comp = ibp.ibp_compress(meta, x, S, err=err)
+        ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+        assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off), f"{name}: offsets"
+        assert np.array_equal(comp.stream[: ref_stream.size].cpu().numpy(), ref_stream), f"{name}: stream"
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
 
 
 @pytest.mark.parametrize("src,dst", [("pinned", "device"), ("device", "pinned"), ("pinned", "pinned")])
