@@ -66,14 +66,14 @@ uint32_t meta_blocks(uint64_t n) {
   return (uint32_t)(want < 1 ? 1 : (want > kMetaMaxBlocks ? kMetaMaxBlocks : want));
 }
 
-uint32_t enc_segs_per_tile(uint32_t S, bool pos, bool pair = false) {
-  const uint32_t tile = enc_tile_chunks(pos, pair);
+uint32_t enc_segs_per_tile(uint32_t S, bool pos, bool pair, uint32_t W) {
+  const uint32_t tile = enc_tile_chunks(pos, pair, W);
   return S >= tile ? 1u : tile / S;
 }
 
-uint64_t enc_tiles(uint64_t n_chunks, uint32_t S, bool pos, bool pair = false) {
+uint64_t enc_tiles(uint64_t n_chunks, uint32_t S, bool pos, bool pair, uint32_t W) {
   const uint64_t nseg = (n_chunks + S - 1) / S;
-  const uint32_t G = enc_segs_per_tile(S, pos, pair);
+  const uint32_t G = enc_segs_per_tile(S, pos, pair, W);
   return (nseg + G - 1) / G;
 }
 
@@ -159,7 +159,7 @@ IBP_API uint64_t ibp_metadata_workspace_bytes(uint64_t n_sample_chunks, uint32_t
 
 IBP_API uint64_t ibp_compress_workspace_bytes(uint64_t n_chunks, uint32_t S) {
   if (S == 0) return 0;
-  return 8 + 16 * enc_tiles(n_chunks, S, true);  // position-metadata tiles are the smaller ones
+  return 8 + 16 * enc_tiles(n_chunks, S, true, false, 32);  // the smallest tiles (position metadata, W > 16)
 }
 
 IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, uint32_t W, double T,
@@ -231,14 +231,14 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   // W = 16 with one Mask reads chunk pairs as 32-bit words when the segments are
   // whole 64-chunk blocks and the input allows it
   a.pair = (p.W == 16 && !pmask && S % kWave == 0 && aligned(d_in, 4)) ? 1u : 0u;
-  a.ntiles = enc_tiles(n, S, pmask != nullptr, a.pair != 0u);
+  a.ntiles = enc_tiles(n, S, pmask != nullptr, a.pair != 0u, p.W);
   a.tails = a.status + a.ntiles;
   a.err = d_err_word;
   a.n_chunks = n;
   a.nseg = nseg;
   a.S = S;
   a.s_log2 = log2_if_pow2(S);
-  a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u);
+  a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W);
   a.tile_chunks = a.G * S;
   a.obuf_dw = ((127 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;  // image from the 16-byte block of the first bit
   return status_of(launch_encode(a, p, s));

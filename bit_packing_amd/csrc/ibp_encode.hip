@@ -77,13 +77,13 @@ __device__ __forceinline__ uint64_t interleave32(uint32_t e, uint32_t o) {
 // The pair form asks for 8 wavefronts per SIMD (its 16 unrolled passes otherwise
 // take enough scalar registers to allow only 7: 1.28 -> 1.11 ms per 2^30 chunks).
 template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false>
-__global__ void __launch_bounds__(kPos ? kEncBlockPos : kEncBlock, kPair ? 8 : 1)
+__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 1)
     encode_kernel(EncodeArgs a, CodecParams p) {
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   constexpr uint32_t W = sizeof(T) * 8;
-  constexpr uint32_t kThreads = kPos ? kEncBlockPos : kEncBlock;
+  constexpr uint32_t kThreads = enc_threads(kPos, W);
   constexpr uint32_t kWaves = kThreads / kWave;
-  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair);
+  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair, W);
   constexpr uint32_t kQ = kTile / kThreads;  // passes of kThreads chunks
   constexpr uint32_t kBal = kTile / kWave;   // 64-chunk blocks per tile
   constexpr uint32_t kPer = (kBal + kWave - 1) / kWave;  // 64-chunk blocks per lane of the prefix scan
@@ -458,7 +458,7 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
   hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos, kPair>), dim3((uint32_t)a.ntiles),
-                     dim3(kPos ? kEncBlockPos : kEncBlock), shmem, s, a, p);
+                     dim3(enc_threads(kPos, sizeof(T) * 8)), shmem, s, a, p);
   return hipGetLastError();
 }
 
@@ -509,7 +509,7 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
   // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
-  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u);
+  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u, p.W);
   size_t shmem = (size_t)a.obuf_dw * 4 + (tile / kWave) * 8 + ((tile / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   if (a.pmask) {

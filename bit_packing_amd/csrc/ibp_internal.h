@@ -12,18 +12,17 @@ constexpr uint32_t kBlock = 256;        // threads per workgroup for every kerne
 constexpr uint32_t kWavesPerBlock = kBlock / kWave;
 constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-bit chunk
 
-// Compression: a workgroup of kEncBlock threads sizes, offsets and packs a tile
-// of 16 chunks per thread; with position-dependent metadata, whose tables and
-// per-chunk prefixes also live in LDS, kEncBlockPos threads.  Measured on the
-// workloads: 512 threads beat 256 by 3-10% with one Mask (1024 did not), while
-// position metadata is fastest at 256 (its LDS per workgroup doubles with the
-// tile); 128 and 64 threads were 10-50% slower, their per-tile costs spread over
-// fewer chunks.  The W = 16 pair form (two chunks per lane) takes 32 chunks per
-// thread, so a tile still moves 32 KB of input.
-constexpr uint32_t kEncBlock = 512;
-constexpr uint32_t kEncBlockPos = 256;
-constexpr uint32_t enc_tile_chunks(bool pos, bool pair = false) {
-  return (pair ? 32u : 16u) * (pos ? kEncBlockPos : kEncBlock);
+// Compression: a workgroup of enc_threads() threads sizes, offsets and packs a
+// tile of 16 chunks per thread.  Measured on the workloads: 512 threads beat 256
+// by 3-10% with one Mask (1024 did not); with position-dependent metadata, whose
+// tables and per-chunk prefixes also live in LDS, 256 is fastest at W = 32 and 64
+// (512: 17-50% slower) and 512 at W = 16 (4.4 -> 3.3 ms per 2^30 chunks); 128 and
+// 64 threads were 10-50% slower, their per-tile costs spread over fewer chunks.
+// The W = 16 pair form (two chunks per lane) takes 32 chunks per thread, so a
+// tile still moves 32 KB of input.
+constexpr uint32_t enc_threads(bool pos, uint32_t W) { return pos && W != 16 ? 256u : 512u; }
+constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W) {
+  return (pair ? 32u : 16u) * enc_threads(pos, W);
 }
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
