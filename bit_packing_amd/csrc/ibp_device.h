@@ -312,7 +312,9 @@ __device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *contro
 
 }  // namespace dev
 
-// Compile-time run count for a runtime one: 1..8 exactly, 0 = loop.
-inline uint32_t runs_bucket(uint32_t n) { return (n >= 1 && n <= 8) ? n : 0u; }
+// Template run count for n runs: 1..8 unrolled, 0 = a loop over the runtime count.
+// No free bits (Mask covers the chunk) takes the one-run form: the unused entry is
+// zero (pmask 0, shift 0), so the deposit is 0 with no loop.
+inline uint32_t runs_bucket(uint32_t n) { return n <= 8 ? (n == 0 ? 1u : n) : 0u; }
 
 }  // namespace ibp
