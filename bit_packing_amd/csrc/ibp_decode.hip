@@ -121,21 +121,24 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
           // decode each row as soon as its own blocks have arrived, while the
           // later rows' loads are still in flight
           T *out = static_cast<T *>(a.out) + chunk0;
-          auto row = [&](uint32_t r, const uint4 &t) {
-            put(r, t);
+          // rows four at a time, their passes interleaved (four independent
+          // LDS-latency chains)
+          auto rows = [&](uint32_t r, const uint4 &t0, const uint4 &t1, const uint4 &t2, const uint4 &t3) {
+            put(r, t0);
+            put(r + 1, t1);
+            put(r + 2, t2);
+            put(r + 3, t3);
             wave_lds_sync();
-            if (r < nu)
-              err |= decode_segment<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S,
-                                           lane);
+            if (r + 3 < nu) {
+              err |= decode_segments<T, NR, 4>(p, a.S, stg, lbeg, lend, r, out + (uint64_t)r * a.S, lane);
+            } else {
+              for (uint32_t k = r; k < nu; ++k)
+                err |= decode_segment<T, NR>(p, a.S, stg, uniform(lbeg[k]), uniform(lend[k]), out + (uint64_t)k * a.S,
+                                             lane);
+            }
           };
-          row(0, t0);
-          row(1, t1);
-          row(2, t2);
-          row(3, t3);
-          row(4, t4);
-          row(5, t5);
-          row(6, t6);
-          row(7, t7);
+          rows(0, t0, t1, t2, t3);
+          rows(4, t4, t5, t6, t7);
           if (err && a.err) atomicOr(a.err, err);
           return;
         }

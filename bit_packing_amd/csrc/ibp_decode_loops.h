@@ -114,26 +114,24 @@ __device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const Co
 // [lb, le): every pass is full, so the per-pass bookkeeping reduces to two
 // running bit positions: hp, the header bit of the pass's first chunk, and base,
 // the payload bit it would have if every earlier chunk of the segment were raw.
-template <typename T, uint32_t NR>
-__device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
-                                               uint32_t le, T *o, uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
-  if (lb == kBad) return 0u;
-  const uint32_t pc = p.pc;
-  const T bitval = (T)p.bitval;
-  const uint32_t lane_bits = lane * W;
-  o += lane;
-  uint32_t hp = lb, base = lb + S;
-  for (uint32_t q = 0; q < S; q += kWave) {
+template <typename T, uint32_t NR> struct Row1 {
+  static constexpr uint32_t W = sizeof(T) * 8;
+  static constexpr uint32_t kStep = kWave;  // chunks per pass
+  uint32_t hp = 0, base = 0;
+  T *o = nullptr;
+  static T *o_type();
+  Row1() = default;
+  __device__ __forceinline__ Row1(uint32_t S, uint32_t lb, T *out, uint32_t lane)
+      : hp(lb), base(lb + S), o(out + lane) {}
+  __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
     const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
-    const uint32_t pos = base + lane_bits - __umul24(pc, count_below(H));
+    const uint32_t pos = base + lane * W - __umul24(p.pc, count_below(H));
     const T x = lds_field<T>(stg, pos);
-    o[q] = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
-    base += kWave * W - pc * popc(H);
+    o[q] = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | (T)p.bitval) : x;
+    base += kWave * W - p.pc * popc(H);
     hp += kWave;
   }
-  return base != le ? IBP_DEVERR_CORRUPT : 0u;
-}
+};
 
 // The same for W <= 32 and S a multiple of 128, two chunks per lane: lane l takes
 // chunks 2l and 2l + 1 of each 128-chunk pass and reads their two participation
@@ -144,27 +142,27 @@ __device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S,
 // the 32 bits from chunk 2l's payload, read once; the second sits 16 - pc bits up
 // when the first is compressed, and the deposit runs on the pair word with each
 // run's mask in both halves (a run never crosses a half).
-template <typename T, uint32_t NR>
-__device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
-                                                uint32_t le, T *o, uint32_t lane) {
-  constexpr uint32_t W = sizeof(T) * 8;
+template <typename T, uint32_t NR> struct Row2 {
+  static constexpr uint32_t W = sizeof(T) * 8;
   static_assert(W <= 32, "two chunks per lane up to W = 32");
+  static constexpr uint32_t kStep = 2 * kWave;
   using P = typename std::conditional<(W == 32), uint64_t, uint32_t>::type;  // a pair of chunks
-  if (lb == kBad) return 0u;
-  const uint32_t pc = p.pc;
-  const T bitval = (T)p.bitval;
-  const uint32_t lane_bits = lane * 2u * W;
-  P *op = reinterpret_cast<P *>(o) + lane;
-  uint32_t hp = lb + 2u * lane, base = lb + S;  // hp: this lane's first participation bit
-  for (uint32_t q = 0; q < S; q += 2 * kWave) {
+  uint32_t hp = 0, base = 0;  // hp: this lane's first participation bit
+  P *op = nullptr;
+  static T *o_type();
+  Row2() = default;
+  __device__ __forceinline__ Row2(uint32_t S, uint32_t lb, T *out, uint32_t lane)
+      : hp(lb + 2u * lane), base(lb + S), op(reinterpret_cast<P *>(out) + lane) {}
+  __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
+    const uint32_t pc = p.pc;
     const uint32_t b2 = lds_field<uint32_t>(stg, hp) & 3u;
     const bool h0 = (b2 & 1u) != 0u, h1 = b2 > 1u;
     const uint64_t E = ballot(h0), O = ballot(h1);
-    const uint32_t pos0 = base + lane_bits - __umul24(pc, count_below(E) + count_below(O));
+    const uint32_t pos0 = base + lane * 2u * W - __umul24(pc, count_below(E) + count_below(O));
     if constexpr (W == 16) {
       const uint32_t w = lds_field<uint32_t>(stg, pos0);
       const uint32_t x = (w & 0xFFFFu) | ((w << (h0 ? pc : 0u)) & 0xFFFF0000u);
-      uint32_t d = (uint32_t)bitval * 0x10001u;
+      uint32_t d = (uint32_t)(T)p.bitval * 0x10001u;
       if constexpr (NR == 0) {
         for (uint32_t r = 0; r < p.runs.n; ++r)
           d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
@@ -177,14 +175,31 @@ __device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S
     } else {
       const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
       const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
-      const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | bitval) : x0;
-      const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | bitval) : x1;
+      const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | (T)p.bitval) : x0;
+      const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | (T)p.bitval) : x1;
       op[q / 2] = (P)v0 | ((P)v1 << W);
     }
     base += 2u * kWave * W - pc * (popc(E) + popc(O));
     hp += 2u * kWave;
   }
-  return base != le ? IBP_DEVERR_CORRUPT : 0u;
+};
+
+template <typename T, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
+                                               uint32_t le, T *o, uint32_t lane) {
+  if (lb == kBad) return 0u;
+  Row1<T, NR> r(S, lb, o, lane);
+  for (uint32_t q = 0; q < S; q += Row1<T, NR>::kStep) r.pass(p, stg, q, lane);
+  return r.base != le ? IBP_DEVERR_CORRUPT : 0u;
+}
+
+template <typename T, uint32_t NR>
+__device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
+                                                uint32_t le, T *o, uint32_t lane) {
+  if (lb == kBad) return 0u;
+  Row2<T, NR> r(S, lb, o, lane);
+  for (uint32_t q = 0; q < S; q += Row2<T, NR>::kStep) r.pass(p, stg, q, lane);
+  return r.base != le ? IBP_DEVERR_CORRUPT : 0u;
 }
 
 // One whole segment: two chunks per lane where that applies (W <= 32, S a multiple
@@ -199,13 +214,62 @@ __device__ __forceinline__ uint32_t decode_segment(const CodecParams &p, uint32_
   return decode_row<T, NR>(p, S, stg, lb, le, o, lane);
 }
 
-// Units that are all whole segments of S chunks, S a multiple of 64.
+// K whole segments (rows) r, ..., r + K - 1 of S chunks each, S a multiple of 64,
+// whose outputs follow each other from o: their passes are interleaved, K
+// independent LDS-latency chains per step, when all are valid and take the same
+// form; otherwise one at a time.
+template <typename R, uint32_t K>
+__device__ __forceinline__ uint32_t decode_interleaved(const CodecParams &p, uint32_t S, const uint32_t *stg,
+                                                       const uint32_t (&lb)[K], const uint32_t (&le)[K],
+                                                       decltype(R::o_type()) o, uint32_t lane) {
+  R rows[K] = {};
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) rows[k] = R(S, lb[k], o + (uint64_t)k * S, lane);
+  for (uint32_t q = 0; q < S; q += R::kStep) {
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) rows[k].pass(p, stg, q, lane);
+  }
+  bool bad = false;
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) bad |= rows[k].base != le[k];
+  return bad ? IBP_DEVERR_CORRUPT : 0u;
+}
+
+template <typename T, uint32_t NR, uint32_t K>
+__device__ __forceinline__ uint32_t decode_segments(const CodecParams &p, uint32_t S, const uint32_t *stg,
+                                                    const uint32_t *lbeg, const uint32_t *lend, uint32_t r, T *o,
+                                                    uint32_t lane) {
+  uint32_t lb[K], le[K];
+  bool ok = true;
+#pragma unroll
+  for (uint32_t k = 0; k < K; ++k) {
+    lb[k] = uniform(lbeg[r + k]);
+    le[k] = uniform(lend[r + k]);
+    ok &= lb[k] != kBad;
+  }
+  if (!ok) {
+    uint32_t err = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < K; ++k) err |= decode_segment<T, NR>(p, S, stg, lb[k], le[k], o + (uint64_t)k * S, lane);
+    return err;
+  }
+  if constexpr (sizeof(T) <= 4) {
+    if (S % (2u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & (2u * sizeof(T) - 1u)) == 0u)
+      return decode_interleaved<Row2<T, NR>, K>(p, S, stg, lb, le, o, lane);
+  }
+  return decode_interleaved<Row1<T, NR>, K>(p, S, stg, lb, le, o, lane);
+}
+
+// Units that are all whole segments of S chunks, S a multiple of 64, two at a time.
 template <typename T, uint32_t NR>
 __device__ __forceinline__ uint32_t decode_rows(const DecodeArgs &a, const CodecParams &p, const uint32_t *stg,
                                                 const uint32_t *lbeg, const uint32_t *lend, uint32_t nu, T *out,
                                                 uint32_t lane) {
   uint32_t err = 0;
-  for (uint32_t r = 0; r < nu; ++r)
+  uint32_t r = 0;
+  for (; r + 1 < nu; r += 2)
+    err |= decode_segments<T, NR, 2>(p, a.S, stg, lbeg, lend, r, out + (uint64_t)r * a.S, lane);
+  if (r < nu)
     err |= decode_segment<T, NR>(p, a.S, stg, uniform(lbeg[r]), uniform(lend[r]), out + (uint64_t)r * a.S, lane);
   return err;
 }
