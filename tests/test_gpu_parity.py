@@ -186,11 +186,14 @@ def test_gather_parity(ibp, W, S, where):
     assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1), (32, 256), (16, 256)])
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1), (32, 256), (16, 256), (64, 64), (32, 64),
+                                 (16, 128)])
 def test_gather_many_ids(ibp, W, S):
     """A gather from HBM large enough that several rounds of wavefronts run (and,
-    for S >= 64, the per-row staging path); compared with the rows themselves and,
-    for a prefix, with the oracle's decode of the same stream."""
+    for S >= 64, the per-row staging path, whose rows are decoded four at a time:
+    two chunks per lane at S = 128, 256 for W <= 32, one at S = 64 and W = 64);
+    compared with the rows themselves and, for a prefix, with the oracle's decode
+    of the same stream."""
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(1000 + S + W)
     nseg = 5000
