@@ -1,13 +1,17 @@
-// ibp_decode_loops.h -- the per-pass decode loops shared by the packed-stream
-// decoder (ibp_decode.hip) and the fixed-slot decoder (ibp_slots.hip).
+// ibp_decode_loops.h -- the staging of a contiguous tile and the per-pass decode
+// loops shared by the packed-stream decoders (ibp_decode.hip, ibp_decode_pos.hip)
+// and the fixed-slot decoder (ibp_slots.hip).
 //
 // Each loop decodes the units (segments / rows) of one wavefront's tile whose
 // bits are staged in LDS: unit r occupies local bits [lbeg[r], lend[r]) (kBad =
 // skip), header first.  A lane's payload offset inside its unit is m + i*W
-// minus popcount(Mask) for every compressed chunk before it; the three loops
-// compute that prefix count for S a multiple of 64 (one broadcast 64-bit header
-// word per pass), S dividing 64 (a ballot masked to the lane's unit), or any S
-// (a ballot plus a per-unit carry kept in gseg).
+// minus popcount(Mask) for every compressed chunk before it; the loops compute
+// that prefix count for S a multiple of 64 (one broadcast 64-bit header word per
+// pass, or each lane's own two participation bits and two ballots when a lane
+// takes two chunks), S dividing 64 (a ballot masked to the lane's unit), or any S
+// (a ballot plus a per-unit carry kept in gseg).  Whole segments can be decoded
+// several at a time with their passes interleaved, which gives the scheduler
+// independent LDS-latency chains.
 #pragma once
 
 #include <type_traits>

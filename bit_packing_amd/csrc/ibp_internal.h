@@ -160,12 +160,13 @@ struct ZipArgs {
 
 constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;
 
-// Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip, ibp_slots.hip).  Each returns the hipError_t of its launch(es).
+// Launchers (ibp_meta.hip, ibp_encode.hip, ibp_decode.hip, ibp_decode_pos.hip,
+// ibp_slots.hip, ibp_zip.hip).  Each returns the hipError_t of its launch(es).
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s);
 hipError_t launch_meta_pos(const MetaArgs &a, uint32_t S, uint64_t *d_mask, uint64_t *d_bitval, hipStream_t s);
 hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs &a, const CodecParams &p, bool gather, hipStream_t s);
-hipError_t launch_decode_pos(const DecodeArgs &a, const CodecParams &p, hipStream_t s);
+hipError_t launch_decode_pos(const DecodeArgs &a, const CodecParams &p, hipStream_t s);  // ibp_decode_pos.hip
 hipError_t launch_raw_gather(const RawGatherArgs &a, hipStream_t s);
 hipError_t launch_zero(uint64_t *p, uint64_t n, hipStream_t s);
 hipError_t launch_zip_encode(const ZipArgs &a, hipStream_t s);  // ibp_zip.hip
