@@ -123,7 +123,6 @@ template <typename T, uint32_t NR> struct Row1 {
   static constexpr uint32_t kStep = kWave;  // chunks per pass
   uint32_t hp = 0, base = 0;
   T *o = nullptr;
-  static T *o_type();
   Row1() = default;
   __device__ __forceinline__ Row1(uint32_t S, uint32_t lb, T *out, uint32_t lane)
       : hp(lb), base(lb + S), o(out + lane) {}
@@ -153,7 +152,6 @@ template <typename T, uint32_t NR> struct Row2 {
   using P = typename std::conditional<(W == 32), uint64_t, uint32_t>::type;  // a pair of chunks
   uint32_t hp = 0, base = 0;  // hp: this lane's first participation bit
   P *op = nullptr;
-  static T *o_type();
   Row2() = default;
   __device__ __forceinline__ Row2(uint32_t S, uint32_t lb, T *out, uint32_t lane)
       : hp(lb + 2u * lane), base(lb + S), op(reinterpret_cast<P *>(out) + lane) {}
@@ -222,10 +220,10 @@ __device__ __forceinline__ uint32_t decode_segment(const CodecParams &p, uint32_
 // whose outputs follow each other from o: their passes are interleaved, K
 // independent LDS-latency chains per step, when all are valid and take the same
 // form; otherwise one at a time.
-template <typename R, uint32_t K>
+template <typename R, typename T, uint32_t K>
 __device__ __forceinline__ uint32_t decode_interleaved(const CodecParams &p, uint32_t S, const uint32_t *stg,
-                                                       const uint32_t (&lb)[K], const uint32_t (&le)[K],
-                                                       decltype(R::o_type()) o, uint32_t lane) {
+                                                       const uint32_t (&lb)[K], const uint32_t (&le)[K], T *o,
+                                                       uint32_t lane) {
   R rows[K] = {};
 #pragma unroll
   for (uint32_t k = 0; k < K; ++k) rows[k] = R(S, lb[k], o + (uint64_t)k * S, lane);
@@ -259,9 +257,9 @@ __device__ __forceinline__ uint32_t decode_segments(const CodecParams &p, uint32
   }
   if constexpr (sizeof(T) <= 4) {
     if (S % (2u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & (2u * sizeof(T) - 1u)) == 0u)
-      return decode_interleaved<Row2<T, NR>, K>(p, S, stg, lb, le, o, lane);
+      return decode_interleaved<Row2<T, NR>, T, K>(p, S, stg, lb, le, o, lane);
   }
-  return decode_interleaved<Row1<T, NR>, K>(p, S, stg, lb, le, o, lane);
+  return decode_interleaved<Row1<T, NR>, T, K>(p, S, stg, lb, le, o, lane);
 }
 
 // Units that are all whole segments of S chunks, S a multiple of 64, two at a time.
