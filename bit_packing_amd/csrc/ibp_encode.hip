@@ -39,10 +39,11 @@ enum : uint32_t {
 //     (decoupled look-back) to get the tile's first bit;
 //  6. write the segment offsets;
 //  7. store the image shifted to the first bit's place in its 16-byte block
-//     (interior 16-byte stores from two aligned LDS reads); the dword shared with
-//     the previous tile is written by this tile after OR-ing in the bits the
-//     previous tile handed over, and the dword shared with the next tile is
-//     handed over instead of written.
+//     (interior 16-byte stores from two aligned LDS reads); a dword shared with
+//     a neighbouring tile is written by whichever of the two tiles comes second:
+//     each ORs its bits of the dword and its flag into the boundary's hand-over
+//     word, and the one whose OR returns the other's flag writes the dword.
+//     No tile waits for a neighbour's store.
 // The per-chunk prefix count has the decoder's three forms (S a multiple of 64,
 // S dividing 64, any S).
 //
@@ -376,10 +377,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   const uint64_t excl = s_excl;
   // a tile that gave up waiting has no valid start bit: it stores nothing that
   // depends on it (its neighbours see the abort flag and give up as well)
-  if (s_failed != 0u) {
-    if (tid == 0) atomic_store_agent(&a.tails[t], kTailReady);
-    return;
-  }
+  if (s_failed != 0u) return;
 
   // 6. segment offsets
   for (uint32_t r = tid; r < nsegt; r += kThreads)
@@ -426,22 +424,16 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   }
   for (uint32_t d = e4 + tid; d < hi; d += kThreads) gdst[d] = out_dw(d);
   if (tid == 0) {
-    if (has_tail && !last) atomic_store_agent(&a.tails[t], kTailReady | out_dw(last_d));
+    // the dwords shared with the neighbours: the second of the two tiles writes
+    if (has_tail && !last) {
+      const uint32_t mine = out_dw(last_d);
+      const uint64_t old = atomic_or_agent(&a.tails[t], kTailReady | mine);
+      if (old & kHeadReady) gdst[last_d] = mine | (uint32_t)old;
+    }
     if (has_head) {
-      uint64_t prev = 0;
-      uint32_t spins = 0;
-      while (true) {
-        prev = atomic_load_agent(&a.tails[t - 1]);
-        if (prev & kTailReady) break;
-        if ((++spins & 1023u) == 0u && atomic_load_agent32(&a.control[1]) != 0u) break;
-        if (spins > (1u << 20)) {
-          atomic_store_agent32(&a.control[1], 1u);
-          if (a.err) atomicOr(a.err, IBP_DEVERR_TIMEOUT);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-      }
-      gdst[first_d] = out_dw(first_d) | (uint32_t)prev;
+      const uint32_t mine = out_dw(first_d);
+      const uint64_t old = atomic_or_agent(&a.tails[t - 1], kHeadReady | mine);
+      if (old & kTailReady) gdst[first_d] = mine | (uint32_t)old;
     }
   }
 }

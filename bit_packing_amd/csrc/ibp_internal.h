@@ -36,7 +36,10 @@ constexpr uint32_t kMetaMaxBlocks = 256;
 constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagPrefix = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
-constexpr uint64_t kTailReady = 1ull << 63;
+// Hand-over word of the boundary between tiles t and t + 1 (when it falls inside a
+// dword): each tile ORs in its bits of that dword (low 32 bits) and its flag.
+constexpr uint64_t kTailReady = 1ull << 63;  // tile t's bits are in
+constexpr uint64_t kHeadReady = 1ull << 62;  // tile t + 1's bits are in
 
 // The free (non-Mask) positions of a chunk split into maximal runs of
 // consecutive bits.  Run r sits at chunk bits [pos_r, pos_r + len_r) and at
@@ -73,7 +76,7 @@ struct EncodeArgs {
   uint32_t *stream;    // dword view of the output stream
   uint64_t *off;       // nseg + 1 bit offsets
   uint64_t *status;    // ntiles look-back words
-  uint64_t *tails;     // ntiles hand-over words (last partial dword of a tile)
+  uint64_t *tails;     // ntiles hand-over words (the dword shared by tiles t and t + 1)
   uint32_t *control;   // [0] unused, [1] abort flag
   uint32_t *err;       // optional
   const uint64_t *pmask;    // position-dependent metadata: Mask_i, i < S (device), else null
