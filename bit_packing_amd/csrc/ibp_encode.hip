@@ -299,9 +299,16 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
     const bool valid = cl < nch;
     const bool h = __builtin_amdgcn_inverse_ballot_w64(B[q]);
     auto payload = [&]() -> T {
-      if constexpr (kPos) {
-        using U = typename std::conditional<(W > 32), uint64_t, uint32_t>::type;
-        return h ? (T)extract_runs<U>((U)v[q], (U)(~mtab[ip[q]] & low_lanes(W))) : v[q];
+      if constexpr (kPos && W == 64) {
+        // in 32-bit halves: the free bits of the low half come first
+        if (!h) return v[q];
+        const uint64_t F = ~mtab[ip[q]];
+        const uint32_t Flo = (uint32_t)F, Fhi = (uint32_t)(F >> 32);
+        const uint64_t lo = extract_runs<uint32_t>((uint32_t)v[q], Flo);
+        const uint64_t hi = extract_runs<uint32_t>((uint32_t)((uint64_t)v[q] >> 32), Fhi);
+        return (T)(lo | (hi << __builtin_popcount(Flo)));
+      } else if constexpr (kPos) {
+        return h ? (T)extract_runs<uint32_t>((uint32_t)v[q], (uint32_t)(~mtab[ip[q]] & low_lanes(W))) : v[q];
       } else {
         return h ? extract_free<T, NR>(v[q], p.runs) : v[q];
       }
