@@ -297,9 +297,50 @@ __device__ __forceinline__ uint32_t pos_row2(uint32_t S, const uint4 *tab, uint3
   return base != le ? IBP_DEVERR_CORRUPT : 0u;
 }
 
+// Four chunks per lane, W = 16 and S a multiple of 256: lane l takes chunks 4l ..
+// 4l + 3 of each 256-chunk pass (one savings scan per four chunks).  The four lie
+// in the 64 bits from chunk 4l's payload bit, read once; chunk k + 1 starts 16 bits
+// after chunk k, popcount(Mask) fewer when chunk k matches.  Chunks 4l, 4l + 1 and
+// 4l + 2, 4l + 3 go through the shift steps as two pair words, stored as one
+// 64-bit word (o 8-byte aligned).
+template <bool kShift>
+__device__ __forceinline__ uint32_t pos_row4(uint32_t S, const uint4 *tab, uint32_t n, const uint32_t *stg,
+                                             uint32_t lb, uint32_t le, uint16_t *o, uint32_t lane) {
+  constexpr uint32_t W = 16;
+  if (lb == kBad) return 0u;
+  uint64_t *op = reinterpret_cast<uint64_t *>(o) + lane;
+  uint32_t hp = lb + 4u * lane, base = lb + S;
+  for (uint32_t q = 0; q < S; q += 4 * kWave) {
+    const uint32_t b4 = lds_field<uint32_t>(stg, hp);
+    const bool h0 = (b4 & 1u) != 0u, h1 = (b4 & 2u) != 0u, h2 = (b4 & 4u) != 0u, h3 = (b4 & 8u) != 0u;
+    const uint32_t j = q / 2u + 2u * lane;  // the lane's first pair of positions
+    const uint4 fa = tab[n + j], fb = tab[n + j + 1u];  // F, Bitval, popcount pairs
+    const uint32_t s0 = h0 ? (fa.z & 0xFFFFu) : 0u, s1 = h1 ? (fa.z >> 16) : 0u;
+    const uint32_t s2 = h2 ? (fb.z & 0xFFFFu) : 0u, s3 = h3 ? (fb.z >> 16) : 0u;
+    const uint32_t s = s0 + s1 + s2 + s3;
+    const uint32_t incl = wave_incl_scan(s);
+    const uint64_t w = lds_field<uint64_t>(stg, base + 4u * lane * W - (incl - s));
+    const uint32_t o1 = W - s0, o2 = o1 + W - s1, o3 = o2 + W - s2;
+    const uint32_t xa = ((uint32_t)w & 0xFFFFu) | ((uint32_t)(w >> o1) << 16);
+    const uint32_t xb = ((uint32_t)(w >> o2) & 0xFFFFu) | ((uint32_t)(w >> o3) << 16);
+    const uint32_t ya = kShift ? expand16x2(xa, tab[j], fa) : bfi(fa.x, xa, fa.y);
+    const uint32_t yb = kShift ? expand16x2(xb, tab[j + 1u], fb) : bfi(fb.x, xb, fb.y);
+    const uint32_t sa = (h0 ? 0x0000FFFFu : 0u) | (h1 ? 0xFFFF0000u : 0u);
+    const uint32_t sb = (h2 ? 0x0000FFFFu : 0u) | (h3 ? 0xFFFF0000u : 0u);
+    op[q / 4u] = (uint64_t)bfi(sa, ya, xa) | ((uint64_t)bfi(sb, yb, xb) << 32);
+    base += 4u * kWave * W - last_lane(incl);
+    hp += 4u * kWave;
+  }
+  return base != le ? IBP_DEVERR_CORRUPT : 0u;
+}
+
 template <typename T, bool kShift>
 __device__ __forceinline__ uint32_t pos_segment(uint32_t S, const uint4 *tab, uint32_t n, const uint32_t *stg,
                                                 uint32_t lb, uint32_t le, T *o, uint32_t lane) {
+  if constexpr (sizeof(T) == 2) {
+    if (S % (4u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & 7u) == 0u)
+      return pos_row4<kShift>(S, tab, n, stg, lb, le, o, lane);
+  }
   if constexpr (sizeof(T) <= 4) {
     if (S % (2u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & (2u * sizeof(T) - 1u)) == 0u)
       return pos_row2<T, kShift>(S, tab, n, stg, lb, le, o, lane);

@@ -104,8 +104,9 @@ def _data_rows(rng, n, W, masks, bitvals, S, p):
                                    (16, 64, 1_000_077), (32, 256, 1_000_077), (64, 1000, 1_000_077)])
 def test_pos_decode_many_tiles(ibp, W, S, n):
     """Large inputs (each workgroup loops over many tiles): the decode of the
-    oracle's stream equals the input, and so does a decode into an output one
-    chunk past an aligned address."""
+    oracle's stream equals the input, and so do decodes into outputs one and two
+    chunks past an 8-byte boundary (W = 16 stores four chunks per lane as one
+    word only from 8-byte aligned outputs, two from 4-byte aligned ones)."""
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(5 * W + S)
     masks, bitvals = _tables(rng, S, W)
@@ -122,9 +123,11 @@ def test_pos_decode_many_tiles(ibp, W, S, n):
     del out
     cb = W // 8
     big = torch.zeros(n * cb + 16, dtype=torch.uint8, device=dev)
-    out2 = big[cb: cb + n * cb]
-    ibp.ibp_decompress_pos(meta, s_d, o_d, n, out=out2, err=err)
-    assert torch.equal(out2, x), "decode into an unaligned output"
+    for k in (1, 2):  # one and two chunks past an 8-byte boundary (the narrower store forms)
+        out2 = big[k * cb: k * cb + n * cb]
+        out2.zero_()
+        ibp.ibp_decompress_pos(meta, s_d, o_d, n, out=out2, err=err)
+        assert torch.equal(out2, x), f"decode into an output {k} chunk(s) past alignment"
     torch.cuda.synchronize()
     assert int(err.item()) == 0
 
