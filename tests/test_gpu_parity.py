@@ -101,9 +101,10 @@ def test_compress_decompress_parity(ibp, W, S):
 @pytest.mark.parametrize("W", [16, 32])
 @pytest.mark.parametrize("S", [128, 256])
 def test_decode_into_unaligned_output(ibp, W, S):
-    """Outputs that start one chunk past an aligned address: the decoders store a
-    pair of W <= 32 chunks as one word only when the output allows it, else one
-    chunk per lane; both the contiguous decode and the HBM gather are checked."""
+    """Outputs that start one or two chunks past an 8-byte boundary: the decoders
+    store a pair of W <= 32 chunks as one word only when the output allows it, else
+    one chunk per lane; the contiguous decode (both offsets) and the HBM gather
+    (one chunk) are checked."""
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(W * 31 + S)
     cb = W // 8
@@ -116,9 +117,11 @@ def test_decode_into_unaligned_output(ibp, W, S):
             x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
             comp = ibp.ibp_compress(meta, x, S, err=err)
             big = torch.zeros(n * cb + 16, dtype=torch.uint8, device=dev)
-            out = big[cb: cb + n * cb]
-            ibp.ibp_decompress(meta, comp.stream, comp.offsets, n, S, out=out, err=err)
-            assert torch.equal(out, x), f"{name} n={n}: contiguous decode into an unaligned output"
+            for k in (1, 2):  # one and two chunks past an 8-byte boundary
+                out = big[k * cb: k * cb + n * cb]
+                out.zero_()
+                ibp.ibp_decompress(meta, comp.stream, comp.offsets, n, S, out=out, err=err)
+                assert torch.equal(out, x), f"{name} n={n}: contiguous decode {k} chunk(s) past alignment"
             ids_np = rng.integers(0, n // S, 300).astype(np.int64)
             big2 = torch.zeros(ids_np.size * S * cb + 16, dtype=torch.uint8, device=dev)
             out2 = big2[cb: cb + ids_np.size * S * cb]
