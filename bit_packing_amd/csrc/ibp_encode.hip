@@ -317,7 +317,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
       // the block lies inside one segment: everything but the lane's own count is uniform
       if constexpr (kPos) {
         // position metadata: header written here, saved-bit prefixes read from LDS
-        const uint32_t s0 = (cb / a.S) * a.S;
+        const uint32_t s0 = seg_start(cb);
         const uint32_t gs = uniform(pref[s0 >> 6]);
         const uint32_t m = min(a.S, nch - s0);
         const uint32_t segbase = s0 * (W + 1) - gs;
