@@ -95,44 +95,14 @@ template <typename T, uint32_t NR> __device__ __forceinline__ T deposit_free(T x
   return out;
 }
 
-// Bit deposit for a per-lane free-position mask F: one step per run of
-// consecutive free positions (runs differ between lanes, so the loop is per lane).
-template <typename T> __device__ __forceinline__ T deposit_var(T x, uint64_t F) {
-  uint64_t out = 0;
-  uint32_t k = 0;
-  while (F) {
-    const uint32_t lo = (uint32_t)__builtin_ctzll(F);
-    const uint64_t rest = ~(F >> lo);
-    const uint32_t len = rest ? (uint32_t)__builtin_ctzll(rest) : 64u - lo;
-    const uint64_t run = low_lanes(len);
-    out |= (((uint64_t)x >> k) & run) << lo;
-    k += len;
-    F &= ~(run << lo);
-  }
-  return (T)out;
-}
-
-// The same, one step per run with all-integer-width operations on U (uint32_t
-// for W <= 32, uint64_t for W = 64): R = F & ~(F + lowest set bit) is F's lowest
-// run of consecutive set positions.  Shift counts are masked to the width, which
-// only matters for a run covering all of U, after which F is 0 and the loop ends.
+// Bit extract for a per-lane free-position mask F (the lane's own Mask, so runs
+// differ between lanes): one step per run, with integer-width operations on U:
+// R = F & ~(F + lowest set bit) is F's lowest run of consecutive set positions.
 template <typename U> __device__ __forceinline__ uint32_t ctz_u(U v) {
   return sizeof(U) > 4 ? (uint32_t)__builtin_ctzll((uint64_t)v) : (uint32_t)__builtin_ctz((uint32_t)v);
 }
 template <typename U> __device__ __forceinline__ uint32_t popc_u(U v) {
   return sizeof(U) > 4 ? (uint32_t)__builtin_popcountll((uint64_t)v) : (uint32_t)__builtin_popcount((uint32_t)v);
-}
-
-template <typename U> __device__ __forceinline__ U deposit_runs(U x, U F) {
-  constexpr uint32_t kMask = sizeof(U) * 8 - 1;
-  U out = 0;
-  while (F) {
-    const U R = F & ~(F + (F & (U)(0 - F)));
-    out |= (x << ctz_u(F)) & R;
-    x >>= popc_u(R) & kMask;
-    F ^= R;
-  }
-  return out;
 }
 
 template <typename U> __device__ __forceinline__ U extract_runs(U v, U F) {
