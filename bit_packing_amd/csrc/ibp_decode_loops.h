@@ -136,6 +136,23 @@ template <typename T, uint32_t NR> struct Row1 {
   }
 };
 
+// Two W = 16 chunks in one word x (chunk a in bits 0-15, b in 16-31, each
+// payload from bit 0 of its half): deposit both with each run's mask in both
+// halves (a run never crosses a half), OR in Bitval, and keep the raw half of a
+// chunk that did not participate.
+template <uint32_t NR>
+__device__ __forceinline__ uint32_t merge16x2(const CodecParams &p, uint32_t x, bool ha, bool hb) {
+  uint32_t d = (uint32_t)(uint16_t)p.bitval * 0x10001u;
+  if constexpr (NR == 0) {
+    for (uint32_t r = 0; r < p.runs.n; ++r) d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
+  } else {
+#pragma unroll
+    for (uint32_t r = 0; r < NR; ++r) d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
+  }
+  const uint32_t sel = (ha ? 0x0000FFFFu : 0u) | (hb ? 0xFFFF0000u : 0u);
+  return (sel & d) | (~sel & x);
+}
+
 // The same for W <= 32 and S a multiple of 128, two chunks per lane: lane l takes
 // chunks 2l and 2l + 1 of each 128-chunk pass and reads their two participation
 // bits itself; the compressed chunks before chunk 2l are those below lane l in
@@ -157,23 +174,15 @@ template <typename T, uint32_t NR> struct Row2 {
       : hp(lb + 2u * lane), base(lb + S), op(reinterpret_cast<P *>(out) + lane) {}
   __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
     const uint32_t pc = p.pc;
-    const uint32_t b2 = lds_field<uint32_t>(stg, hp) & 3u;
-    const bool h0 = (b2 & 1u) != 0u, h1 = b2 > 1u;
-    const uint64_t E = ballot(h0), O = ballot(h1);
+    const uint32_t b2 = lds_field<uint32_t>(stg, hp);
+    // the selects below take the ballots back (one compare per bit)
+    const uint64_t E = ballot((b2 & 1u) != 0u), O = ballot((b2 & 2u) != 0u);
+    const bool h0 = __builtin_amdgcn_inverse_ballot_w64(E), h1 = __builtin_amdgcn_inverse_ballot_w64(O);
     const uint32_t pos0 = base + lane * 2u * W - __umul24(pc, count_below(E) + count_below(O));
     if constexpr (W == 16) {
       const uint32_t w = lds_field<uint32_t>(stg, pos0);
       const uint32_t x = (w & 0xFFFFu) | ((w << (h0 ? pc : 0u)) & 0xFFFF0000u);
-      uint32_t d = (uint32_t)(T)p.bitval * 0x10001u;
-      if constexpr (NR == 0) {
-        for (uint32_t r = 0; r < p.runs.n; ++r)
-          d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
-      } else {
-#pragma unroll
-        for (uint32_t r = 0; r < NR; ++r) d |= (x & ((uint32_t)p.runs.pmask[r] * 0x10001u)) << p.runs.shift[r];
-      }
-      const uint32_t sel = (h0 ? 0x0000FFFFu : 0u) | (h1 ? 0xFFFF0000u : 0u);
-      op[q / 2] = (P)((sel & d) | (~sel & x));
+      op[q / 2] = (P)merge16x2<NR>(p, x, h0, h1);
     } else {
       const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
       const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
@@ -186,34 +195,75 @@ template <typename T, uint32_t NR> struct Row2 {
   }
 };
 
-template <typename T, uint32_t NR>
-__device__ __forceinline__ uint32_t decode_row(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
+// W = 16 and S a multiple of 256, four chunks per lane: lane l takes chunks
+// 4l, ..., 4l + 3 of each 256-chunk pass and reads their four participation bits
+// itself; the compressed chunks before chunk 4l are those below lane l in the
+// four ballots (one per chunk of a lane), whose popcounts give the pass's total.
+// The four payloads lie in the 64 bits from chunk 4l's payload, read once; each
+// starts W - pc bits after a compressed predecessor and W bits after a raw one.
+// They are aligned into two pair words, merged as in Row2, and stored as one
+// 8-byte word, so o must be 8-byte aligned.  Per chunk this halves the header,
+// prefix-count and address work of Row2.
+template <typename T, uint32_t NR> struct Row4 {
+  static_assert(sizeof(T) == 2, "four chunks per lane for W = 16");
+  static constexpr uint32_t W = 16;
+  static constexpr uint32_t kStep = 4 * kWave;
+  uint32_t hp = 0, base = 0;  // hp: this lane's first participation bit
+  uint64_t *op = nullptr;
+  Row4() = default;
+  __device__ __forceinline__ Row4(uint32_t S, uint32_t lb, T *out, uint32_t lane)
+      : hp(lb + 4u * lane), base(lb + S), op(reinterpret_cast<uint64_t *>(out) + lane) {}
+  __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
+    const uint32_t pc = p.pc;
+    const uint32_t b4 = lds_field<uint32_t>(stg, hp);
+    // the selects below take the ballots back (one compare per bit)
+    const uint64_t B0 = ballot((b4 & 1u) != 0u), B1 = ballot((b4 & 2u) != 0u);
+    const uint64_t B2 = ballot((b4 & 4u) != 0u), B3 = ballot((b4 & 8u) != 0u);
+    const bool h0 = __builtin_amdgcn_inverse_ballot_w64(B0), h1 = __builtin_amdgcn_inverse_ballot_w64(B1);
+    const bool h2 = __builtin_amdgcn_inverse_ballot_w64(B2), h3 = __builtin_amdgcn_inverse_ballot_w64(B3);
+    const uint32_t below = count_below(B0) + count_below(B1) + count_below(B2) + count_below(B3);
+    const uint64_t w = lds_field<uint64_t>(stg, base + lane * 4u * W - __umul24(pc, below));
+    const uint32_t o1 = h0 ? W - pc : W, o2 = o1 + (h1 ? W - pc : W), o3 = o2 + (h2 ? W - pc : W);
+    const uint32_t xa = ((uint32_t)w & 0xFFFFu) | ((uint32_t)(w >> o1) << 16);
+    const uint32_t xb = ((uint32_t)(w >> o2) & 0xFFFFu) | ((uint32_t)(w >> o3) << 16);
+    op[q / 4] = (uint64_t)merge16x2<NR>(p, xa, h0, h1) | ((uint64_t)merge16x2<NR>(p, xb, h2, h3) << 32);
+    base += 4u * kWave * W - pc * (popc(B0) + popc(B1) + popc(B2) + popc(B3));
+    hp += 4u * kWave;
+  }
+};
+
+template <typename R, typename T>
+__device__ __forceinline__ uint32_t decode_one(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
                                                uint32_t le, T *o, uint32_t lane) {
   if (lb == kBad) return 0u;
-  Row1<T, NR> r(S, lb, o, lane);
-  for (uint32_t q = 0; q < S; q += Row1<T, NR>::kStep) r.pass(p, stg, q, lane);
+  R r(S, lb, o, lane);
+  for (uint32_t q = 0; q < S; q += R::kStep) r.pass(p, stg, q, lane);
   return r.base != le ? IBP_DEVERR_CORRUPT : 0u;
 }
 
-template <typename T, uint32_t NR>
-__device__ __forceinline__ uint32_t decode_row2(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
-                                                uint32_t le, T *o, uint32_t lane) {
-  if (lb == kBad) return 0u;
-  Row2<T, NR> r(S, lb, o, lane);
-  for (uint32_t q = 0; q < S; q += Row2<T, NR>::kStep) r.pass(p, stg, q, lane);
-  return r.base != le ? IBP_DEVERR_CORRUPT : 0u;
+// Chunks per lane for whole segments of S chunks (S a multiple of 64) stored from
+// o: four for W = 16 with S a multiple of 256, two for W <= 32 with S a multiple
+// of 128, the output aligned for the lane's word; else one.
+template <typename T>
+__device__ __forceinline__ uint32_t chunks_per_lane(uint32_t S, const T *o) {
+  const uintptr_t ad = reinterpret_cast<uintptr_t>(o);
+  if (sizeof(T) == 2 && S % (4u * kWave) == 0u && (ad & 7u) == 0u) return 4u;
+  if (sizeof(T) <= 4 && S % (2u * kWave) == 0u && (ad & (2u * sizeof(T) - 1u)) == 0u) return 2u;
+  return 1u;
 }
 
-// One whole segment: two chunks per lane where that applies (W <= 32, S a multiple
-// of 128, o aligned for the pair stores), else one.
+// One whole segment.
 template <typename T, uint32_t NR>
 __device__ __forceinline__ uint32_t decode_segment(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
                                                    uint32_t le, T *o, uint32_t lane) {
-  if constexpr (sizeof(T) <= 4) {
-    if (S % (2u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & (2u * sizeof(T) - 1u)) == 0u)
-      return decode_row2<T, NR>(p, S, stg, lb, le, o, lane);
+  const uint32_t per = chunks_per_lane(S, o);
+  if constexpr (sizeof(T) == 2) {
+    if (per == 4u) return decode_one<Row4<T, NR>, T>(p, S, stg, lb, le, o, lane);
   }
-  return decode_row<T, NR>(p, S, stg, lb, le, o, lane);
+  if constexpr (sizeof(T) <= 4) {
+    if (per == 2u) return decode_one<Row2<T, NR>, T>(p, S, stg, lb, le, o, lane);
+  }
+  return decode_one<Row1<T, NR>, T>(p, S, stg, lb, le, o, lane);
 }
 
 // K whole segments (rows) r, ..., r + K - 1 of S chunks each, S a multiple of 64,
@@ -255,9 +305,12 @@ __device__ __forceinline__ uint32_t decode_segments(const CodecParams &p, uint32
     for (uint32_t k = 0; k < K; ++k) err |= decode_segment<T, NR>(p, S, stg, lb[k], le[k], o + (uint64_t)k * S, lane);
     return err;
   }
+  const uint32_t per = chunks_per_lane(S, o);
+  if constexpr (sizeof(T) == 2) {
+    if (per == 4u) return decode_interleaved<Row4<T, NR>, T, K>(p, S, stg, lb, le, o, lane);
+  }
   if constexpr (sizeof(T) <= 4) {
-    if (S % (2u * kWave) == 0u && (reinterpret_cast<uintptr_t>(o) & (2u * sizeof(T) - 1u)) == 0u)
-      return decode_interleaved<Row2<T, NR>, T, K>(p, S, stg, lb, le, o, lane);
+    if (per == 2u) return decode_interleaved<Row2<T, NR>, T, K>(p, S, stg, lb, le, o, lane);
   }
   return decode_interleaved<Row1<T, NR>, T, K>(p, S, stg, lb, le, o, lane);
 }

@@ -102,9 +102,9 @@ def test_compress_decompress_parity(ibp, W, S):
 @pytest.mark.parametrize("S", [128, 256])
 def test_decode_into_unaligned_output(ibp, W, S):
     """Outputs that start one or two chunks past an 8-byte boundary: the decoders
-    store a pair of W <= 32 chunks as one word only when the output allows it, else
-    one chunk per lane; the contiguous decode (both offsets) and the HBM gather
-    (one chunk) are checked."""
+    store four W = 16 chunks or a pair of W <= 32 chunks as one word only when the
+    output allows it, else fewer chunks per lane; the contiguous decode (both
+    offsets) and the HBM gather (one chunk) are checked."""
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(W * 31 + S)
     cb = W // 8
@@ -161,7 +161,7 @@ def test_metadata_parity(ibp, W, T):
         assert (meta.mask, meta.bitval, meta.W) == (mask, bitval, W)
 
 
-@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (64, 1), (32, 1000), (16, 128), (16, 40)])
+@pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (64, 1), (32, 1000), (16, 128), (16, 40), (16, 512)])
 @pytest.mark.parametrize("where", ["device", "pinned"])
 def test_gather_parity(ibp, W, S, where):
     dev = torch.device("cuda:0")
@@ -194,7 +194,8 @@ def test_gather_parity(ibp, W, S, where):
 def test_gather_many_ids(ibp, W, S):
     """A gather from HBM large enough that several rounds of wavefronts run (and,
     for S >= 64, the per-row staging path, whose rows are decoded four at a time:
-    two chunks per lane at S = 128, 256 for W <= 32, one at S = 64 and W = 64);
+    four chunks per lane at W = 16 and S = 256, two at S = 128 and at W = 32 and
+    S = 256, one at S = 64);
     compared with the rows themselves and, for a prefix, with the oracle's decode
     of the same stream."""
     dev = torch.device("cuda:0")
