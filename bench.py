@@ -443,6 +443,13 @@ def main() -> int:
     torch.cuda.synchronize()
     del cal, cal2
 
+    # the counter traffic of the step kernel as a rate, beside the device copy's
+    # (how close the kernel moves its actual bytes to what a plain copy achieves)
+    if roofline["bound"] == "hbm" and roofline["traffic"]:
+        tr_gbps = roofline["traffic"] / roofline["kernel_ms"] / 1e6
+        roofline["traffic_GBps"] = tr_gbps
+        roofline["traffic_rate_vs_device_copy"] = tr_gbps / extra["device_copy_reference"]["GBps"]
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inst, meta, stream_d, off_h, S, cpu_work, args.cpu_seconds)
