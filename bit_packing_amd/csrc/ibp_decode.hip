@@ -22,8 +22,9 @@
 //  - S a multiple of 64: a pass lies inside one segment, whose 64 participation
 //    bits are one broadcast 64-bit LDS read; for W <= 32 and S a multiple of 128
 //    a lane takes two chunks of a 128-chunk pass instead (its own two
-//    participation bits, the ballots of the even and the odd chunks) and stores
-//    them as one word;
+//    participation bits, the ballots of the even and the odd chunks), and for
+//    W = 16 and S a multiple of 256 four chunks of a 256-chunk pass (four
+//    ballots), and stores them as one word;
 //  - S dividing 64: a pass holds 64/S whole segments; a ballot of the
 //    participation bits, masked to the lane's segment;
 //  - any other S: a ballot plus a per-segment carry kept in LDS.

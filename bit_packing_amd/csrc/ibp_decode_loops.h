@@ -7,8 +7,8 @@
 // skip), header first.  A lane's payload offset inside its unit is m + i*W
 // minus popcount(Mask) for every compressed chunk before it; the loops compute
 // that prefix count for S a multiple of 64 (one broadcast 64-bit header word per
-// pass, or each lane's own two participation bits and two ballots when a lane
-// takes two chunks), S dividing 64 (a ballot masked to the lane's unit), or any S
+// pass, or each lane's own participation bits and one ballot per chunk of a lane
+// when a lane takes two or four chunks), S dividing 64 (a ballot masked to the lane's unit), or any S
 // (a ballot plus a per-unit carry kept in gseg).  Whole segments can be decoded
 // several at a time with their passes interleaved, which gives the scheduler
 // independent LDS-latency chains.
