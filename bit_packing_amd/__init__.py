@@ -42,7 +42,7 @@ EXPORTS = (
     "ibp_slot_flag_words", "ibp_compress_slots", "ibp_decompress_gather_slots",
     "ibp_metadata_pos_workspace_bytes", "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos",
     "ibp_zip_table_from_sigma", "ibp_zip_blocks", "ibp_zip_codes_bytes", "ibp_zip_workspace_bytes",
-    "ibp_zip_compress", "ibp_zip_decompress",
+    "ibp_zip_compress", "ibp_zip_decompress", "ibp_set_wait_limit",
 )
 
 
@@ -128,6 +128,8 @@ def load_library() -> ctypes.CDLL:
             getattr(lib, f).restype = _u64
         lib.ibp_zip_compress.argtypes = [_vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp, _u64, _vp, _vp]
         lib.ibp_zip_decompress.argtypes = [_vp, _vp, _vp, _vp, _u64, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_set_wait_limit.argtypes = [_u32]
+        lib.ibp_set_wait_limit.restype = _u32
         for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",
                   "ibp_gather_raw", "ibp_compress_slots", "ibp_decompress_gather_slots",
                   "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos", "ibp_zip_table_from_sigma",
@@ -191,6 +193,13 @@ def ibp_metadata_workspace_bytes(n_sample_chunks: int, W: int) -> int:
 
 def ibp_compress_workspace_bytes(n_chunks: int, S: int) -> int:
     return int(load_library().ibp_compress_workspace_bytes(n_chunks, S))
+
+
+def ibp_set_wait_limit(polls: int) -> int:
+    """Tests of the compressors' give-up path only: look-back polls of one
+    unpublished predecessor before a tile gives up (0xFFFFFFFF = the default).
+    Returns the former value."""
+    return int(load_library().ibp_set_wait_limit(polls))
 
 
 # ------------------------------------------------------------------ codec

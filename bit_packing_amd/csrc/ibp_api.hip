@@ -6,6 +6,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "ibp.h"
 #include "ibp_internal.h"
 
@@ -25,6 +27,14 @@ uint32_t log2_if_pow2(uint32_t S) {
 }
 
 bool aligned(const void *p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
+
+// x * y, false when the product does not fit 64 bits
+bool mul_ok(uint64_t x, uint64_t y, uint64_t *out) { return !__builtin_mul_overflow(x, y, out); }
+
+// Look-back polls of one unpublished predecessor before a compressing tile gives
+// up (see lookback_exclusive); lowered only by tests of that path.
+constexpr uint32_t kDefaultWaitLimit = 1u << 20;
+std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
 
 // Mask/Bitval -> kernel parameters: popcount and the runs of free positions.
 bool make_params(const ibp_meta_t *m, CodecParams *p) {
@@ -108,15 +118,21 @@ const void *device_range(const void *p, uint64_t bytes, bool *is_host = nullptr)
   } else {
     return nullptr;
   }
-  hipDeviceptr_t base = nullptr;
-  size_t size = 0;
-  if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)dev) == hipSuccess) {
-    if ((uintptr_t)dev < (uintptr_t)base || (uintptr_t)dev + bytes > (uintptr_t)base + size) return nullptr;
-  } else {
-    (void)hipGetLastError();
-    if (at.type != hipMemoryTypeHost) return nullptr;
-  }
-  return dev;
+  // the allocation that holds q must also hold [q, q + bytes): 1 yes, 0 no, -1 unknown
+  auto inside = [bytes](const void *q) -> int {
+    hipDeviceptr_t base = nullptr;
+    size_t size = 0;
+    if (hipMemGetAddressRange(&base, &size, (hipDeviceptr_t)q) != hipSuccess) {
+      (void)hipGetLastError();
+      return -1;
+    }
+    const uintptr_t b = (uintptr_t)base, a = (uintptr_t)q;
+    return (a >= b && bytes <= size && a - b <= size - bytes) ? 1 : 0;
+  };
+  int in = inside(dev);
+  // pinned host memory: the range may be known under its host address instead
+  if (in < 0 && at.type == hipMemoryTypeHost) in = inside(p);
+  return in == 1 ? dev : nullptr;
 }
 
 template <typename P> bool view(P *&p, uint64_t bytes, bool *is_host = nullptr) {
@@ -139,6 +155,10 @@ IBP_API const char *ibp_status_str(int status) {
     case IBP_ERR_DEVICE: return "IBP_ERR_DEVICE";
     default: return "IBP_ERR_UNKNOWN";
   }
+}
+
+IBP_API uint32_t ibp_set_wait_limit(uint32_t polls) {
+  return g_wait_limit.exchange(polls == 0xFFFFFFFFu ? kDefaultWaitLimit : polls);
 }
 
 IBP_API uint64_t ibp_num_segments(uint64_t n_chunks, uint32_t S) {
@@ -241,6 +261,7 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W);
   a.tile_chunks = a.G * S;
   a.obuf_dw = ((127 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;  // image from the 16-byte block of the first bit
+  a.wait_limit = g_wait_limit.load();
   return status_of(launch_encode(a, p, s));
 }
 
@@ -324,6 +345,7 @@ static int decode_common(const CodecParams &p, const uint64_t *pmask, const uint
   if (gather && n_units && !d_ids) return IBP_ERR_INVALID_ARG;
   if (!aligned(stream_in, 16) || !aligned(d_out, cb) || !aligned(d_offsets, 8) || !aligned(d_ids, 8))
     return IBP_ERR_INVALID_ARG;
+  if (nseg >= (1ull << 55) / S) return IBP_ERR_SIZE;  // keeps 8 (nseg + 1) and nseg S exact
   if (!total_fits(n_chunks, p.W) || (gather && !total_fits(nseg * (uint64_t)S, p.W))) return IBP_ERR_SIZE;
   if (n_units == 0) return IBP_OK;
   bool host_stream = false;
@@ -414,10 +436,14 @@ IBP_API int ibp_decompress_gather(const ibp_meta_t *meta, const void *stream_in,
 IBP_API int ibp_gather_raw(const void *src, uint64_t row_bytes, uint64_t n_rows, const int64_t *d_ids,
                            uint64_t n_ids, void *d_out, uint32_t *d_err_word, void *hip_stream) {
   if (row_bytes == 0 || row_bytes % 16) return IBP_ERR_SIZE;
+  uint64_t src_bytes = 0, out_bytes = 0, id_bytes = 0;
+  if (!mul_ok(row_bytes, n_rows, &src_bytes) || !mul_ok(row_bytes, n_ids, &out_bytes) || !mul_ok(8, n_ids, &id_bytes))
+    return IBP_ERR_SIZE;
   if (n_ids && (!src || !d_ids || !d_out)) return IBP_ERR_INVALID_ARG;
   if (!aligned(src, 16) || !aligned(d_out, 16) || !aligned(d_ids, 8)) return IBP_ERR_INVALID_ARG;
   if (n_ids == 0) return IBP_OK;
-  if (!view(src, row_bytes * n_rows) || !view(d_ids, 8 * n_ids) || !view(d_out, row_bytes * n_ids) ||
+  if (n_rows == 0) return IBP_ERR_SIZE;  // every id would be out of range
+  if (!view(src, src_bytes) || !view(d_ids, id_bytes) || !view(d_out, out_bytes) ||
       !view(d_err_word, d_err_word ? 4 : 0))
     return IBP_ERR_INVALID_ARG;
   RawGatherArgs a;
@@ -504,7 +530,21 @@ IBP_API int ibp_decompress_gather_slots(const ibp_meta_t *meta, const void *slot
   a.row_bytes = (uint32_t)row_bytes;
   const uint32_t row_blocks = (uint32_t)(row_bytes / 16);
   a.img_dw = row_blocks * 4 + 4;
-  a.head_blocks = (S + 127) / 128 > (row_blocks < 4 ? row_blocks : 4) ? (S + 127) / 128 : (row_blocks < 4 ? row_blocks : 4);
+  // First round of loads: the blocks of the shortest compressed row (every chunk
+  // matching: S + S (W - popcount(Mask)) bits), at least its header and four
+  // blocks, rounded up to whole 128-byte lines of the slot when slots start on
+  // lines (host memory is read in 128-byte requests, so the rest of a line costs
+  // nothing).  A row longer than that takes a second round.  When most rows are
+  // near the shortest length, as on dense data, the slot is read in one round.
+  {
+    const uint32_t min_bits = S + S * (p.W - p.pc);
+    uint32_t h = (min_bits + 127) / 128;
+    const uint32_t hdr = (S + 127) / 128;
+    if (h < hdr) h = hdr;
+    if (h < 4) h = 4;
+    if (row_bytes % 128 == 0) h = (h + 7) & ~7u;
+    a.head_blocks = h < row_blocks ? h : row_blocks;
+  }
   a.wave_dw = (a.G * a.img_dw + 8 * a.G + (a.G & 1u) + 3) & ~3u;
   return status_of(launch_decode_slots(a, p, static_cast<hipStream_t>(hip_stream)));
 }
@@ -576,6 +616,7 @@ IBP_API int ibp_zip_compress(const uint8_t *table, const void *d_in, uint64_t n,
   a.n = n;
   a.nblk = nblk;
   for (int k = 0; k < 7; ++k) a.table[k] = table[k];
+  a.wait_limit = g_wait_limit.load();
   return status_of(launch_zip_encode(a, s));
 }
 

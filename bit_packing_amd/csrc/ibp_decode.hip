@@ -98,10 +98,12 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
     //    before any LDS write
     if (a.S >= kWave && a.slot_dw <= 4u * kWave && whole > 0) {
       // a row's blocks fit one 16-byte load per lane: one load instruction per row
-      // (row base address scalar), all kGatherMaxRows of them unconditional, so the
-      // compiler can wait for each row's load alone.  Lanes past a row's whole
-      // blocks, and rows past the tile, read a block that exists and write it to
-      // the 16 spare bytes after the slots.
+      // (row base address scalar).  A tile of one row (rows read over PCIe) issues
+      // that one load.  Larger tiles issue all kGatherMaxRows loads unconditionally,
+      // so the compiler can wait for each row's load alone.  Lanes past a row's
+      // whole blocks re-read the row's last whole block (the same address as a
+      // neighbouring lane, so no extra request); rows past the tile read block 0
+      // of the stream.  Both write into the 16 spare bytes after the slots.
       static_assert(kGatherMaxRows == 8, "one named register per row");
       const uint32_t spare = a.G * a.slot_dw;
       auto fetch = [&](uint32_t r) -> uint4 {
@@ -115,6 +117,20 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
         const uint32_t n_r = (uint32_t)__builtin_amdgcn_readlane((int)my_whole, (int)r);
         *reinterpret_cast<uint4 *>(stg + (lane < n_r ? r * a.slot_dw + 4u * lane : spare)) = t;
       };
+      if (a.G == 1) {
+        // one row per wavefront (rows read over PCIe): one load, no other row
+        const uint4 t0 = fetch(0);
+        put(0, t0);
+        if constexpr (kMode == kModeLargeS) {
+          if (!ballot(tail_row)) {
+            wave_lds_sync();
+            err |= decode_segment<T, NR>(p, a.S, stg, uniform(lbeg[0]), uniform(lend[0]),
+                                         static_cast<T *>(a.out) + chunk0, lane);
+            if (err && a.err) atomicOr(a.err, err);
+            return;
+          }
+        }
+      } else {
       const uint4 t0 = fetch(0), t1 = fetch(1), t2 = fetch(2), t3 = fetch(3);
       const uint4 t4 = fetch(4), t5 = fetch(5), t6 = fetch(6), t7 = fetch(7);
       if constexpr (kMode == kModeLargeS) {
@@ -152,6 +168,7 @@ __global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParam
       put(5, t5);
       put(6, t6);
       put(7, t7);
+      }
     } else if (a.S >= kWave) {
       // four loads in flight per lane before any LDS write
       // one load instruction per (row, 64 blocks): the row's base address is scalar

@@ -237,9 +237,14 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
 // in increasing order, so the lowest unfinished tile always has a slot (every
 // earlier workgroup of its XCD has finished) and the wait chain makes progress.
 // (A single atomic ticket counter would also order them, but it serialises all
-// workgroups on one address, at about 12 ns each.)  Bounded: after ~2^20 polls,
-// or once another tile has aborted (control[1] != 0), it sets control[1] and
-// IBP_DEVERR_TIMEOUT and returns with timed_out set (the value is then invalid).
+// workgroups on one address, at about 12 ns each.)
+// Bounded: a tile gives up after wait_limit polls of an unpublished predecessor,
+// or at a poll that finds the abort flag control[1] set by another tile.  The
+// first tile to give up sets control[1] and IBP_DEVERR_TIMEOUT.  A tile that gives
+// up returns with timed_out set and publishes no prefix, so no successor takes a
+// start bit from it: successors walk past its aggregate to the same unpublished
+// predecessor, and either find it published later (their prefixes are then
+// right) or give up too.
 // Publish tile t's aggregate agg (tile 0: its inclusive prefix) before its
 // look-back, as early as possible: one thread.
 __device__ inline void lookback_publish(uint64_t *status, uint64_t t, uint64_t agg) {
@@ -247,7 +252,7 @@ __device__ inline void lookback_publish(uint64_t *status, uint64_t t, uint64_t a
 }
 
 __device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
-                                              uint64_t agg, uint32_t lane, bool &timed_out) {
+                                              uint64_t agg, uint32_t wait_limit, uint32_t lane, bool &timed_out) {
   uint64_t excl = 0;
   timed_out = false;
   if (t == 0) return 0;
@@ -261,19 +266,21 @@ __device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *contro
     const uint64_t zm = ballot(flag == 0);
     const uint32_t first_p = pm ? (uint32_t)__builtin_ctzll(pm) : 64u;
     const uint64_t needed = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
-    if ((zm & needed) && !timed_out) {
-      // bounded wait: give up when another tile has aborted or after ~2^20 polls
-      bool give_up = false;
-      if ((++spins & 1023u) == 0u) give_up = atomic_load_agent32(&control[1]) != 0u;
-      if (spins > (1u << 20)) {
-        give_up = true;
-        if (lane == 0) {
-          atomic_store_agent32(&control[1], 1u);
-          if (err) atomicOr(err, IBP_DEVERR_TIMEOUT);
-        }
+    if (zm & needed) {
+      // an unpublished predecessor: wait for it, within the bound
+      ++spins;
+      const bool over = spins > wait_limit;
+      bool give_up = over;
+      if (!over && (spins & 1023u) == 0u) give_up = atomic_load_agent32(&control[1]) != 0u;
+      if (over && lane == 0) {
+        atomic_store_agent32(&control[1], 1u);
+        if (err) atomicOr(err, IBP_DEVERR_TIMEOUT);
       }
-      timed_out = ballot(give_up) != 0;
-      if (!timed_out) __builtin_amdgcn_s_sleep(1);
+      if (ballot(give_up)) {
+        timed_out = true;
+        return 0;
+      }
+      __builtin_amdgcn_s_sleep(1);
       continue;
     }
     excl += wave_sum64(lane <= first_p ? (s & kValueMask) : 0ull);

@@ -374,7 +374,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   // 5. the tile's start bit: decoupled look-back over the predecessors
   if (wave == 0) {
     bool timed_out = false;
-    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, t, agg, lane, timed_out);
+    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, t, agg, a.wait_limit, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
       s_failed = timed_out ? 1u : 0u;
@@ -382,9 +382,14 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   }
   __syncthreads();
   const uint64_t excl = s_excl;
-  // a tile that gave up waiting has no valid start bit: it stores nothing that
-  // depends on it (its neighbours see the abort flag and give up as well)
-  if (s_failed != 0u) return;
+  // a tile that gave up waiting has no valid start bit: it stores no stream bits,
+  // and its offsets become ~0, which no decoder accepts (the segments' bit ranges
+  // fail their checks), so the stream is refused even without an error word
+  if (s_failed != 0u) {
+    for (uint32_t r = tid; r < nsegt; r += kThreads) a.off[k0 + r] = ~0ull;
+    if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = ~0ull;
+    return;
+  }
 
   // 6. segment offsets
   for (uint32_t r = tid; r < nsegt; r += kThreads)

@@ -90,6 +90,7 @@ struct EncodeArgs {
   uint32_t tile_chunks;
   uint32_t obuf_dw;    // LDS dwords for the packed tile
   uint32_t pair;       // 1: W = 16 chunk pairs (one Mask, S a multiple of 64, input 4-byte aligned)
+  uint32_t wait_limit; // look-back polls of one unpublished predecessor before a tile gives up
 };
 
 struct DecodeArgs {
@@ -159,6 +160,7 @@ struct ZipArgs {
   uint64_t n;
   uint64_t nblk;
   uint32_t table[7];   // exponents of codes 1..7, distinct
+  uint32_t wait_limit; // compress: look-back polls of one unpublished predecessor before giving up
 };
 
 constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;

@@ -163,14 +163,22 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   }
   if (wave == 0) {
     bool timed_out = false;
-    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, g, wtot, lane, timed_out);
+    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, g, wtot, a.wait_limit, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
       s_failed = timed_out ? 1u : 0u;
     }
   }
   __syncthreads();
-  if (s_failed != 0u) return;  // no valid escape offset: nothing more is stored
+  if (s_failed != 0u) {
+    // no valid escape offset: no escapes are stored, and the blocks' offsets become
+    // ~0, which the decoder refuses
+    if (tid == 0) {
+      for (uint32_t b = 0; b < nbw; ++b) a.eoff[j0 + b] = ~0ull;
+      if (j0 + nbw == a.nblk) a.eoff[a.nblk] = ~0ull;
+    }
+    return;
+  }
   const uint64_t base = s_excl;
   if (tid == 0) {
     uint64_t o = base;

@@ -74,7 +74,9 @@ typedef enum {
 #define IBP_DEVERR_CORRUPT 1u   /* a segment's decoded length differs from its offset span,
                                    or its offsets are not monotone / exceed the stream */
 #define IBP_DEVERR_BAD_ID 2u    /* a gather id is negative or >= n_segments; its row is skipped */
-#define IBP_DEVERR_TIMEOUT 4u   /* compression: a wait on a neighbouring tile timed out */
+#define IBP_DEVERR_TIMEOUT 4u   /* compression: a tile gave up waiting for a predecessor's offset;
+                                   its stream bits are not written and its offsets are set to
+                                   ~0, which every decoder refuses (IBP_DEVERR_CORRUPT) */
 
 /* Largest segment length (chunks per segment). */
 #define IBP_MAX_S 1024u
@@ -90,6 +92,14 @@ typedef struct {
 
 /* Human-readable name of a status code (static string). */
 IBP_API const char *ibp_status_str(int status);
+
+/* For tests of the compressors' give-up path only.  A compressing tile waits for
+ * its predecessors' offsets (decoupled look-back); it gives up after `polls` polls
+ * of one unpublished predecessor (default 2^20; 0xFFFFFFFF restores the default)
+ * and reports IBP_DEVERR_TIMEOUT.  0 makes every tile that would wait give up at
+ * once, so the give-up path runs without any kernel waiting.  Applies to calls
+ * made after it, process-wide; returns the former value. */
+IBP_API uint32_t ibp_set_wait_limit(uint32_t polls);
 
 /* ceil(n_chunks / S); 0 when S == 0. */
 IBP_API uint64_t ibp_num_segments(uint64_t n_chunks, uint32_t S);
@@ -171,7 +181,8 @@ IBP_API int ibp_decompress_gather(const ibp_meta_t *meta, const void *stream_in,
  * transfer that IBP replaces (the page's "Risultati" compare against it).
  * Row j of d_out = row d_ids[j] of a table of n_rows rows of row_bytes bytes at
  * src (pinned host memory or device memory, aligned to 16); row_bytes % 16 == 0.
- * Out-of-range ids leave the row untouched and set IBP_DEVERR_BAD_ID.
+ * Out-of-range ids leave the row untouched and set IBP_DEVERR_BAD_ID.  n_rows == 0
+ * with n_ids > 0, or a byte count beyond 64 bits, is IBP_ERR_SIZE.
  */
 IBP_API int ibp_gather_raw(const void *src, uint64_t row_bytes, uint64_t n_rows, const int64_t *d_ids,
                            uint64_t n_ids, void *d_out, uint32_t *d_err_word, void *hip_stream);
@@ -202,8 +213,11 @@ IBP_API int ibp_compress_slots(const ibp_meta_t *meta, const void *d_in, uint64_
 
 /* Row j of d_out = row d_ids[j] of a slot table of n_rows rows (slots in pinned
  * host memory, read zero-copy, or device memory).  Only the used part of a
- * compressed slot is read: its header first, then the rest.  Out-of-range ids
- * leave the row untouched and set IBP_DEVERR_BAD_ID.  Asynchronous. */
+ * compressed slot is read: a first round reads as much as the shortest
+ * compressed row can use (its header included), in whole 128-byte lines when
+ * row_bytes is a multiple of 128; a longer row's rest follows in a second round.
+ * Out-of-range ids leave the row untouched and set IBP_DEVERR_BAD_ID.
+ * Asynchronous. */
 IBP_API int ibp_decompress_gather_slots(const ibp_meta_t *meta, const void *slots, uint64_t slots_bytes,
                                         uint64_t n_rows, uint32_t S, const uint64_t *d_flags,
                                         const int64_t *d_ids, uint64_t n_ids, void *d_out,

@@ -97,6 +97,12 @@ def _load():
     return _lib
 
 
+def lib() -> ctypes.CDLL:
+    """The loaded oracle library (for callers that run its C functions from several
+    threads at once; ctypes releases the GIL during each call)."""
+    return _load()
+
+
 def _ptr(a: np.ndarray | None):
     if a is None:
         return None

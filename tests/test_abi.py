@@ -147,3 +147,35 @@ def test_zip_table_matches_oracle(ibp):
     assert lib.ibp_zip_workspace_bytes(4096) == 16
     t = (ctypes.c_uint8 * 7)(1, 2, 3, 4, 5, 6, 6)  # repeated exponent
     assert lib.ibp_zip_compress(t, FAKE, 16, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 64, None, None) == ibp.IBP_ERR_INVALID_ARG
+
+
+def test_byte_counts_that_overflow_are_refused(ibp):
+    """Products of counts that do not fit 64 bits are refused with IBP_ERR_SIZE on the
+    host, before any pointer is resolved (so fake pointers are never looked at)."""
+    lib = ibp.load_library()
+    m = _meta(ibp)
+    # gather: 8 (n_segments + 1) and n_segments * S would wrap
+    for nseg in (1 << 61, (1 << 64) - 1, (1 << 55) // 128):
+        assert lib.ibp_decompress_gather(ctypes.byref(m), FAKE, 4096, FAKE, nseg, 128, FAKE, 4, FAKE, None,
+                                         None) == ibp.IBP_ERR_SIZE, nseg
+    # raw gather: row_bytes * n_rows, row_bytes * n_ids and 8 n_ids would wrap
+    assert lib.ibp_gather_raw(FAKE, 16, 1 << 61, FAKE, 4, FAKE, None, None) == ibp.IBP_ERR_SIZE
+    assert lib.ibp_gather_raw(FAKE, 1 << 40, 1 << 30, FAKE, 4, FAKE, None, None) == ibp.IBP_ERR_SIZE
+    assert lib.ibp_gather_raw(FAKE, 16, 4, FAKE, 1 << 61, FAKE, None, None) == ibp.IBP_ERR_SIZE
+    assert lib.ibp_gather_raw(FAKE, 16, 0, FAKE, 4, FAKE, None, None) == ibp.IBP_ERR_SIZE  # no rows to gather from
+    # slots: row and id counts are bounded before any product
+    assert lib.ibp_decompress_gather_slots(ctypes.byref(m), FAKE, 1 << 62, 1 << 61, 128, FAKE, FAKE, 4, FAKE, None,
+                                           None) == ibp.IBP_ERR_SIZE
+    assert lib.ibp_compress_slots(ctypes.byref(m), FAKE, 1 << 61, 128, FAKE, 1 << 62, FAKE, None, None) \
+        == ibp.IBP_ERR_SIZE
+
+
+def test_wait_limit_setter(ibp):
+    """The test-only look-back bound: set, read back, restore the default."""
+    lib = ibp.load_library()
+    first = ibp.ibp_set_wait_limit(5)
+    assert ibp.ibp_set_wait_limit(0) == 5
+    assert ibp.ibp_set_wait_limit(0xFFFFFFFF) == 0
+    assert ibp.ibp_set_wait_limit(0xFFFFFFFF) == 1 << 20
+    assert first == 1 << 20
+    assert lib.ibp_set_wait_limit(0xFFFFFFFF) == 1 << 20

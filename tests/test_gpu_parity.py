@@ -427,3 +427,73 @@ def test_graph_replay(ibp):
             assert np.array_equal(r.cpu().numpy(), ref), f"replay {rep}: gather {k}"
         assert torch.equal(other, x)
     assert int(err.item()) == 0
+
+
+def test_lookback_give_up_path(ibp):
+    """The compressors' bounded wait, forced from the host: with a wait limit of 0 a
+    tile that finds an unpublished predecessor gives up at once (no kernel waits).
+    A call then either produced the exact stream (no tile had to wait) or reports
+    IBP_DEVERR_TIMEOUT, left ~0 in the offsets of the tiles that gave up, and every
+    decoder refuses the result.  The default limit is restored afterwards and the
+    next compression is exact."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(77)
+    W, S, mask, bitval = 32, 128, 0xC0000000, 0
+    v = _data(rng, 2_000_000, W, mask, bitval, 0.97)
+    meta = ibp.make_meta(W, mask, bitval)
+    x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    nb = (int(ref_off[-1]) + 7) // 8
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    gave_up = 0
+    try:
+        ibp.ibp_set_wait_limit(0)
+        for it in range(4):
+            say(f"give-up path: IBP compression, wait limit 0, call {it}")
+            err.zero_()
+            comp = ibp.ibp_compress(meta, x, S, err=err)
+            torch.cuda.synchronize()
+            e = int(err.item())
+            off = comp.offsets.cpu().numpy()
+            if e == 0:
+                assert np.array_equal(off.view(np.uint64), ref_off)
+                assert np.array_equal(comp.stream[:nb].cpu().numpy(), ref_stream)
+                continue
+            gave_up += 1
+            assert e == ibp.IBP_DEVERR_TIMEOUT, e
+            assert (off == -1).any(), "a tile that gave up leaves ~0 offsets"
+            err.zero_()
+            ibp.ibp_decompress(meta, comp.stream, comp.offsets, v.size, S, err=err)
+            torch.cuda.synchronize()
+            assert int(err.item()) & ibp.IBP_DEVERR_CORRUPT
+        # the comparison codec's look-back, on a BF16 tensor of several blocks
+        bf = rng.integers(0, 1 << 16, size=1_000_000, dtype=np.uint64).astype(np.uint16)
+        xb = torch.from_numpy(bf.view(np.uint8).copy()).to(dev)
+        table = ibp.ibp_zip_table_from_sigma(1e-3)
+        for it in range(2):
+            say(f"give-up path: exponent codec, wait limit 0, call {it}")
+            err.zero_()
+            z = ibp.ibp_zip_compress(table, xb, err=err)
+            torch.cuda.synchronize()
+            e = int(err.item())
+            if e == 0:
+                out = ibp.ibp_zip_decompress(z, err=err)
+                torch.cuda.synchronize()
+                assert torch.equal(out.view(torch.uint8), xb) and int(err.item()) == 0
+                continue
+            gave_up += 1
+            assert e == ibp.IBP_DEVERR_TIMEOUT, e
+            assert (z.eoff.cpu().numpy() == -1).any()
+            err.zero_()
+            ibp.ibp_zip_decompress(z, err=err)
+            torch.cuda.synchronize()
+            assert int(err.item()) & ibp.IBP_DEVERR_CORRUPT
+    finally:
+        ibp.ibp_set_wait_limit(0xFFFFFFFF)
+    say(f"give-up path: {gave_up} of 6 calls gave up; default limit restored")
+    err.zero_()
+    comp = ibp.ibp_compress(meta, x, S, err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off)
+    assert np.array_equal(comp.stream[:nb].cpu().numpy(), ref_stream)
