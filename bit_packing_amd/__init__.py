@@ -34,6 +34,7 @@ LIB_PATH = os.path.join(_HERE, "libibp.so")
 IBP_OK, IBP_ERR_INVALID_ARG, IBP_ERR_SIZE, IBP_ERR_CAPACITY, IBP_ERR_DEVICE = 0, 1, 2, 3, 4
 IBP_DEVERR_CORRUPT, IBP_DEVERR_BAD_ID, IBP_DEVERR_TIMEOUT = 1, 2, 4
 IBP_MAX_S = 1024
+IBP_NOALLOC_SCRATCH_BYTES = 8 << 20  # device array behind ibp_compress_noalloc, per GPU
 
 EXPORTS = (
     "ibp_status_str", "ibp_num_segments", "ibp_max_stream_bytes", "ibp_stream_bytes",
@@ -42,7 +43,7 @@ EXPORTS = (
     "ibp_slot_flag_words", "ibp_compress_slots", "ibp_decompress_gather_slots",
     "ibp_metadata_pos_workspace_bytes", "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos",
     "ibp_zip_table_from_sigma", "ibp_zip_blocks", "ibp_zip_codes_bytes", "ibp_zip_workspace_bytes",
-    "ibp_zip_compress", "ibp_zip_decompress", "ibp_set_wait_limit",
+    "ibp_zip_compress", "ibp_zip_decompress", "ibp_set_wait_limit", "ibp_compress_noalloc",
 )
 
 
@@ -128,6 +129,8 @@ def load_library() -> ctypes.CDLL:
             getattr(lib, f).restype = _u64
         lib.ibp_zip_compress.argtypes = [_vp, _vp, _u64, _vp, _vp, _vp, _u64, _vp, _vp, _u64, _vp, _vp]
         lib.ibp_zip_decompress.argtypes = [_vp, _vp, _vp, _vp, _u64, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_compress_noalloc.argtypes = [_metap, _vp, _u64, _u32, _vp, _u64, _vp, _vp, _vp]
+        lib.ibp_compress_noalloc.restype = _int
         lib.ibp_set_wait_limit.argtypes = [_u32]
         lib.ibp_set_wait_limit.restype = _u32
         for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",

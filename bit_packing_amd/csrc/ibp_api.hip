@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "ibp.h"
 #include "ibp_internal.h"
@@ -142,6 +143,35 @@ template <typename P> bool view(P *&p, uint64_t bytes, bool *is_host = nullptr) 
   return true;
 }
 
+// Workspace of ibp_compress_noalloc, for callers that cannot allocate: a file-scope
+// device array (each GPU the library runs on holds its own copy until the process
+// ends), shared by every such call on that GPU.  Its device address on each GPU is
+// resolved once, with that GPU current, by hipGetSymbolAddress; host code uses only
+// that address (the array's name is not a device address in host code).
+constexpr uint64_t kScratchBytes = IBP_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+void *scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -220,10 +250,12 @@ IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, 
   return IBP_OK;
 }
 
+// ws_is_scratch: d_workspace is this library's own device array (ibp_compress_noalloc),
+// known to be device memory of kScratchBytes bytes; it is not looked up.
 static int compress_common(const CodecParams &p, const uint64_t *pmask, const uint64_t *pbitval, const void *d_in,
                            uint64_t n_bytes, uint32_t S, void *d_stream, uint64_t stream_capacity,
                            uint64_t *d_offsets, void *d_workspace, uint64_t workspace_bytes, uint32_t *d_err_word,
-                           void *hip_stream) {
+                           void *hip_stream, bool ws_is_scratch = false) {
   if (S == 0 || S > IBP_MAX_S || !d_offsets) return IBP_ERR_INVALID_ARG;
   const uint32_t cb = p.W / 8;
   if (n_bytes % cb) return IBP_ERR_SIZE;
@@ -236,7 +268,8 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   if (workspace_bytes < ibp_compress_workspace_bytes(n, S)) return IBP_ERR_CAPACITY;
   const uint64_t nseg = (n + S - 1) / S;
   if (!view(d_in, n_bytes) || !view(d_stream, ibp_max_stream_bytes(n, p.W)) || !view(d_offsets, 8 * (nseg + 1)) ||
-      !view(d_workspace, n ? ibp_compress_workspace_bytes(n, S) : 0) || !view(d_err_word, d_err_word ? 4 : 0))
+      (!ws_is_scratch && !view(d_workspace, n ? ibp_compress_workspace_bytes(n, S) : 0)) ||
+      !view(d_err_word, d_err_word ? 4 : 0))
     return IBP_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   if (n == 0) return status_of(launch_zero(d_offsets, 1, s));  // offset table = {0}
@@ -273,6 +306,25 @@ IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_by
   if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
   return compress_common(p, nullptr, nullptr, d_in, n_bytes, S, d_stream, stream_capacity, d_offsets, d_workspace,
                          workspace_bytes, d_err_word, hip_stream);
+}
+
+IBP_API int ibp_compress_noalloc(const ibp_meta_t *meta, const void *d_in, uint64_t n_bytes, uint32_t S,
+                                 void *d_stream, uint64_t stream_capacity, uint64_t *d_offsets,
+                                 uint32_t *d_err_word, void *hip_stream) {
+  CodecParams p;
+  if (!make_params(meta, &p)) return IBP_ERR_INVALID_ARG;
+  if (S == 0 || S > IBP_MAX_S) return IBP_ERR_INVALID_ARG;
+  const uint32_t cb = p.W / 8;
+  if (n_bytes % cb) return IBP_ERR_SIZE;
+  if (!total_fits(n_bytes / cb, p.W)) return IBP_ERR_SIZE;
+  if (ibp_compress_workspace_bytes(n_bytes / cb, S) > kScratchBytes) return IBP_ERR_CAPACITY;
+  void *ws = nullptr;
+  if (n_bytes) {
+    ws = scratch_of_current_device();
+    if (!ws) return IBP_ERR_DEVICE;
+  }
+  return compress_common(p, nullptr, nullptr, d_in, n_bytes, S, d_stream, stream_capacity, d_offsets, ws,
+                         kScratchBytes, d_err_word, hip_stream, true);
 }
 
 // Position-dependent metadata: W/S checks, device tables of S words each.

@@ -150,6 +150,28 @@ IBP_API int ibp_compress(const ibp_meta_t *meta, const void *d_in, uint64_t n_by
                          void *hip_stream);
 
 /*
+ * Step 2 for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): ibp_compress with
+ * the workspace taken from a fixed array inside the library instead of an argument.
+ * The array is IBP_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from the
+ * library's first such call on that GPU until the process ends; the call itself
+ * allocates nothing.  Inputs up to IBP_NOALLOC_SCRATCH_BYTES of compression
+ * workspace (ibp_compress_workspace_bytes(n, S) <= the limit: about 2 * 10^9 chunks
+ * at S = 256) are accepted; larger ones return IBP_ERR_CAPACITY before any launch.
+ *   Uses the GPU that is current on the calling thread; hip_stream must belong to it.
+ *   Every call on one GPU shares that GPU's array: calls that overlap in time on one
+ *   GPU (other streams, other threads) race and may corrupt each other's output;
+ *   calls on one stream are ordered and safe.  The array is cleared by a kernel at
+ *   the start of each call, so no state carries from one call to the next.
+ *   Other arguments, outputs and errors as ibp_compress; IBP_ERR_DEVICE also when the
+ *   array's address cannot be resolved.
+ */
+#define IBP_NOALLOC_SCRATCH_BYTES (8ull << 20)
+IBP_API int ibp_compress_noalloc(const ibp_meta_t *meta, const void *d_in, uint64_t n_bytes, uint32_t S,
+                                 void *d_stream, uint64_t stream_capacity, uint64_t *d_offsets,
+                                 uint32_t *d_err_word, void *hip_stream);
+
+/*
  * Step 3 -- decompression, device-resident ("Algoritmo Core", Decompressione).
  *   stream_in: compressed stream (device, or pinned host memory), aligned to 16,
  *     readable for stream_bytes bytes.

@@ -179,3 +179,24 @@ def test_wait_limit_setter(ibp):
     assert ibp.ibp_set_wait_limit(0xFFFFFFFF) == 1 << 20
     assert first == 1 << 20
     assert lib.ibp_set_wait_limit(0xFFFFFFFF) == 1 << 20
+
+
+def test_noalloc_limit_and_refusal(ibp):
+    """The header's limit of the no-alloc compression equals the binding's, and an
+    input whose workspace exceeds it is refused on the host (IBP_ERR_CAPACITY) before
+    any pointer is looked at."""
+    text = open(HEADER).read()
+    m = re.search(r"#define IBP_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == ibp.IBP_NOALLOC_SCRATCH_BYTES
+    lib = ibp.load_library()
+    meta = _meta(ibp, W=64, mask=0xFF00)
+    n = 1
+    while ibp.ibp_compress_workspace_bytes(n, 1) <= ibp.IBP_NOALLOC_SCRATCH_BYTES:
+        n *= 2
+    rc = lib.ibp_compress_noalloc(ctypes.byref(meta), FAKE, n * 8, 1, FAKE, ibp.ibp_max_stream_bytes(n, 64), FAKE,
+                                  None, None)
+    assert rc == ibp.IBP_ERR_CAPACITY
+    assert lib.ibp_compress_noalloc(ctypes.byref(meta), FAKE, 4096, 0, FAKE, 1 << 20, FAKE, None, None) \
+        == ibp.IBP_ERR_INVALID_ARG
+    assert lib.ibp_compress_noalloc(ctypes.byref(meta), FAKE, 4095, 256, FAKE, 1 << 20, FAKE, None, None) \
+        == ibp.IBP_ERR_SIZE
