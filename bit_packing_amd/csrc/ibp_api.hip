@@ -33,7 +33,7 @@ bool aligned(const void *p, uint64_t a) { return ((uintptr_t)p % a) == 0; }
 bool mul_ok(uint64_t x, uint64_t y, uint64_t *out) { return !__builtin_mul_overflow(x, y, out); }
 
 // Look-back polls of one unpublished predecessor before a compressing tile gives
-// up (see lookback_exclusive); lowered only by tests of that path.
+// up (see lookback_finish); lowered only by tests of that path.
 constexpr uint32_t kDefaultWaitLimit = 1u << 20;
 std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
 

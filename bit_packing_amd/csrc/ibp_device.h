@@ -9,6 +9,10 @@
 namespace ibp {
 namespace dev {
 
+// s_waitcnt immediate (gfx9 encoding) that waits for all vector memory operations
+// and nothing else: vmcnt 0 (bits 3:0 and 15:14), expcnt 7 (6:4), lgkmcnt 15 (11:8).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // ------------------------------------------------------------------ wave helpers
 
 __device__ __forceinline__ uint32_t lane_id() { return threadIdx.x & (kWave - 1); }
@@ -229,44 +233,73 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
 }
 
 // Decoupled look-back (Merrill & Garland, "Single-pass Parallel Prefix Scan with
-// Decoupled Look-back", 2016), run by one wavefront for tile t whose aggregate
-// agg (< 2^62) lookback_publish has already published: it walks back over the
-// predecessors' status words 64 at a time until one holds an inclusive prefix,
-// publishes its own inclusive prefix and returns the exclusive one.  Tile t is workgroup t: the
-// dispatcher hands workgroups to the XCDs round-robin and starts each XCD's share
-// in increasing order, so the lowest unfinished tile always has a slot (every
-// earlier workgroup of its XCD has finished) and the wait chain makes progress.
-// (A single atomic ticket counter would also order them, but it serialises all
-// workgroups on one address, at about 12 ns each.)
-// Bounded: a tile gives up after wait_limit polls of an unpublished predecessor,
-// or at a poll that finds the abort flag control[1] set by another tile.  The
-// first tile to give up sets control[1] and IBP_DEVERR_TIMEOUT.  A tile that gives
-// up returns with timed_out set and publishes no prefix, so no successor takes a
-// start bit from it: successors walk past its aggregate to the same unpublished
-// predecessor, and either find it published later (their prefixes are then
-// right) or give up too.
-// Publish tile t's aggregate agg (tile 0: its inclusive prefix) before its
-// look-back, as early as possible: one thread.
+// Decoupled Look-back", 2016).  Tile t publishes its aggregate agg (< 2^62) as soon
+// as it knows it (lookback_publish), then finds its exclusive prefix by walking back
+// over its predecessors' status words until one holds an inclusive prefix, adding
+// the aggregates in between, and publishes its own inclusive prefix.  Here the walk
+// reads 64 predecessors per wavefront and step; a tile's first windows are read by
+// several wavefronts at once right after it publishes (lookback_read), so that their
+// latency overlaps the packing, and are summed by lookback_combine; lookback_finish
+// continues, one window per step, when they are not enough.  With hundreds of tiles
+// in flight the nearest inclusive prefix is often more than 64 tiles back, so one
+// window per step would take several round trips to memory.
+// Tile t is workgroup t: the dispatcher hands workgroups to the XCDs round-robin and
+// starts each XCD's share in increasing order, so the lowest unfinished tile always
+// has a slot (every earlier workgroup of its XCD has finished) and the wait chain
+// makes progress.  (A single atomic ticket counter would also order them, but it
+// serialises all workgroups on one address, at about 12 ns each.)
+// Bounded (lookback_finish): a tile gives up after wait_limit polls of an
+// unpublished predecessor, or at a poll that finds the abort flag control[1] set by
+// another tile.  A tile that gives up sets control[1] and IBP_DEVERR_TIMEOUT, returns
+// with timed_out set and publishes no prefix, so no successor takes a start bit from
+// it: successors walk past its aggregate to the same unpublished predecessor, and
+// either find it published later (their prefixes are then right) or give up too.
+// lookback_publish: tile t's aggregate agg (tile 0: its inclusive prefix); one thread.
 __device__ inline void lookback_publish(uint64_t *status, uint64_t t, uint64_t agg) {
   atomic_store_agent(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
 }
 
-__device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
-                                              uint64_t agg, uint32_t wait_limit, uint32_t lane, bool &timed_out) {
-  uint64_t excl = 0;
+// The status word of predecessor t - 1 - 64 w - lane: window w of the look-back
+// (w = 0 is the nearest).  Before the first tile every word reads as an inclusive
+// prefix of 0.
+__device__ inline uint64_t lookback_read(const uint64_t *status, uint64_t t, uint32_t w, uint32_t lane) {
+  const int64_t j = (int64_t)t - 1 - 64 * (int64_t)w - (int64_t)lane;
+  return j >= 0 ? atomic_load_agent(&status[j]) : kFlagPrefix;
+}
+
+// Summary of one window of 64 status words s (lane 0 the nearest predecessor):
+//   kLbWait:   an unpublished predecessor lies before the window's first inclusive
+//              prefix (the window must be read again later);
+//   kLbPrefix: an inclusive prefix, with every nearer predecessor's aggregate
+//              published: sum = that prefix plus those aggregates;
+//   kLbAggs:   no prefix, every aggregate published: sum = their total.
+enum : uint32_t { kLbWait = 0, kLbPrefix = 1, kLbAggs = 2 };
+__device__ inline uint32_t lookback_window(uint64_t s, uint32_t lane, uint64_t &sum) {
+  const uint64_t flag = s & ~kValueMask;
+  const uint64_t pm = ballot(flag == kFlagPrefix);
+  const uint64_t zm = ballot(flag == 0);
+  const uint32_t first_p = pm ? (uint32_t)__builtin_ctzll(pm) : 64u;
+  const uint64_t needed = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
+  sum = wave_sum64(lane <= first_p ? (s & kValueMask) : 0ull);
+  return (zm & needed) ? kLbWait : (first_p < 64 ? kLbPrefix : kLbAggs);
+}
+
+// The rest of tile t's look-back, run by one wavefront: excl holds the sum of the
+// windows before `base` (the nearest predecessor not yet accounted for); it walks
+// back from base 64 at a time until an inclusive prefix, waiting (bounded) for
+// unpublished predecessors, then publishes tile t's inclusive prefix and returns
+// the exclusive one.
+__device__ inline uint64_t lookback_finish(uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
+                                           int64_t base, uint64_t excl, uint64_t agg, uint32_t wait_limit,
+                                           uint32_t lane, bool &timed_out) {
   timed_out = false;
-  if (t == 0) return 0;
-  int64_t base = (int64_t)t - 1;
   uint32_t spins = 0;
-  while (true) {
+  while (base >= 0) {
     const int64_t j = base - (int64_t)lane;
     const uint64_t s = j >= 0 ? atomic_load_agent(&status[j]) : kFlagPrefix;
-    const uint64_t flag = s & ~kValueMask;
-    const uint64_t pm = ballot(flag == kFlagPrefix);
-    const uint64_t zm = ballot(flag == 0);
-    const uint32_t first_p = pm ? (uint32_t)__builtin_ctzll(pm) : 64u;
-    const uint64_t needed = first_p >= 63 ? ~0ull : ((2ull << first_p) - 1ull);
-    if (zm & needed) {
+    uint64_t sum;
+    const uint32_t st = lookback_window(s, lane, sum);
+    if (st == kLbWait) {
       // an unpublished predecessor: wait for it, within the bound
       ++spins;
       const bool over = spins > wait_limit;
@@ -283,12 +316,37 @@ __device__ inline uint64_t lookback_exclusive(uint64_t *status, uint32_t *contro
       __builtin_amdgcn_s_sleep(1);
       continue;
     }
-    excl += wave_sum64(lane <= first_p ? (s & kValueMask) : 0ull);
-    if (first_p < 64) break;
+    excl += sum;
+    if (st == kLbPrefix) break;
     base -= 64;
   }
   if (lane == 0) atomic_store_agent(&status[t], kFlagPrefix | ((excl + agg) & kValueMask));
   return excl;
+}
+
+// Tile t's look-back from the summaries of its first nwin windows (window w read by
+// wavefront w right after the tile published its aggregate, so those reads' latency
+// overlaps the tile's other work): the windows are taken nearest first until one
+// holds an inclusive prefix; one that must wait, or running out of windows, hands
+// over to lookback_finish.  Run by one wavefront; returns the exclusive prefix.
+__device__ inline uint64_t lookback_combine(const uint32_t *win_state, const uint64_t *win_sum, uint32_t nwin,
+                                            uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
+                                            uint64_t agg, uint32_t wait_limit, uint32_t lane, bool &timed_out) {
+  timed_out = false;
+  if (t == 0) return 0;
+  uint64_t excl = 0;
+  int64_t base = (int64_t)t - 1;
+  for (uint32_t w = 0; w < nwin; ++w) {
+    const uint32_t st = win_state[w];
+    if (st == kLbWait) break;
+    excl += win_sum[w];
+    if (st == kLbPrefix) {
+      if (lane == 0) atomic_store_agent(&status[t], kFlagPrefix | ((excl + agg) & kValueMask));
+      return excl;
+    }
+    base -= 64;
+  }
+  return lookback_finish(status, control, err, t, base, excl, agg, wait_limit, lane, timed_out);
 }
 
 }  // namespace dev

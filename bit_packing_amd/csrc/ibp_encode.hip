@@ -25,7 +25,7 @@ enum : uint32_t {
 
 // One workgroup per tile of G consecutive segments (about 16 chunks per thread,
 // 32 in the W = 16 pair form).
-//  1. tile t = workgroup index (see lookback_exclusive for why the order holds);
+//  1. tile t = workgroup index (see the look-back in ibp_device.h for why the order holds);
 //  2. load the chunks (16 per thread, 64 consecutive per wavefront per pass),
 //     test the invariant bits and ballot the participation bits; clear the LDS
 //     image while the loads are in flight;
@@ -81,6 +81,7 @@ template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false
 __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 1)
     encode_kernel(EncodeArgs a, CodecParams p) {
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
+  static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = enc_threads(kPos, W);
   constexpr uint32_t kWaves = kThreads / kWave;
@@ -199,6 +200,12 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
       if (lane == 0) bal[q * kWaves + wave] = B[q];
     }
   }
+  // Every input load has been consumed.  An explicit wait for all vector memory
+  // operations here (none is outstanding) lets the compiler know it: otherwise,
+  // where the full-tile and tail-tile load paths join, it places a vmcnt(0) wait in
+  // the packing loop, which would also wait for the publish store and the early
+  // look-back read issued after this point.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
   // 3. compressed chunks before each 64-chunk block
   if (wave == 0) {
@@ -374,7 +381,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   // 5. the tile's start bit: decoupled look-back over the predecessors
   if (wave == 0) {
     bool timed_out = false;
-    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, t, agg, a.wait_limit, lane, timed_out);
+    const uint64_t excl = t == 0 ? 0ull
+                                 : lookback_finish(a.status, a.control, a.err, t, (int64_t)t - 1, 0, agg,
+                                                   a.wait_limit, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
       s_failed = timed_out ? 1u : 0u;
@@ -414,6 +423,20 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   const uint32_t lo = first_d + (has_head ? 1u : 0u);
   const uint32_t hi = last_d + 1u - ((has_tail && !last) ? 1u : 0u);  // [lo, hi) stored directly
   uint32_t *gdst = a.stream + ((excl >> 7) << 2);
+  // the dwords shared with the neighbours: the second of the two tiles writes.  The
+  // two hand-over atomics go first, from two wavefronts, so that their round trips
+  // overlap the interior stores; their results are used after those.
+  const bool hand_tail = has_tail && !last, hand_head = has_head;
+  uint32_t mine_tail = 0, mine_head = 0;
+  uint64_t old_tail = 0, old_head = 0;
+  if (tid == 0 && hand_tail) {
+    mine_tail = out_dw(last_d);
+    old_tail = atomic_or_agent(&a.tails[t], kTailReady | mine_tail);
+  }
+  if (tid == kWave && hand_head) {
+    mine_head = out_dw(first_d);
+    old_head = atomic_or_agent(&a.tails[t - 1], kHeadReady | mine_head);
+  }
   const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
   for (uint32_t d = lo + tid; d < a4; d += kThreads) gdst[d] = out_dw(d);
   // interior: output dwords [d, d + 4) are image bits from 32 d - sh0 on, i.e. from
@@ -435,19 +458,8 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
     *reinterpret_cast<uint4 *>(gdst + d) = o;
   }
   for (uint32_t d = e4 + tid; d < hi; d += kThreads) gdst[d] = out_dw(d);
-  if (tid == 0) {
-    // the dwords shared with the neighbours: the second of the two tiles writes
-    if (has_tail && !last) {
-      const uint32_t mine = out_dw(last_d);
-      const uint64_t old = atomic_or_agent(&a.tails[t], kTailReady | mine);
-      if (old & kHeadReady) gdst[last_d] = mine | (uint32_t)old;
-    }
-    if (has_head) {
-      const uint32_t mine = out_dw(first_d);
-      const uint64_t old = atomic_or_agent(&a.tails[t - 1], kHeadReady | mine);
-      if (old & kTailReady) gdst[first_d] = mine | (uint32_t)old;
-    }
-  }
+  if (tid == 0 && hand_tail && (old_tail & kHeadReady)) gdst[last_d] = mine_tail | (uint32_t)old_tail;
+  if (tid == kWave && hand_head && (old_head & kTailReady)) gdst[first_d] = mine_head | (uint32_t)old_head;
 }
 
 __global__ void __launch_bounds__(kBlock) zero_kernel(uint64_t *p, uint64_t n) {

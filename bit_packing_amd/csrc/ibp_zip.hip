@@ -163,7 +163,9 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   }
   if (wave == 0) {
     bool timed_out = false;
-    const uint64_t excl = lookback_exclusive(a.status, a.control, a.err, g, wtot, a.wait_limit, lane, timed_out);
+    const uint64_t excl = g == 0 ? 0ull
+                                 : lookback_finish(a.status, a.control, a.err, g, (int64_t)g - 1, 0, wtot,
+                                                   a.wait_limit, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
       s_failed = timed_out ? 1u : 0u;

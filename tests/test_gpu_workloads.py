@@ -177,3 +177,60 @@ def test_workload_variants_full_size(name):
         assert torch.equal(back.view(torch.uint8), x), "ZipCCL round trip"
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+
+
+@pytest.mark.parametrize("name", ["gnn", "llm"])
+def test_compression_repeats_after_other_kernels(name):
+    """The compressed stream does not depend on what ran before it: one full-size
+    compression (single Mask and position metadata), then other codec kernels on the
+    same GPU (decompression, gathers, fixed slots, the other compressor), then the
+    same compression again; both results are compared byte for byte."""
+    import bit_packing_amd as ibp
+
+    dev = torch.device("cuda:0")
+    say(f"repeat {name}: generating")
+    inst = workloads.generate(name)
+    w = inst.w
+    W, T, S = w.W, w.T, w.S
+    x = torch.from_numpy(inst.data.reshape(-1).view(np.uint8)).to(dev)
+    sample = torch.from_numpy(inst.sample.reshape(-1).view(np.uint8)).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    meta, _ = ibp.ibp_build_metadata(sample, W, T)
+    nrs = inst.sample.nbytes // (S * W // 8)
+    pmeta, _ = ibp.ibp_build_metadata_pos(sample[: nrs * S * W // 8], W, S, T, counts=False)
+
+    def both():
+        a = ibp.ibp_compress(meta, x, S, err=err)
+        b = ibp.ibp_compress_pos(pmeta, x, err=err)
+        torch.cuda.synchronize()
+        out = []
+        for c in (a, b):
+            nb = (int(c.offsets[-1].item()) + 7) // 8
+            out.append((c.offsets.cpu().numpy(), c.stream[:nb].cpu().numpy()))
+        return out, a
+
+    say(f"repeat {name}: first compression")
+    first, comp = both()
+    say(f"repeat {name}: other kernels")
+    out = ibp.ibp_decompress(meta, comp.stream, comp.offsets, comp.n_chunks, S, err=err)
+    assert torch.equal(out, x)
+    del out
+    if w.gather:
+        ids = torch.from_numpy(workloads.gather_ids(name, inst.data.shape[0], 1)[0]).to(dev)
+        ibp.ibp_decompress_gather(meta, comp.stream, comp.offsets, S, ids, err=err)
+        slots, flags = ibp.ibp_compress_slots(meta, x, S, err=err)
+        ibp.ibp_decompress_gather_slots(meta, slots, flags, S, ids, err=err)
+        del slots, flags
+    else:
+        z = ibp.ibp_zip_compress(ibp.ibp_zip_table_from_sigma(w.sigma), x, err=err)
+        ibp.ibp_zip_decompress(z, err=err)
+        del z
+    torch.cuda.synchronize()
+    del comp
+    say(f"repeat {name}: second compression")
+    second, _ = both()
+    assert int(err.item()) == 0
+    for (o1, s1), (o2, s2), kind in zip(first, second, ("single Mask", "position metadata")):
+        assert np.array_equal(o1, o2), f"{kind}: offsets differ between the two compressions"
+        d = np.nonzero(s1 != s2)[0]
+        assert d.size == 0, f"{kind}: {d.size} stream bytes differ, first at {d[:4]}"
