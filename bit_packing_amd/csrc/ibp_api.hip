@@ -293,7 +293,10 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   a.s_log2 = log2_if_pow2(S);
   a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W);
   a.tile_chunks = a.G * S;
-  a.obuf_dw = ((127 + a.tile_chunks * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;  // image from the 16-byte block of the first bit
+  a.halves = enc_halves(pmask != nullptr, a.pair != 0u, p.W, S);
+  if (a.halves == 2 && a.tile_chunks != enc_tile_chunks(false, false, p.W)) a.halves = 1;  // whole tiles only
+  // image (one half's when halves == 2) from the 16-byte block of the first bit
+  a.obuf_dw = ((127 + a.tile_chunks / a.halves * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;
   a.wait_limit = g_wait_limit.load();
   return status_of(launch_encode(a, p, s));
 }

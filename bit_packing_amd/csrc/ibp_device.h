@@ -236,13 +236,8 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
 // Decoupled Look-back", 2016).  Tile t publishes its aggregate agg (< 2^62) as soon
 // as it knows it (lookback_publish), then finds its exclusive prefix by walking back
 // over its predecessors' status words until one holds an inclusive prefix, adding
-// the aggregates in between, and publishes its own inclusive prefix.  Here the walk
-// reads 64 predecessors per wavefront and step; a tile's first windows are read by
-// several wavefronts at once right after it publishes (lookback_read), so that their
-// latency overlaps the packing, and are summed by lookback_combine; lookback_finish
-// continues, one window per step, when they are not enough.  With hundreds of tiles
-// in flight the nearest inclusive prefix is often more than 64 tiles back, so one
-// window per step would take several round trips to memory.
+// the aggregates in between, and publishes its own inclusive prefix; the walk
+// (lookback_finish) reads 64 predecessors per step, one per lane of a wavefront.
 // Tile t is workgroup t: the dispatcher hands workgroups to the XCDs round-robin and
 // starts each XCD's share in increasing order, so the lowest unfinished tile always
 // has a slot (every earlier workgroup of its XCD has finished) and the wait chain
@@ -257,14 +252,6 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
 // lookback_publish: tile t's aggregate agg (tile 0: its inclusive prefix); one thread.
 __device__ inline void lookback_publish(uint64_t *status, uint64_t t, uint64_t agg) {
   atomic_store_agent(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
-}
-
-// The status word of predecessor t - 1 - 64 w - lane: window w of the look-back
-// (w = 0 is the nearest).  Before the first tile every word reads as an inclusive
-// prefix of 0.
-__device__ inline uint64_t lookback_read(const uint64_t *status, uint64_t t, uint32_t w, uint32_t lane) {
-  const int64_t j = (int64_t)t - 1 - 64 * (int64_t)w - (int64_t)lane;
-  return j >= 0 ? atomic_load_agent(&status[j]) : kFlagPrefix;
 }
 
 // Summary of one window of 64 status words s (lane 0 the nearest predecessor):
@@ -322,31 +309,6 @@ __device__ inline uint64_t lookback_finish(uint64_t *status, uint32_t *control, 
   }
   if (lane == 0) atomic_store_agent(&status[t], kFlagPrefix | ((excl + agg) & kValueMask));
   return excl;
-}
-
-// Tile t's look-back from the summaries of its first nwin windows (window w read by
-// wavefront w right after the tile published its aggregate, so those reads' latency
-// overlaps the tile's other work): the windows are taken nearest first until one
-// holds an inclusive prefix; one that must wait, or running out of windows, hands
-// over to lookback_finish.  Run by one wavefront; returns the exclusive prefix.
-__device__ inline uint64_t lookback_combine(const uint32_t *win_state, const uint64_t *win_sum, uint32_t nwin,
-                                            uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
-                                            uint64_t agg, uint32_t wait_limit, uint32_t lane, bool &timed_out) {
-  timed_out = false;
-  if (t == 0) return 0;
-  uint64_t excl = 0;
-  int64_t base = (int64_t)t - 1;
-  for (uint32_t w = 0; w < nwin; ++w) {
-    const uint32_t st = win_state[w];
-    if (st == kLbWait) break;
-    excl += win_sum[w];
-    if (st == kLbPrefix) {
-      if (lane == 0) atomic_store_agent(&status[t], kFlagPrefix | ((excl + agg) & kValueMask));
-      return excl;
-    }
-    base -= 64;
-  }
-  return lookback_finish(status, control, err, t, base, excl, agg, wait_limit, lane, timed_out);
 }
 
 }  // namespace dev

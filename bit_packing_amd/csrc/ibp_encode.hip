@@ -9,6 +9,7 @@
 // look-back over its predecessors (Merrill & Garland, "Single-pass Parallel
 // Prefix Scan with Decoupled Look-back", 2016), and packs the tile in LDS.
 #include <type_traits>
+#include <utility>
 
 #include "ibp_device.h"
 
@@ -77,11 +78,12 @@ __device__ __forceinline__ uint64_t interleave32(uint32_t e, uint32_t o) {
 
 // The pair form asks for 8 wavefronts per SIMD (its 16 unrolled passes otherwise
 // take enough scalar registers to allow only 7: 1.28 -> 1.11 ms per 2^30 chunks).
-template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false>
+template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false, uint32_t kHalves = 1>
 __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 1)
     encode_kernel(EncodeArgs a, CodecParams p) {
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
+  static_assert(kHalves == 1 || (!kPos && !kPair && kMode != kModeGeneral), "halves: one Mask, S a power of two");
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = enc_threads(kPos, W);
   constexpr uint32_t kWaves = kThreads / kWave;
@@ -102,6 +104,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   uint16_t *wpre = reinterpret_cast<uint16_t *>(btab + (kPos ? a.S : 0u));
   __shared__ uint64_t s_excl;
   __shared__ uint32_t s_failed;
+  __shared__ uint32_t s_carry;  // kHalves: the first half's bits of the dword both halves share
 
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = uniform(tid / kWave);
   const uint64_t t = blockIdx.x;  // grid == ntiles
@@ -297,8 +300,13 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
       lds_or_bits(obuf, c < nch ? pos : 0u, c < nch ? field : 0u);  // lanes past the tile hold 0
     }
   }
+  // the passes of half h of the tile (kHalves == 2: the tile's two halves of
+  // kTile / 2 chunks are packed and stored one after the other through an image of
+  // half the size, whose bit 0 is the half's first bit, tile image bit H)
+  auto pack = [&](auto hc, uint32_t H) {
+  constexpr uint32_t qb = decltype(hc)::value * (kQ / kHalves), qe = qb + kQ / kHalves;
 #pragma unroll
-  for (uint32_t q = 0; q < (kPair ? 0u : kQ); ++q) {
+  for (uint32_t q = qb; q < (kPair ? 0u : qe); ++q) {
     const uint32_t blk = q * kWaves + wave;  // this wavefront's 64-chunk block
     const uint32_t cb = blk * kWave;                 // its first tile chunk
     if (cb >= nch) continue;                         // uniform
@@ -335,7 +343,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
         const uint32_t s0 = seg_start(cb);
         const uint32_t m = min(a.S, nch - s0);
         const uint32_t saved = __umul24(pc, pref_at(blk) + count_below(B[q]));
-        const uint32_t pos = (s0 + m + cb * W) + lane_bits - saved;
+        const uint32_t pos = (s0 + m + cb * W) + lane_bits - saved - H;
         lds_or_bits(obuf, valid ? pos : 0u, payload());  // invalid lanes hold 0
       }
     } else if constexpr (kMode == kModeSmallS) {
@@ -349,8 +357,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
         if (valid) lds_or_field(obuf, segbase + m + i_lane * W - (c_cl - gs), payload());
       } else {
         const uint32_t gs = pc * (pref_at(blk) + popc(B[q] & seg_below));
-        if (valid && i_lane == 0) lds_or_bits(obuf, s0 * (W + 1) - gs, (uint32_t)((B[q] >> lane) & low_lanes(m)));
-        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(blk) + count_below(B[q]));
+        if (valid && i_lane == 0)
+          lds_or_bits(obuf, s0 * (W + 1) - gs - H, (uint32_t)((B[q] >> lane) & low_lanes(m)));
+        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(blk) + count_below(B[q])) - H;
         lds_or_bits(obuf, valid ? pos : 0u, payload());
       }
     } else {
@@ -370,12 +379,14 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
     // the headers: lane q of each wavefront ORs in block q * kWaves + wave's
     // 64 participation bits
     const uint32_t blk = lane * kWaves + wave, cb = blk * kWave;
-    if (lane < kQ && cb < nch) {
+    if (lane >= qb && lane < qe && cb < nch) {
       const uint32_t s0 = seg_start(cb);
       const uint64_t hdr = kPair ? interleave32((uint32_t)bal[blk], (uint32_t)(bal[blk] >> 32)) : bal[blk];
-      lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6], hdr);
+      lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6] - H, hdr);
     }
   }
+  };
+  pack(std::integral_constant<uint32_t, 0>{}, 0u);
   __syncthreads();
 
   // 5. the tile's start bit: decoupled look-back over the predecessors
@@ -405,61 +416,88 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
     a.off[k0 + r] = excl + (uint64_t)r * a.S * (W + 1) - (uint64_t)cost(r * a.S);
   if (t == a.ntiles - 1 && tid == 0) a.off[a.nseg] = excl + agg;
 
-  // 7. store.  Output dword d is stream dword (excl >> 7) * 4 + d, so interior
-  //    stores are 16-byte aligned; image bit j is output bit sh0 + j, sh0 = excl & 127.
-  const uint32_t sh0 = (uint32_t)(excl & 127u);
-  const uint32_t dq = sh0 >> 5, sh = sh0 & 31u;
-  const uint32_t img_end = (uint32_t)((agg + 31) >> 5);  // image dwords holding tile bits
-  auto img = [&](int32_t i) -> uint32_t { return (i >= 0 && (uint32_t)i < img_end) ? obuf[i] : 0u; };
-  auto out_dw = [&](uint32_t d) -> uint32_t {
-    const int32_t i = (int32_t)d - (int32_t)dq;
-    return sh ? (img(i) << sh) | (img(i - 1) >> (32u - sh)) : img(i);
-  };
+  // 7. store image bits [0, nbits) at stream bit s_bit.  Output dword d is stream
+  //    dword (s_bit >> 7) * 4 + d, so interior stores are 16-byte aligned; image bit
+  //    j is output bit sh0 + j, sh0 = s_bit & 127.  The dword holding the first bit,
+  //    when shared, is shared with the previous tile (hand-over word) or, head_in_tile,
+  //    with the previous half of this tile, whose bits of it are `carry`: this half
+  //    writes it.  The dword holding the last bit, when shared, is shared with the
+  //    next tile (hand-over word) or, tail_in_tile, with the next half: its bits go to
+  //    s_carry and the next half writes it.
   const bool last = t == a.ntiles - 1;
-  const uint32_t first_d = dq;                                // dword holding the first bit
-  const uint32_t last_d = (uint32_t)((sh0 + agg - 1) >> 5);   // dword holding the last bit
-  const bool has_head = sh != 0u;
-  const bool has_tail = ((sh0 + agg) & 31u) != 0u;
-  const uint32_t lo = first_d + (has_head ? 1u : 0u);
-  const uint32_t hi = last_d + 1u - ((has_tail && !last) ? 1u : 0u);  // [lo, hi) stored directly
-  uint32_t *gdst = a.stream + ((excl >> 7) << 2);
-  // the dwords shared with the neighbours: the second of the two tiles writes.  The
-  // two hand-over atomics go first, from two wavefronts, so that their round trips
-  // overlap the interior stores; their results are used after those.
-  const bool hand_tail = has_tail && !last, hand_head = has_head;
-  uint32_t mine_tail = 0, mine_head = 0;
-  uint64_t old_tail = 0, old_head = 0;
-  if (tid == 0 && hand_tail) {
-    mine_tail = out_dw(last_d);
-    old_tail = atomic_or_agent(&a.tails[t], kTailReady | mine_tail);
-  }
-  if (tid == kWave && hand_head) {
-    mine_head = out_dw(first_d);
-    old_head = atomic_or_agent(&a.tails[t - 1], kHeadReady | mine_head);
-  }
-  const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
-  for (uint32_t d = lo + tid; d < a4; d += kThreads) gdst[d] = out_dw(d);
-  // interior: output dwords [d, d + 4) are image bits from 32 d - sh0 on, i.e. from
-  // bit t = 128 - sh0 of the eight image dwords [d - 4, d + 4) (two aligned 16-byte
-  // LDS reads; the image is zero past its last bit and a4 >= 4 unless sh0 == 0)
-  const uint32_t t_sh = 128u - sh0, jt = t_sh >> 5, st = t_sh & 31u;
-  auto al = [&](uint32_t hi, uint32_t lo) -> uint32_t { return __builtin_amdgcn_alignbit(hi, lo, st); };
-  for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kThreads) {
-    const uint4 A = *reinterpret_cast<const uint4 *>(obuf + ((max(d, 4u) - 4u) & ~3u));
-    const uint4 C = *reinterpret_cast<const uint4 *>(obuf + d);
-    uint4 o;
-    switch (jt) {  // uniform
-      case 0: o = make_uint4(al(A.y, A.x), al(A.z, A.y), al(A.w, A.z), al(C.x, A.w)); break;
-      case 1: o = make_uint4(al(A.z, A.y), al(A.w, A.z), al(C.x, A.w), al(C.y, C.x)); break;
-      case 2: o = make_uint4(al(A.w, A.z), al(C.x, A.w), al(C.y, C.x), al(C.z, C.y)); break;
-      case 3: o = make_uint4(al(C.x, A.w), al(C.y, C.x), al(C.z, C.y), al(C.w, C.z)); break;
-      default: o = C; break;  // sh0 == 0
+  auto store = [&](uint64_t s_bit, uint64_t nbits, bool head_in_tile, bool tail_in_tile, uint32_t carry) {
+    const uint32_t sh0 = (uint32_t)(s_bit & 127u);
+    const uint32_t dq = sh0 >> 5, sh = sh0 & 31u;
+    const uint32_t img_end = (uint32_t)((nbits + 31) >> 5);  // image dwords holding the bits
+    auto img = [&](int32_t i) -> uint32_t { return (i >= 0 && (uint32_t)i < img_end) ? obuf[i] : 0u; };
+    auto out_dw = [&](uint32_t d) -> uint32_t {
+      const int32_t i = (int32_t)d - (int32_t)dq;
+      return sh ? (img(i) << sh) | (img(i - 1) >> (32u - sh)) : img(i);
+    };
+    const uint32_t first_d = dq;                                 // dword holding the first bit
+    const uint32_t last_d = (uint32_t)((sh0 + nbits - 1) >> 5);  // dword holding the last bit
+    const bool has_head = sh != 0u;
+    const bool has_tail = ((sh0 + nbits) & 31u) != 0u;
+    const bool hand_head = has_head && !head_in_tile, hand_tail = has_tail && !tail_in_tile && !last;
+    const bool keep_tail = has_tail && tail_in_tile;
+    const uint32_t lo = first_d + (has_head ? 1u : 0u);
+    const uint32_t hi = last_d + 1u - ((hand_tail || keep_tail) ? 1u : 0u);  // [lo, hi) stored directly
+    uint32_t *gdst = a.stream + ((s_bit >> 7) << 2);
+    // the hand-over atomics go first, from two wavefronts, so that their round trips
+    // overlap the interior stores; their results are used after those
+    uint32_t mine_tail = 0, mine_head = 0;
+    uint64_t old_tail = 0, old_head = 0;
+    if (tid == 0 && hand_tail) {
+      mine_tail = out_dw(last_d);
+      old_tail = atomic_or_agent(&a.tails[t], kTailReady | mine_tail);
     }
-    *reinterpret_cast<uint4 *>(gdst + d) = o;
+    if (tid == kWave && hand_head) {
+      mine_head = out_dw(first_d);
+      old_head = atomic_or_agent(&a.tails[t - 1], kHeadReady | mine_head);
+    }
+    if (tid == 0 && keep_tail) s_carry = out_dw(last_d);
+    if (tid == 0 && has_head && head_in_tile) gdst[first_d] = out_dw(first_d) | carry;
+    const uint32_t a4 = min((lo + 3u) & ~3u, hi), e4 = max(hi & ~3u, a4);
+    for (uint32_t d = lo + tid; d < a4; d += kThreads) gdst[d] = out_dw(d);
+    // interior: output dwords [d, d + 4) are image bits from 32 d - sh0 on, i.e. from
+    // bit t = 128 - sh0 of the eight image dwords [d - 4, d + 4) (two aligned 16-byte
+    // LDS reads; the image is zero past its last bit and a4 >= 4 unless sh0 == 0)
+    const uint32_t t_sh = 128u - sh0, jt = t_sh >> 5, st = t_sh & 31u;
+    auto al = [&](uint32_t hi, uint32_t lo) -> uint32_t { return __builtin_amdgcn_alignbit(hi, lo, st); };
+    for (uint32_t d = a4 + 4 * tid; d < e4; d += 4 * kThreads) {
+      const uint4 A = *reinterpret_cast<const uint4 *>(obuf + ((max(d, 4u) - 4u) & ~3u));
+      const uint4 C = *reinterpret_cast<const uint4 *>(obuf + d);
+      uint4 o;
+      switch (jt) {  // uniform
+        case 0: o = make_uint4(al(A.y, A.x), al(A.z, A.y), al(A.w, A.z), al(C.x, A.w)); break;
+        case 1: o = make_uint4(al(A.z, A.y), al(A.w, A.z), al(C.x, A.w), al(C.y, C.x)); break;
+        case 2: o = make_uint4(al(A.w, A.z), al(C.x, A.w), al(C.y, C.x), al(C.z, C.y)); break;
+        case 3: o = make_uint4(al(C.x, A.w), al(C.y, C.x), al(C.z, C.y), al(C.w, C.z)); break;
+        default: o = C; break;  // sh0 == 0
+      }
+      *reinterpret_cast<uint4 *>(gdst + d) = o;
+    }
+    for (uint32_t d = e4 + tid; d < hi; d += kThreads) gdst[d] = out_dw(d);
+    if (tid == 0 && hand_tail && (old_tail & kHeadReady)) gdst[last_d] = mine_tail | (uint32_t)old_tail;
+    if (tid == kWave && hand_head && (old_head & kTailReady)) gdst[first_d] = mine_head | (uint32_t)old_head;
+  };
+  if constexpr (kHalves == 1) {
+    store(excl, agg, false, false, 0u);
+  } else {
+    // the first half's size: its segments end at chunk kTile / 2
+    const bool two = nch > kTile / 2;
+    const uint64_t agg0 = two ? (uint64_t)(kTile / 2) * (W + 1) - (uint64_t)pc * pref[kBal / 2] : agg;
+    store(excl, agg0, false, two, 0u);
+    if (two) {
+      __syncthreads();  // the first half's image has been read
+      for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kThreads)
+        *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+      pack(std::integral_constant<uint32_t, 1>{}, (uint32_t)agg0);
+      __syncthreads();
+      store(excl + agg0, agg - agg0, true, false, s_carry);
+    }
   }
-  for (uint32_t d = e4 + tid; d < hi; d += kThreads) gdst[d] = out_dw(d);
-  if (tid == 0 && hand_tail && (old_tail & kHeadReady)) gdst[last_d] = mine_tail | (uint32_t)old_tail;
-  if (tid == kWave && hand_head && (old_head & kTailReady)) gdst[first_d] = mine_head | (uint32_t)old_head;
 }
 
 __global__ void __launch_bounds__(kBlock) zero_kernel(uint64_t *p, uint64_t n) {
@@ -473,6 +511,13 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
+  if constexpr (sizeof(T) == 8 && !kPos && !kPair && M != kModeGeneral) {
+    if (a.halves == 2) {
+      hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2>), dim3((uint32_t)a.ntiles),
+                         dim3(enc_threads(false, 64)), shmem, s, a, p);
+      return hipGetLastError();
+    }
+  }
   hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos, kPair>), dim3((uint32_t)a.ntiles),
                      dim3(enc_threads(kPos, sizeof(T) * 8)), shmem, s, a, p);
   return hipGetLastError();

@@ -24,6 +24,13 @@ constexpr uint32_t enc_threads(bool pos, uint32_t W) { return pos && W != 16 ? 2
 constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W) {
   return (pair ? 32u : 16u) * enc_threads(pos, W);
 }
+// A compression tile of 64-bit chunks with one Mask and S a power of two is packed
+// and stored in two halves of kTile / 2 chunks (segments end at the middle) through
+// an LDS image of half the size: the full-size image (8192 chunks x 65 bits) leaves
+// room for two workgroups per CU, the half-size one for four.
+inline uint32_t enc_halves(bool pos, bool pair, uint32_t W, uint32_t S) {
+  return W == 64 && !pos && !pair && S != 0 && (S & (S - 1)) == 0 ? 2u : 1u;
+}
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
@@ -91,6 +98,7 @@ struct EncodeArgs {
   uint32_t obuf_dw;    // LDS dwords for the packed tile
   uint32_t pair;       // 1: W = 16 chunk pairs (one Mask, S a multiple of 64, input 4-byte aligned)
   uint32_t wait_limit; // look-back polls of one unpublished predecessor before a tile gives up
+  uint32_t halves;     // 2: the tile is packed and stored in two halves through a half-size image
 };
 
 struct DecodeArgs {
