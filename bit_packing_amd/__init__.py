@@ -29,7 +29,10 @@ from dataclasses import dataclass
 import torch  # imported first so that libibp.so binds to the HIP runtime torch loaded
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libibp.so")
+# IBP_SANITIZE_LIB=1 loads the build whose host code carries AddressSanitizer and
+# UndefinedBehaviorSanitizer checks (build_library(sanitize=True); the process must
+# preload the clang ASan runtime, see tests/sanitize.sh)
+LIB_PATH = os.path.join(_HERE, "libibp_san.so" if os.environ.get("IBP_SANITIZE_LIB") == "1" else "libibp.so")
 
 IBP_OK, IBP_ERR_INVALID_ARG, IBP_ERR_SIZE, IBP_ERR_CAPACITY, IBP_ERR_DEVICE = 0, 1, 2, 3, 4
 IBP_DEVERR_CORRUPT, IBP_DEVERR_BAD_ID, IBP_DEVERR_TIMEOUT = 1, 2, 4

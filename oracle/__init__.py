@@ -26,7 +26,11 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ibp_oracle.c")
-_LIB = os.path.join(_HERE, "libibp_oracle.so")
+# IBP_SANITIZE_ORACLE=1 selects the AddressSanitizer + UndefinedBehaviorSanitizer build
+# (build(sanitize=True); the process must preload gcc's libasan, see tests/sanitize.sh)
+_SANITIZED = os.environ.get("IBP_SANITIZE_ORACLE") == "1"
+_LIB = os.path.join(_HERE, "libibp_oracle_san.so" if _SANITIZED else "libibp_oracle.so")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 OK, EARG, ESIZE, ECAP, ECORRUPT = 0, 1, 2, 3, 5
 
@@ -37,14 +41,16 @@ class OracleError(RuntimeError):
         self.rc = rc
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc into ``oracle/libibp_oracle.so``."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-Wall", "-Wextra",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile the oracle with gcc into ``oracle/libibp_oracle.so`` (sanitize:
+    ``oracle/libibp_oracle_san.so``, instrumented with ASan and UBSan)."""
+    lib = os.path.join(_HERE, "libibp_oracle_san.so" if sanitize else "libibp_oracle.so")
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O1" if sanitize else "-O2", "-fPIC", "-shared", "-Wall",
+                               "-Wextra", *(SAN_FLAGS if sanitize else []), "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 _lib = None
@@ -61,7 +67,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
-            build(force=True)
+            build(force=True, sanitize=_SANITIZED)
         lib = ctypes.CDLL(_LIB)
         lib.ibpo_threshold.argtypes = [_u64, ctypes.c_double]
         lib.ibpo_threshold.restype = _u64

@@ -38,16 +38,22 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gen.c")
-_LIB = os.path.join(_HERE, "libibpgen.so")
+_SANITIZED = os.environ.get("IBP_SANITIZE_ORACLE") == "1"  # ASan + UBSan build (tests/sanitize.sh)
+_LIB = os.path.join(_HERE, "libibpgen_san.so" if _SANITIZED else "libibpgen.so")
 
 
-def build(force: bool = True) -> str:
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
-        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall",
-                               "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB)
-    return _LIB
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile gen.c into libibpgen.so (sanitize: libibpgen_san.so, with ASan and
+    UBSan and without OpenMP)."""
+    lib = os.path.join(_HERE, "libibpgen_san.so" if sanitize else "libibpgen.so")
+    if force or not os.path.exists(lib):
+        tmp = lib + ".tmp"
+        flags = (["-O1", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g",
+                  "-Wno-unknown-pragmas"]
+                 if sanitize else ["-O2", "-fopenmp"])
+        subprocess.check_call(["gcc", "-std=c11", *flags, "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, lib)
+    return lib
 
 
 _lib = None
@@ -57,7 +63,7 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB):
-            build()
+            build(sanitize=_SANITIZED)
         L = ctypes.CDLL(_LIB)
         u64, vp, dbl, uint = ctypes.c_uint64, ctypes.c_void_p, ctypes.c_double, ctypes.c_uint
         L.gen_key.argtypes = [u64, u64]
