@@ -271,7 +271,7 @@ __global__ void __launch_bounds__(kBlock) raw_gather_kernel(RawGatherArgs a) {
       continue;
     }
     const uint4 x = reinterpret_cast<const uint4 *>(a.src)[(uint64_t)id * a.row_blocks + b];
-    reinterpret_cast<uint4 *>(a.out)[f] = x;
+    store_nt16(reinterpret_cast<uint4 *>(a.out) + f, x);
   }
 }
 

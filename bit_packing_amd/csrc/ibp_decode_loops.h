@@ -106,7 +106,7 @@ __device__ __forceinline__ uint32_t decode_large_s(const DecodeArgs &a, const Co
       const uint32_t pos = (lb + m + q * W - pc * run) + lane_bits - __umul24(pc, count_below(H));
       const T x = lds_field<T>(stg, pos);
       const T v = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
-      if (full || lane < m - q) o[q + lane] = v;
+      if (full || lane < m - q) store_nt(&o[q + lane], v);
       run += popc(H);
     }
     if (lb + m + m * W - pc * run != uniform(lend[r])) err |= IBP_DEVERR_CORRUPT;
@@ -130,7 +130,7 @@ template <typename T, uint32_t NR> struct Row1 {
     const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
     const uint32_t pos = base + lane * W - __umul24(p.pc, count_below(H));
     const T x = lds_field<T>(stg, pos);
-    o[q] = __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | (T)p.bitval) : x;
+    store_nt(&o[q], __builtin_amdgcn_inverse_ballot_w64(H) ? (deposit_free<T, NR>(x, p.runs) | (T)p.bitval) : x);
     base += kWave * W - p.pc * popc(H);
     hp += kWave;
   }
@@ -182,13 +182,13 @@ template <typename T, uint32_t NR> struct Row2 {
     if constexpr (W == 16) {
       const uint32_t w = lds_field<uint32_t>(stg, pos0);
       const uint32_t x = (w & 0xFFFFu) | ((w << (h0 ? pc : 0u)) & 0xFFFF0000u);
-      op[q / 2] = (P)merge16x2<NR>(p, x, h0, h1);
+      store_nt(&op[q / 2], (P)merge16x2<NR>(p, x, h0, h1));
     } else {
       const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
       const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
       const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | (T)p.bitval) : x0;
       const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | (T)p.bitval) : x1;
-      op[q / 2] = (P)v0 | ((P)v1 << W);
+      store_nt(&op[q / 2], (P)v0 | ((P)v1 << W));
     }
     base += 2u * kWave * W - pc * (popc(E) + popc(O));
     hp += 2u * kWave;
@@ -226,7 +226,7 @@ template <typename T, uint32_t NR> struct Row4 {
     const uint32_t o1 = h0 ? W - pc : W, o2 = o1 + (h1 ? W - pc : W), o3 = o2 + (h2 ? W - pc : W);
     const uint32_t xa = ((uint32_t)w & 0xFFFFu) | ((uint32_t)(w >> o1) << 16);
     const uint32_t xb = ((uint32_t)(w >> o2) & 0xFFFFu) | ((uint32_t)(w >> o3) << 16);
-    op[q / 4] = (uint64_t)merge16x2<NR>(p, xa, h0, h1) | ((uint64_t)merge16x2<NR>(p, xb, h2, h3) << 32);
+    store_nt(&op[q / 4], (uint64_t)merge16x2<NR>(p, xa, h0, h1) | ((uint64_t)merge16x2<NR>(p, xb, h2, h3) << 32));
     base += 4u * kWave * W - pc * (popc(B0) + popc(B1) + popc(B2) + popc(B3));
     hp += 4u * kWave;
   }
@@ -355,7 +355,7 @@ __device__ __forceinline__ uint32_t decode_small_s(const DecodeArgs &a, const Co
     const T x = lds_field<T>(stg, pos);
     const T v = h ? (deposit_free<T, NR>(x, p.runs) | bitval) : x;
     if (ok) {
-      out[cl] = v;
+      store_nt(&out[cl], v);
       if (i == m - 1 && pos + (h ? W - pc : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
     }
   }
@@ -396,7 +396,7 @@ __device__ __forceinline__ uint32_t decode_general(const DecodeArgs &a, const Co
     const T x = lds_field<T>(stg, pos);
     const T v = h ? (deposit_free<T, 0>(x, p.runs) | bitval) : x;
     if (ok) {
-      out[cl] = v;
+      store_nt(&out[cl], v);
       if (i == m - 1 && pos + (h ? W - pc : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
     }
     running += popc(H);

@@ -239,7 +239,7 @@ __device__ __forceinline__ uint32_t pos_row1(uint32_t S, const uint4 *tab, uint3
     const uint32_t s = h ? pos_pc<T>(tab, n, q + lane) : 0u;
     const uint32_t incl = wave_incl_scan(s);
     const T x = lds_field<T>(stg, base + lane * W - (incl - s));
-    o[q] = h ? pos_apply<T, kShift>(tab, n, q + lane, x) : x;
+    store_nt(&o[q], h ? pos_apply<T, kShift>(tab, n, q + lane, x) : x);
     base += kWave * W - last_lane(incl);
     hp += kWave;
   }
@@ -272,7 +272,7 @@ __device__ __forceinline__ uint32_t pos_row2(uint32_t S, const uint4 *tab, uint3
       const uint32_t w = lds_field<uint32_t>(stg, base + 2u * lane * W - (incl - s));
       const uint32_t x = bfi(0xFFFFu, w, w << s0);
       const uint32_t sel = (h0 ? 0x0000FFFFu : 0u) | (h1 ? 0xFFFF0000u : 0u);
-      op[q / 2] = (P)bfi(sel, kShift ? expand16x2(x, tab[i >> 1], e1) : bfi(e1.x, x, e1.y), x);
+      store_nt(&op[q / 2], (P)bfi(sel, kShift ? expand16x2(x, tab[i >> 1], e1) : bfi(e1.x, x, e1.y), x));
       base += 2u * kWave * W - last_lane(incl);
     } else {
       const uint32_t j = i >> 1;  // positions i (even) and i + 1 (odd)
@@ -289,7 +289,7 @@ __device__ __forceinline__ uint32_t pos_row2(uint32_t S, const uint4 *tab, uint3
       }
       v0 = h0 ? v0 : x0;
       v1 = h1 ? v1 : x1;
-      op[q / 2] = (P)v0 | ((P)v1 << 32);
+      store_nt(&op[q / 2], (P)v0 | ((P)v1 << 32));
       base += 2u * kWave * W - last_lane(incl);
     }
     hp += 2u * kWave;
@@ -327,7 +327,7 @@ __device__ __forceinline__ uint32_t pos_row4(uint32_t S, const uint4 *tab, uint3
     const uint32_t yb = kShift ? expand16x2(xb, tab[j + 1u], fb) : bfi(fb.x, xb, fb.y);
     const uint32_t sa = (h0 ? 0x0000FFFFu : 0u) | (h1 ? 0xFFFF0000u : 0u);
     const uint32_t sb = (h2 ? 0x0000FFFFu : 0u) | (h3 ? 0xFFFF0000u : 0u);
-    op[q / 4u] = (uint64_t)bfi(sa, ya, xa) | ((uint64_t)bfi(sb, yb, xb) << 32);
+    store_nt(&op[q / 4u], (uint64_t)bfi(sa, ya, xa) | ((uint64_t)bfi(sb, yb, xb) << 32));
     base += 4u * kWave * W - last_lane(incl);
     hp += 4u * kWave;
   }
@@ -379,7 +379,7 @@ __device__ __forceinline__ uint32_t pos_general(const DecodeArgs &a, const uint4
     const uint32_t pos = ok ? lb + m + i * W - (c + x - sv - before) : 0u;
     const T xv = lds_field<T>(stg, pos);
     if (ok) {
-      out[cl] = h ? pos_apply<T, kShift>(tab, n, i, xv) : xv;
+      store_nt(&out[cl], h ? pos_apply<T, kShift>(tab, n, i, xv) : xv);
       if (i == m - 1 && pos + (h ? W - pci : W) != lend[r]) err |= IBP_DEVERR_CORRUPT;
     }
     wave_lds_sync();

@@ -198,6 +198,26 @@ __device__ __forceinline__ void lds_or_bits(uint32_t *s, uint32_t q, uint64_t x)
 
 // ------------------------------------------------------------------ global memory
 
+// Output the kernel never reads back (decoded chunks, stream words, gathered rows):
+// non-temporal stores (measured on the contiguous decoders: 0.73 -> 0.77 of the HBM
+// peak for 64-bit chunks, 0.68 -> 0.75 for the GNN rows, 0.47 -> 0.64 for the
+// sparse rows; the compressor, with non-temporal loads of its input, 3-4% faster).
+template <typename V, typename X> __device__ __forceinline__ void store_nt(V *p, X v) {
+  __builtin_nontemporal_store((V)v, p);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void store_nt16(void *p, const uint4 &v) {
+  __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, static_cast<u32x4 *>(p));
+}
+__device__ __forceinline__ void store_nt8(void *p, const uint2 &v) {
+  __builtin_nontemporal_store(u32x2{v.x, v.y}, static_cast<u32x2 *>(p));
+}
+
+// Input read once (the compressor's chunks): a non-temporal load.
+template <typename V> __device__ __forceinline__ V load_nt(const V *p) { return __builtin_nontemporal_load(p); }
+
 __device__ __forceinline__ uint4 load16(const uint8_t *src, uint64_t blk) {
   return *reinterpret_cast<const uint4 *>(src + blk * 16u);
 }

@@ -124,7 +124,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
     const uint32_t *in2 = reinterpret_cast<const uint32_t *>(in);
     if (nch == kTile) {
 #pragma unroll
-      for (uint32_t q = 0; q < kQP; ++q) v2[q] = in2[q * kThreads + tid];
+      for (uint32_t q = 0; q < kQP; ++q) v2[q] = load_nt(&in2[q * kThreads + tid]);
     } else {
 #pragma unroll
       for (uint32_t q = 0; q < kQP; ++q) {
@@ -134,7 +134,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
     }
   } else if (nch == kTile) {  // every tile but possibly the last: no bounds tests
 #pragma unroll
-    for (uint32_t q = 0; q < kQ; ++q) v[q] = in[q * kThreads + tid];
+    for (uint32_t q = 0; q < kQ; ++q) v[q] = load_nt(&in[q * kThreads + tid]);
   } else {
 #pragma unroll
     for (uint32_t q = 0; q < kQ; ++q) {
@@ -475,7 +475,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
         case 3: o = make_uint4(al(C.x, A.w), al(C.y, C.x), al(C.z, C.y), al(C.w, C.z)); break;
         default: o = C; break;  // sh0 == 0
       }
-      *reinterpret_cast<uint4 *>(gdst + d) = o;
+      store_nt16(gdst + d, o);
     }
     for (uint32_t d = e4 + tid; d < hi; d += kThreads) gdst[d] = out_dw(d);
     if (tid == 0 && hand_tail && (old_tail & kHeadReady)) gdst[last_d] = mine_tail | (uint32_t)old_tail;

@@ -198,7 +198,7 @@ __global__ void __launch_bounds__(kBlock) decode_slots_kernel(SlotArgs a, CodecP
     if (uniform(kind[r]) != 2u) continue;
     uint4 *o = reinterpret_cast<uint4 *>(out + (uint64_t)r * a.S);
     const uint4 *s = reinterpret_cast<const uint4 *>(stg + r * a.img_dw);
-    for (uint32_t q = lane; q < row_blocks; q += kWave) o[q] = s[q];
+    for (uint32_t q = lane; q < row_blocks; q += kWave) store_nt16(o + q, s[q]);
   }
   DecodeArgs da{};
   da.S = a.S;

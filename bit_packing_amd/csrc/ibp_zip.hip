@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
       const uint32_t t0 = q * kHalf + kGroup * tid;
       uint8_t *smo = a.sm + e0 + t0;
       if (t0 + kGroup <= nb) {
-        *reinterpret_cast<uint2 *>(smo) = make_uint2(smw[b][q][0], smw[b][q][1]);
+        store_nt8(smo, make_uint2(smw[b][q][0], smw[b][q][1]));
       } else {
         for (uint32_t k = 0; t0 + k < nb; ++k) smo[k] = (uint8_t)(smw[b][q][k / 4] >> (8 * (k % 4)));
       }
@@ -297,7 +297,7 @@ __global__ void __launch_bounds__(kBlock) zip_decode_kernel(ZipArgs a) {
     const uint32_t w3 = bf16_pair(__builtin_amdgcn_perm(0u, sm[q][1], 0x0C030C02u), __builtin_amdgcn_perm(0u, ex[1], 0x0C030C02u));
     uint16_t *o = a.out + e0 + t0;
     if (t0 + kGroup <= nb) {
-      *reinterpret_cast<uint4 *>(o) = make_uint4(w0, w1, w2, w3);
+      store_nt16(o, make_uint4(w0, w1, w2, w3));
     } else {
       const uint32_t w[4] = {w0, w1, w2, w3};
       for (uint32_t k = 0; t0 + k < nb; ++k) o[k] = (uint16_t)(w[k / 2] >> (16 * (k % 2)));
