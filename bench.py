@@ -327,7 +327,7 @@ def run_workload(ctx: Ctx, name: str, headline: bool) -> dict:
         rec["roofline_compress"] = roofline("hbm", c_alg, c_ms, "ibp_compress (encode_kernel)",
                                             committed_counters(name, "compress"))
     else:
-        gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, checks)
+        gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, checks, headline)
 
     if name == "llm":
         variants_on_llm(ctx, inst, x, sample, meta, S, rec, checks)
@@ -346,7 +346,7 @@ def run_workload(ctx: Ctx, name: str, headline: bool) -> dict:
     return rec
 
 
-def gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, checks):
+def gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, checks, headline=False):
     """PCIe transfer mode: rows read zero-copy from pinned host memory (fixed slots
     and packed stream), the uncompressed zero-copy gather of the same rows, the
     measured PCIe ceilings, and the HBM-resident gather (cache mode)."""
@@ -360,7 +360,7 @@ def gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, c
     S = w.S
     n_rows = inst.data.shape[0]
     row_bytes = inst.row_bytes
-    steps = 20
+    steps = ctx.args.steps if headline else 20
     ids_all = workloads.gather_ids(name, n_rows, steps)
     ids_d = torch.from_numpy(ids_all).to(dev)
     m = ids_all.shape[1]
@@ -530,6 +530,36 @@ def zero_copy_compress(ctx, meta, inst, x, S, stream_d, off_d, ws, C, rec, check
     rec["compress_zero_copy_host"] = {"kernel_ms": zcc_ms, "pcie_read_GBps": U / zcc_ms / 1e6,
                                       "pcie_write_GBps": C / zcc_ms / 1e6}
     del raw_host, zc_stream, zc_off
+
+
+def host_call_cost(ctx) -> dict:
+    """Host time of one codec call (argument checks, pointer look-ups, launch set-up,
+    enqueue) through the C ABI and through the Python binding: the mean wall time of
+    200 calls of ibp_decompress on a small input, queued behind a spin kernel so that
+    the GPU never makes the host wait."""
+    import ctypes
+
+    torch, ibp = ctx.torch, ctx.ibp
+    dev = ctx.dev
+    meta = ibp.make_meta(64, 0xFFFFFFFFFF000000, 0)
+    x = torch.zeros(64 * 1024, dtype=torch.uint8, device=dev)
+    comp = ibp.ibp_compress(meta, x, 256, err=ctx.err)
+    out = torch.empty_like(x)
+    lib = ibp.load_library()
+    args = (ctypes.byref(meta), comp.stream.data_ptr(), comp.stream.numel(), comp.offsets.data_ptr(), comp.n_chunks,
+            256, out.data_ptr(), ctx.err.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for label, fn in (("c_abi_us", lambda: lib.ibp_decompress(*args)),
+                      ("python_binding_us", lambda: ibp.ibp_decompress(meta, comp.stream, comp.offsets, comp.n_chunks,
+                                                                       256, out=out, err=ctx.err))):
+        torch.cuda.synchronize()
+        ctx.timer._hold(50.0)
+        t0 = time.perf_counter()
+        for _ in range(200):
+            fn()
+        res[label] = (time.perf_counter() - t0) / 200 * 1e6
+        torch.cuda.synchronize()
+    return res
 
 
 # ---------------------------------------------------------------------------- CPU oracle baseline
@@ -749,7 +779,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs", default=",".join(CONFIG_ORDER),
                     help="workloads to run, in order (tiny,gnn,dlrm,llm,ids; variants: sparse,llm16)")
-    ap.add_argument("--headline", default="ids", help="the workload whose step is timed K times")
+    ap.add_argument("--headline", default=None,
+                    help="the workload whose step is timed K times (default: ids when it runs, else the first)")
     ap.add_argument("--variants", action="store_true", help="also run the sparse and W = 16 variants")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink every workload (testing only)")
     ap.add_argument("--cpu-seconds", type=float, default=0.5, help="oracle time per operation on one thread")
@@ -762,6 +793,8 @@ def main() -> int:
     names = [n for n in args.configs.split(",") if n]
     if args.variants:
         names += [v for v in VARIANTS if v not in names]
+    if args.headline is None:
+        args.headline = "ids" if "ids" in names else names[0]
     if args.headline not in names:
         names.append(args.headline)
     import workloads
@@ -769,9 +802,6 @@ def main() -> int:
         if n not in workloads.WORKLOADS:
             print(f"unknown workload {n}", file=sys.stderr)
             return 2
-    if workloads.WORKLOADS[args.headline].gather:
-        print("the headline must be a device-resident workload (tiny, llm, ids, llm16)", file=sys.stderr)
-        return 2
 
     ctx = Ctx(args)
     log("start")
@@ -779,6 +809,7 @@ def main() -> int:
     for n in names:
         results[n] = run_workload(ctx, n, headline=(n == args.headline))
     dc = ctx.device_copy()
+    host_call = host_call_cost(ctx)
     # a plain device copy of known size (the last one of the run): its counter readings
     # calibrate FETCH_SIZE / WRITE_SIZE in the committed counter summaries
     cal = ctx.torch.empty(256 << 20, dtype=ctx.torch.uint8, device=ctx.dev)
@@ -798,11 +829,12 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": f"u{w.W}", "data": "synthetic (seeded SplitMix64 generators)",
         "config": {"workload": head["workload"], "elements": head["elements"],
-                   "W": w.W, "T": w.T, "S": w.S, "source": "compressed stream resident in HBM",
-                   "step": "device-resident decompression of the whole tensor"},
+                   "W": w.W, "T": w.T, "S": w.S,
+                   "source": "pinned host memory, fixed slots" if w.gather else "compressed stream resident in HBM",
+                   "step": head["step"]},
         "compression_ratio": head["ratio"]["r_stream"], "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
-        "configs": configs, "variants": variants, "device_copy_reference": dc,
+        "configs": configs, "variants": variants, "device_copy_reference": dc, "host_call_cost": host_call,
         "checks": {"all_equal": all(all_checks.values()), **all_checks}, "device_error_words": err_words,
         "kernel_source_sha256_16": kernel_source_hash(),
     }
