@@ -87,7 +87,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = enc_threads(kPos, W);
   constexpr uint32_t kWaves = kThreads / kWave;
-  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair, W);
+  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair, W, kHalves);
   constexpr uint32_t kQ = kTile / kThreads;  // passes of kThreads chunks
   constexpr uint32_t kBal = kTile / kWave;   // 64-chunk blocks per tile
   constexpr uint32_t kPer = (kBal + kWave - 1) / kWave;  // 64-chunk blocks per lane of the prefix scan
@@ -511,10 +511,10 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  if constexpr (sizeof(T) == 8 && !kPos && !kPair && M != kModeGeneral) {
+  if constexpr (sizeof(T) >= 4 && !kPos && !kPair && M != kModeGeneral) {
     if (a.halves == 2) {
       hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2>), dim3((uint32_t)a.ntiles),
-                         dim3(enc_threads(false, 64)), shmem, s, a, p);
+                         dim3(enc_threads(false, sizeof(T) * 8)), shmem, s, a, p);
       return hipGetLastError();
     }
   }
@@ -570,7 +570,7 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
   // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
-  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u, p.W);
+  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u, p.W, a.halves);
   size_t shmem = (size_t)a.obuf_dw * 4 + (tile / kWave) * 8 + ((tile / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   if (a.pmask) {

@@ -21,15 +21,18 @@ constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-
 // The W = 16 pair form (two chunks per lane) takes 32 chunks per thread, so a
 // tile still moves 32 KB of input.
 constexpr uint32_t enc_threads(bool pos, uint32_t W) { return pos && W != 16 ? 256u : 512u; }
-constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W) {
-  return (pair ? 32u : 16u) * enc_threads(pos, W);
+constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t halves = 1) {
+  return (pair || (halves == 2 && W == 32) ? 32u : 16u) * enc_threads(pos, W);
 }
-// A compression tile of 64-bit chunks with one Mask and S a power of two is packed
-// and stored in two halves of kTile / 2 chunks (segments end at the middle) through
-// an LDS image of half the size: the full-size image (8192 chunks x 65 bits) leaves
-// room for two workgroups per CU, the half-size one for four.
+// A compression tile of 32- or 64-bit chunks with one Mask and S a power of two is
+// packed and stored in two halves (segments end at the middle) through an LDS
+// image of half the size.  64-bit chunks: 8192-chunk tiles, whose full-size image
+// (8192 chunks x 65 bits) would leave room for two workgroups per CU, the half-size
+// one for four.  32-bit chunks: 16384-chunk tiles (32 per thread) through the
+// image of 8192, so a tile moves 64 KB of input, as at W = 64, with half the
+// look-backs per byte of 8192-chunk tiles.
 inline uint32_t enc_halves(bool pos, bool pair, uint32_t W, uint32_t S) {
-  return W == 64 && !pos && !pair && S != 0 && (S & (S - 1)) == 0 ? 2u : 1u;
+  return (W == 64 || W == 32) && !pos && !pair && S != 0 && (S & (S - 1)) == 0 ? 2u : 1u;
 }
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
