@@ -79,7 +79,7 @@ __device__ __forceinline__ uint64_t interleave32(uint32_t e, uint32_t o) {
 // The pair form asks for 8 wavefronts per SIMD (its 16 unrolled passes otherwise
 // take enough scalar registers to allow only 7: 1.28 -> 1.11 ms per 2^30 chunks).
 template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false, uint32_t kHalves = 1>
-__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), kPair ? 8 : 1)
+__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kHalves == 2) ? 8 : 1)
     encode_kernel(EncodeArgs a, CodecParams p) {
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
