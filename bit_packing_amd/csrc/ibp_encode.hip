@@ -386,7 +386,14 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kH
     }
   }
   };
+  // kHalves == 2: a tile whose whole image fits the half-size buffer (at most the
+  // size of half a tile stored raw) is packed entirely before the look-back and
+  // stored once
+  const bool whole = agg <= (uint64_t)(kTile / 2) * (W + 1);
   pack(std::integral_constant<uint32_t, 0>{}, 0u);
+  if constexpr (kHalves == 2) {
+    if (whole) pack(std::integral_constant<uint32_t, 1>{}, 0u);
+  }
   __syncthreads();
 
   // 5. the tile's start bit: decoupled look-back over the predecessors
@@ -483,20 +490,20 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kH
   };
   if constexpr (kHalves == 1) {
     store(excl, agg, false, false, 0u);
+  } else if (whole) {
+    store(excl, agg, false, false, 0u);
   } else {
-    // the first half's size: its segments end at chunk kTile / 2
-    const bool two = nch > kTile / 2;
-    const uint64_t agg0 = two ? (uint64_t)(kTile / 2) * (W + 1) - (uint64_t)pc * pref[kBal / 2] : agg;
-    store(excl, agg0, false, two, 0u);
-    if (two) {
-      __syncthreads();  // the first half's image has been read
-      for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kThreads)
-        *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
-      __syncthreads();
-      pack(std::integral_constant<uint32_t, 1>{}, (uint32_t)agg0);
-      __syncthreads();
-      store(excl + agg0, agg - agg0, true, false, s_carry);
-    }
+    // a tile larger than the buffer holds more than kTile / 2 chunks, so it has two
+    // halves; the first half's segments end at chunk kTile / 2
+    const uint64_t agg0 = (uint64_t)(kTile / 2) * (W + 1) - (uint64_t)pc * pref[kBal / 2];
+    store(excl, agg0, false, true, 0u);
+    __syncthreads();  // the first half's image has been read
+    for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kThreads)
+      *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    pack(std::integral_constant<uint32_t, 1>{}, (uint32_t)agg0);
+    __syncthreads();
+    store(excl + agg0, agg - agg0, true, false, s_carry);
   }
 }
 

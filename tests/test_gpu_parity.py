@@ -2,9 +2,9 @@
 
 Tolerance is 0 everywhere: the codec is lossless, so counts, Mask, Bitval, the
 offset table, every stream byte below ceil(total/8) and the round trip must
-agree exactly.  Sizes span several compression tiles (8192 chunks, 4096 with
-position metadata) and
-decompression tiles (512 chunks per wavefront) plus ragged tails.
+agree exactly.  Sizes span several compression tiles (8,192 or 16,384 chunks,
+4,096 with position metadata) and decompression tiles (512 chunks per wavefront)
+plus ragged tails.
 """
 import numpy as np
 import pytest
@@ -96,6 +96,41 @@ def test_compress_decompress_parity(ibp, W, S):
         for n in sizes:
             p = 0.9 if name != "zero" else 1.0
             _run_case(ibp, dev, _data(rng, n, W, mask, bitval, p), W, S, mask, bitval, f"{name}-{n}")
+
+
+@pytest.mark.parametrize("W", [32, 64])
+@pytest.mark.parametrize("S", [1, 32, 64, 256])
+def test_tiles_near_the_half_image_size(ibp, W, S):
+    """One Mask and S a power of two: a compression tile (16,384 chunks at W = 32,
+    8,192 at W = 64) whose stream size is at most that of half the tile stored raw
+    is packed whole and stored once, a larger one in two halves.  Tiles alternate
+    between the two, including sizes exactly at the limit and one chunk's saving
+    above it, and end in a ragged tail; every byte must match the oracle."""
+    dev = torch.device("cuda:0")
+    tile = 16384 if W == 32 else 8192
+    pc = 24 if W == 32 else 40  # popcount(Mask); tile (W + 1) / (2 pc) is an integer
+    mask = ((1 << pc) - 1) << (W - pc)
+    bitval = mask & 0x5A5A5A5A5A5A5A5A
+    limit = tile * (W + 1) // 2      # the largest tile that is packed whole, in bits
+    k_at = (tile * (W + 1) - limit) // pc  # matching chunks that give exactly that size
+    rng = np.random.default_rng(W * 7 + S)
+    # matching chunks per tile: exactly at the limit, one saving short of it, none,
+    # all, and random fractions; then a ragged tail
+    counts = [k_at, k_at - 1, 0, tile, k_at + 1, tile // 3]
+    parts = []
+    for k in counts:
+        v = _data(rng, tile, W, mask, bitval, 0.0)
+        keep = rng.permutation(tile)[:k]
+        t = DT[W]
+        v[keep] = (v[keep] & t(~mask & ((1 << W) - 1))) | t(bitval)
+        # no chunk outside `keep` may match by chance
+        others = np.setdiff1d(np.arange(tile), keep)
+        hit = ((v[others] ^ t(bitval)) & t(mask)) == 0
+        v[others[hit]] ^= t(1 << (W - 1))
+        parts.append(v)
+    parts.append(_data(rng, 3 * tile // 4 + 5, W, mask, bitval, 0.5))
+    v = np.concatenate(parts)
+    _run_case(ibp, dev, v, W, S, mask, bitval, f"half-image W={W} S={S}")
 
 
 @pytest.mark.parametrize("W", [16, 32])
