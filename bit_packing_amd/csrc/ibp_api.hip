@@ -77,8 +77,8 @@ uint32_t meta_blocks(uint64_t n) {
   return (uint32_t)(want < 1 ? 1 : (want > kMetaMaxBlocks ? kMetaMaxBlocks : want));
 }
 
-uint32_t enc_segs_per_tile(uint32_t S, bool pos, bool pair, uint32_t W, uint32_t halves = 1) {
-  const uint32_t tile = enc_tile_chunks(pos, pair, W, halves);
+uint32_t enc_segs_per_tile(uint32_t S, bool pos, bool pair, uint32_t W, uint32_t halves = 1, bool big = false) {
+  const uint32_t tile = enc_tile_chunks(pos, pair, W, halves, big);
   return S >= tile ? 1u : tile / S;
 }
 
@@ -285,7 +285,8 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   // whole 64-chunk blocks and the input allows it
   a.pair = (p.W == 16 && !pmask && S % kWave == 0 && aligned(d_in, 4)) ? 1u : 0u;
   a.halves = enc_halves(pmask != nullptr, a.pair != 0u, p.W, S);
-  a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W, a.halves);
+  a.big = enc_big(p.W, a.halves, p.pc) ? 1u : 0u;
+  a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W, a.halves, a.big != 0u);
   a.ntiles = (nseg + a.G - 1) / a.G;  // at most the workspace's tile count (its tiles are the smallest)
   a.tails = a.status + a.ntiles;
   a.err = d_err_word;
@@ -294,7 +295,8 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   a.S = S;
   a.s_log2 = log2_if_pow2(S);
   a.tile_chunks = a.G * S;
-  if (a.halves == 2 && a.tile_chunks != enc_tile_chunks(false, false, p.W, 2)) return IBP_ERR_INVALID_ARG;
+  if (a.halves == 2 && a.tile_chunks != enc_tile_chunks(false, false, p.W, 2, a.big != 0u))
+    return IBP_ERR_INVALID_ARG;
   // image (one half's when halves == 2) from the 16-byte block of the first bit
   a.obuf_dw = ((127 + a.tile_chunks / a.halves * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;
   a.wait_limit = g_wait_limit.load();

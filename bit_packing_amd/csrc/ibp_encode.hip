@@ -78,16 +78,17 @@ __device__ __forceinline__ uint64_t interleave32(uint32_t e, uint32_t o) {
 
 // The pair form asks for 8 wavefronts per SIMD (its 16 unrolled passes otherwise
 // take enough scalar registers to allow only 7: 1.28 -> 1.11 ms per 2^30 chunks).
-template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false, uint32_t kHalves = 1>
-__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kHalves == 2) ? 8 : 1)
+template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false, uint32_t kHalves = 1, bool kBig = false>
+__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair || kHalves == 2) ? 8 : 1)
     encode_kernel(EncodeArgs a, CodecParams p) {
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
   static_assert(kHalves == 1 || (!kPos && !kPair && kMode != kModeGeneral), "halves: one Mask, S a power of two");
+  static_assert(!kBig || (kHalves == 2 && sizeof(T) == 8), "1024-thread tiles: 64-bit chunks in halves");
   constexpr uint32_t W = sizeof(T) * 8;
-  constexpr uint32_t kThreads = enc_threads(kPos, W);
+  constexpr uint32_t kThreads = enc_threads(kPos, W, kBig);
   constexpr uint32_t kWaves = kThreads / kWave;
-  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair, W, kHalves);
+  constexpr uint32_t kTile = enc_tile_chunks(kPos, kPair, W, kHalves, kBig);
   constexpr uint32_t kQ = kTile / kThreads;  // passes of kThreads chunks
   constexpr uint32_t kBal = kTile / kWave;   // 64-chunk blocks per tile
   constexpr uint32_t kPer = (kBal + kWave - 1) / kWave;  // 64-chunk blocks per lane of the prefix scan
@@ -260,11 +261,17 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kH
   uint32_t my_pref[kPer];
 #pragma unroll
   for (uint32_t k = 0; k < kPer; ++k) my_pref[k] = kWave * k + lane <= kBal ? pref[kWave * k + lane] : 0u;
-  auto pref_at = [&](uint32_t b) -> uint32_t {  // b wave-uniform
+  // the prefix of block b0 + m wave, where b0 = m q kWaves is a constant once the
+  // passes are unrolled: m kWaves divides 64 and wave < kWaves, so every
+  // wavefront's block lies in my_pref[b0 / 64], lane (b0 mod 64) + m wave, and the
+  // lookup is one v_readlane
+  static_assert(kWave % (2 * kWaves) == 0, "two blocks per wavefront fit one lane row");
+  auto pref_at = [&](uint32_t b0, uint32_t m) -> uint32_t {
+    const uint32_t l = (b0 & 63u) + m * wave;
     uint32_t v = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k)
-      if ((b >> 6) == k) v = (uint32_t)__builtin_amdgcn_readlane((int)my_pref[k], (int)(b & 63u));
+      if ((b0 >> 6) == k) v = (uint32_t)__builtin_amdgcn_readlane((int)my_pref[k], (int)l);
     return v;
   };
   auto seg_start = [&](uint32_t c) -> uint32_t {  // first chunk of the segment holding tile chunk c
@@ -285,7 +292,8 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kH
       const uint32_t m = min(a.S, nch - s0);
       bool h0, h1;
       even_odd(q, h0, h1);
-      const uint32_t saved = __umul24(pc, pref_at(blk) + count_below(ballot(h0)) + count_below(ballot(h1)));
+      const uint32_t saved =
+          __umul24(pc, pref_at(2u * q * kWaves, 2u) + count_below(ballot(h0)) + count_below(ballot(h1)));
       const uint32_t pos = s0 + m + c * W - saved;
       const uint32_t x = v2[q];
       uint32_t ext = 0;
@@ -342,7 +350,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kH
       } else {
         const uint32_t s0 = seg_start(cb);
         const uint32_t m = min(a.S, nch - s0);
-        const uint32_t saved = __umul24(pc, pref_at(blk) + count_below(B[q]));
+        const uint32_t saved = __umul24(pc, pref_at(q * kWaves, 1u) + count_below(B[q]));
         const uint32_t pos = (s0 + m + cb * W) + lane_bits - saved - H;
         lds_or_bits(obuf, valid ? pos : 0u, payload());  // invalid lanes hold 0
       }
@@ -356,10 +364,10 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8), (kPair || kH
         const uint32_t c_cl = uniform(pref[blk]) + svx[q];
         if (valid) lds_or_field(obuf, segbase + m + i_lane * W - (c_cl - gs), payload());
       } else {
-        const uint32_t gs = pc * (pref_at(blk) + popc(B[q] & seg_below));
+        const uint32_t gs = pc * (pref_at(q * kWaves, 1u) + popc(B[q] & seg_below));
         if (valid && i_lane == 0)
           lds_or_bits(obuf, s0 * (W + 1) - gs - H, (uint32_t)((B[q] >> lane) & low_lanes(m)));
-        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(blk) + count_below(B[q])) - H;
+        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(q * kWaves, 1u) + count_below(B[q])) - H;
         lds_or_bits(obuf, valid ? pos : 0u, payload());
       }
     } else {
@@ -520,6 +528,13 @@ template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = f
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
   if constexpr (sizeof(T) >= 4 && !kPos && !kPair && M != kModeGeneral) {
     if (a.halves == 2) {
+      if constexpr (sizeof(T) == 8) {
+        if (a.big) {
+          hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2, true>), dim3((uint32_t)a.ntiles),
+                             dim3(enc_threads(false, 64, true)), shmem, s, a, p);
+          return hipGetLastError();
+        }
+      }
       hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2>), dim3((uint32_t)a.ntiles),
                          dim3(enc_threads(false, sizeof(T) * 8)), shmem, s, a, p);
       return hipGetLastError();
@@ -577,7 +592,7 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
   if (e != hipSuccess) return e;
   // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
-  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u, p.W, a.halves);
+  const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u, p.W, a.halves, a.big != 0u);
   size_t shmem = (size_t)a.obuf_dw * 4 + (tile / kWave) * 8 + ((tile / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   if (a.pmask) {

@@ -14,15 +14,17 @@ constexpr uint32_t kMaxRuns = 32;       // at most 32 runs of free bits in a 64-
 
 // Compression: a workgroup of enc_threads() threads sizes, offsets and packs a
 // tile of 16 chunks per thread.  Measured on the workloads: 512 threads beat 256
-// by 3-10% with one Mask (1024 did not); with position-dependent metadata, whose
-// tables and per-chunk prefixes also live in LDS, 256 is fastest at W = 32 and 64
-// (512: 17-50% slower) and 512 at W = 16 (4.4 -> 3.3 ms per 2^30 chunks); 128 and
-// 64 threads were 10-50% slower, their per-tile costs spread over fewer chunks.
-// The W = 16 pair form (two chunks per lane) takes 32 chunks per thread, so a
-// tile still moves 32 KB of input.
-constexpr uint32_t enc_threads(bool pos, uint32_t W) { return pos && W != 16 ? 256u : 512u; }
-constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t halves = 1) {
-  return (pair || (halves == 2 && W == 32) ? 32u : 16u) * enc_threads(pos, W);
+// by 3-10% with one Mask; with position-dependent metadata, whose tables and
+// per-chunk prefixes also live in LDS, 256 is fastest at W = 32 and 64 (512: 17-50%
+// slower) and 512 at W = 16 (4.4 -> 3.3 ms per 2^30 chunks); 128 and 64 threads were
+// 10-50% slower, their per-tile costs spread over fewer chunks.  The W = 16 pair
+// form (two chunks per lane) takes 32 chunks per thread, so a tile still moves
+// 32 KB of input.
+constexpr uint32_t enc_threads(bool pos, uint32_t W, bool big = false) {
+  return big ? 1024u : (pos && W != 16 ? 256u : 512u);
+}
+constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t halves = 1, bool big = false) {
+  return (pair || (halves == 2 && W == 32) ? 32u : 16u) * enc_threads(pos, W, big);
 }
 // A compression tile of 32- or 64-bit chunks with one Mask and S a power of two is
 // packed and stored in two halves (segments end at the middle) through an LDS
@@ -30,10 +32,17 @@ constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t hal
 // (8192 chunks x 65 bits) would leave room for two workgroups per CU, the half-size
 // one for four.  32-bit chunks: 16384-chunk tiles (32 per thread) through the
 // image of 8192, so a tile moves 64 KB of input, as at W = 64, with half the
-// look-backs per byte of 8192-chunk tiles.
+// look-backs per byte of 8192-chunk tiles.  A tile whose stream fits the half-size
+// image is packed whole before its look-back and stored once.
 inline uint32_t enc_halves(bool pos, bool pair, uint32_t W, uint32_t S) {
   return (W == 64 || W == 32) && !pos && !pair && S != 0 && (S & (S - 1)) == 0 ? 2u : 1u;
 }
+// A tile saves at most popcount(Mask) bits per chunk, so only when popcount(Mask) >
+// (W + 1) / 2 can a whole tile fit the half-size image.  For such 64-bit chunks the
+// tile doubles (1024 threads, 16384 chunks, two workgroups per CU): each look-back
+// then covers 128 KB (measured on the id stream, which fits: 1.19 -> 1.12 ms; tiles
+// that do not fit ran 2-13% slower at this size, so the others keep 512 threads).
+inline bool enc_big(uint32_t W, uint32_t halves, uint32_t pc) { return halves == 2 && W == 64 && 2 * pc > W + 1; }
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
@@ -102,6 +111,7 @@ struct EncodeArgs {
   uint32_t pair;       // 1: W = 16 chunk pairs (one Mask, S a multiple of 64, input 4-byte aligned)
   uint32_t wait_limit; // look-back polls of one unpublished predecessor before a tile gives up
   uint32_t halves;     // 2: the tile is packed and stored in two halves through a half-size image
+  uint32_t big;        // 1: 1024-thread tiles (enc_big)
 };
 
 struct DecodeArgs {

@@ -101,13 +101,15 @@ def test_compress_decompress_parity(ibp, W, S):
 @pytest.mark.parametrize("W", [32, 64])
 @pytest.mark.parametrize("S", [1, 32, 64, 256])
 def test_tiles_near_the_half_image_size(ibp, W, S):
-    """One Mask and S a power of two: a compression tile (16,384 chunks at W = 32,
-    8,192 at W = 64) whose stream size is at most that of half the tile stored raw
-    is packed whole and stored once, a larger one in two halves.  Tiles alternate
-    between the two, including sizes exactly at the limit and one chunk's saving
-    above it, and end in a ragged tail; every byte must match the oracle."""
+    """One Mask and S a power of two: a compression tile whose stream size is at
+    most that of half the tile stored raw is packed whole and stored once, a larger
+    one in two halves.  The tile is 16,384 chunks here for both widths (W = 32; and
+    W = 64 with more than 32 invariant bits, where a tile can fit at all).  Tiles
+    alternate between the two forms, including sizes exactly at the limit and one
+    chunk's saving on either side of it, and end in a ragged tail; every byte must
+    match the oracle."""
     dev = torch.device("cuda:0")
-    tile = 16384 if W == 32 else 8192
+    tile = 16384
     pc = 24 if W == 32 else 40  # popcount(Mask); tile (W + 1) / (2 pc) is an integer
     mask = ((1 << pc) - 1) << (W - pc)
     bitval = mask & 0x5A5A5A5A5A5A5A5A
