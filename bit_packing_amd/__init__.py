@@ -46,7 +46,8 @@ EXPORTS = (
     "ibp_slot_flag_words", "ibp_compress_slots", "ibp_decompress_gather_slots",
     "ibp_metadata_pos_workspace_bytes", "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos",
     "ibp_zip_table_from_sigma", "ibp_zip_blocks", "ibp_zip_codes_bytes", "ibp_zip_workspace_bytes",
-    "ibp_zip_compress", "ibp_zip_decompress", "ibp_set_wait_limit", "ibp_compress_noalloc",
+    "ibp_zip_compress", "ibp_zip_decompress", "ibp_set_wait_limit", "ibp_set_halves_min_chunks",
+    "ibp_compress_noalloc",
 )
 
 
@@ -136,6 +137,8 @@ def load_library() -> ctypes.CDLL:
         lib.ibp_compress_noalloc.restype = _int
         lib.ibp_set_wait_limit.argtypes = [_u32]
         lib.ibp_set_wait_limit.restype = _u32
+        lib.ibp_set_halves_min_chunks.argtypes = [_u64]
+        lib.ibp_set_halves_min_chunks.restype = _u64
         for f in ("ibp_build_metadata", "ibp_compress", "ibp_decompress", "ibp_decompress_gather",
                   "ibp_gather_raw", "ibp_compress_slots", "ibp_decompress_gather_slots",
                   "ibp_build_metadata_pos", "ibp_compress_pos", "ibp_decompress_pos", "ibp_zip_table_from_sigma",
@@ -206,6 +209,13 @@ def ibp_set_wait_limit(polls: int) -> int:
     unpublished predecessor before a tile gives up (0xFFFFFFFF = the default).
     Returns the former value."""
     return int(load_library().ibp_set_wait_limit(polls))
+
+
+def ibp_set_halves_min_chunks(n_chunks: int) -> int:
+    """Compression inputs of at least n_chunks chunks (one Mask, W = 32 or 64, S a
+    power of two) take the two-half tiles, smaller ones 8192-chunk tiles; the output
+    is the same.  0xFFFFFFFFFFFFFFFF = the default (2^23).  Returns the former value."""
+    return int(load_library().ibp_set_halves_min_chunks(n_chunks))
 
 
 # ------------------------------------------------------------------ codec

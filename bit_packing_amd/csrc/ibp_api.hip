@@ -36,6 +36,8 @@ bool mul_ok(uint64_t x, uint64_t y, uint64_t *out) { return !__builtin_mul_overf
 // up (see lookback_finish); lowered only by tests of that path.
 constexpr uint32_t kDefaultWaitLimit = 1u << 20;
 std::atomic<uint32_t> g_wait_limit{kDefaultWaitLimit};
+constexpr uint64_t kDefaultHalvesMin = 1ull << 23;  // chunks; see ibp_set_halves_min_chunks
+std::atomic<uint64_t> g_halves_min{kDefaultHalvesMin};
 
 // Mask/Bitval -> kernel parameters: popcount and the runs of free positions.
 bool make_params(const ibp_meta_t *m, CodecParams *p) {
@@ -191,6 +193,10 @@ IBP_API uint32_t ibp_set_wait_limit(uint32_t polls) {
   return g_wait_limit.exchange(polls == 0xFFFFFFFFu ? kDefaultWaitLimit : polls);
 }
 
+IBP_API uint64_t ibp_set_halves_min_chunks(uint64_t n_chunks) {
+  return g_halves_min.exchange(n_chunks == ~0ull ? kDefaultHalvesMin : n_chunks);
+}
+
 IBP_API uint64_t ibp_num_segments(uint64_t n_chunks, uint32_t S) {
   return S ? (n_chunks + S - 1) / S : 0;
 }
@@ -284,7 +290,7 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   // W = 16 with one Mask reads chunk pairs as 32-bit words when the segments are
   // whole 64-chunk blocks and the input allows it
   a.pair = (p.W == 16 && !pmask && S % kWave == 0 && aligned(d_in, 4)) ? 1u : 0u;
-  a.halves = enc_halves(pmask != nullptr, a.pair != 0u, p.W, S);
+  a.halves = n >= g_halves_min.load() ? enc_halves(pmask != nullptr, a.pair != 0u, p.W, S) : 1u;
   a.big = enc_big(p.W, a.halves, p.pc) ? 1u : 0u;
   a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W, a.halves, a.big != 0u);
   a.ntiles = (nseg + a.G - 1) / a.G;  // at most the workspace's tile count (its tiles are the smallest)

@@ -101,6 +101,17 @@ IBP_API const char *ibp_status_str(int status);
  * made after it, process-wide; returns the former value. */
 IBP_API uint32_t ibp_set_wait_limit(uint32_t polls);
 
+/* Compression tile form, for tuning and for tests that run both forms on small
+ * inputs (the stream and offsets do not depend on it).  With one Mask, W = 32 or 64
+ * and S a power of two, inputs of at least `n_chunks` chunks (default 2^23) take
+ * the larger tiles packed in two halves, and smaller ones one-image tiles of 8192
+ * chunks: a launch too small to fill the GPU is latency-bound and gains from more,
+ * shorter tiles (measured: 65,536 chunks 9.5 us against 15.4 us; 2^26 chunks
+ * 120 us against 150 us the other way; the cross-over lies between 2^22 and 2^23).
+ * 0xFFFFFFFFFFFFFFFF restores the default.  Applies to calls made after it,
+ * process-wide; returns the former value. */
+IBP_API uint64_t ibp_set_halves_min_chunks(uint64_t n_chunks);
+
 /* ceil(n_chunks / S); 0 when S == 0. */
 IBP_API uint64_t ibp_num_segments(uint64_t n_chunks, uint32_t S);
 

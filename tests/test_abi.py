@@ -181,6 +181,17 @@ def test_wait_limit_setter(ibp):
     assert lib.ibp_set_wait_limit(0xFFFFFFFF) == 1 << 20
 
 
+def test_halves_min_chunks_setter(ibp):
+    """The compression tile-form threshold: set, read back, restore the default."""
+    lib = ibp.load_library()
+    first = ibp.ibp_set_halves_min_chunks(7)
+    assert ibp.ibp_set_halves_min_chunks(0) == 7
+    assert ibp.ibp_set_halves_min_chunks(0xFFFFFFFFFFFFFFFF) == 0
+    assert ibp.ibp_set_halves_min_chunks(0xFFFFFFFFFFFFFFFF) == 1 << 23
+    assert first == 1 << 23
+    assert lib.ibp_set_halves_min_chunks(0xFFFFFFFFFFFFFFFF) == 1 << 23
+
+
 def test_noalloc_limit_and_refusal(ibp):
     """The header's limit of the no-alloc compression equals the binding's, and an
     input whose workspace exceeds it is refused on the host (IBP_ERR_CAPACITY) before

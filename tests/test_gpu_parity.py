@@ -65,15 +65,22 @@ def _run_case(ibp, dev, v, W, S, mask, bitval, tag):
     meta = ibp.make_meta(W, mask, bitval)
     x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
-    comp = ibp.ibp_compress(meta, x, S, err=err)
     ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
-    off = comp.offsets.cpu().numpy().view(np.uint64)
-    assert np.array_equal(off, ref_off), f"{tag}: offsets differ"
     nb = (int(ref_off[-1]) + 7) // 8
-    got = comp.stream[:nb].cpu().numpy()
-    if not np.array_equal(got, ref_stream):
-        bad = int(np.nonzero(got != ref_stream)[0][0])
-        raise AssertionError(f"{tag}: stream differs first at byte {bad} of {nb}")
+    # both compression tile forms: the size-chosen one, and the large two-half tiles
+    # forced on this small input (threshold 0)
+    for form, threshold in (("default tiles", 0xFFFFFFFFFFFFFFFF), ("two-half tiles", 0)):
+        ibp.ibp_set_halves_min_chunks(threshold)
+        try:
+            comp = ibp.ibp_compress(meta, x, S, err=err)
+        finally:
+            ibp.ibp_set_halves_min_chunks(0xFFFFFFFFFFFFFFFF)
+        off = comp.offsets.cpu().numpy().view(np.uint64)
+        assert np.array_equal(off, ref_off), f"{tag}, {form}: offsets differ"
+        got = comp.stream[:nb].cpu().numpy()
+        if not np.array_equal(got, ref_stream):
+            bad = int(np.nonzero(got != ref_stream)[0][0])
+            raise AssertionError(f"{tag}, {form}: stream differs first at byte {bad} of {nb}")
     # decode the GPU stream
     out = ibp.ibp_decompress(meta, comp.stream, comp.offsets, n, S, err=err)
     assert torch.equal(out, x), f"{tag}: round trip differs"
@@ -104,7 +111,8 @@ def test_tiles_near_the_half_image_size(ibp, W, S):
     """One Mask and S a power of two: a compression tile whose stream size is at
     most that of half the tile stored raw is packed whole and stored once, a larger
     one in two halves.  The tile is 16,384 chunks here for both widths (W = 32; and
-    W = 64 with more than 32 invariant bits, where a tile can fit at all).  Tiles
+    W = 64 with more than 32 invariant bits, where a tile can fit at all), forced on
+    this small input by the case runner, which compresses with both tile forms.  Tiles
     alternate between the two forms, including sizes exactly at the limit and one
     chunk's saving on either side of it, and end in a ragged tail; every byte must
     match the oracle."""
