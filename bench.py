@@ -63,7 +63,7 @@ CONFIG_ORDER = ["tiny", "gnn", "dlrm", "llm", "ids"]
 VARIANTS = ["sparse", "llm16"]
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in
                   ("ibp_device.h", "ibp_decode_loops.h", "ibp_internal.h", "ibp_meta.hip", "ibp_encode.hip",
-                   "ibp_decode.hip", "ibp_decode_pos.hip", "ibp_slots.hip", "ibp_zip.hip")]
+                   "ibp_decode.hip", "ibp_decode_pos.hip", "ibp_slots.hip", "ibp_zip.hip", "ibp_api.hip")]
 T0 = time.perf_counter()
 
 
