@@ -60,7 +60,7 @@ METRIC = "IBP decompress effective GB/s (HBM- and PCIe-sourced) + compression ra
 HBM_PEAK_GBPS = 8000.0     # MI355X HBM3E, AMD published
 PCIE_PEAK_GBPS = 64.0      # PCIe 5.0 x16, one direction, published link rate
 CONFIG_ORDER = ["tiny", "gnn", "dlrm", "llm", "ids"]
-VARIANTS = ["sparse", "llm16"]
+VARIANTS = ["sparse", "llm16", "mixed"]
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_packing_amd", "csrc", f) for f in
                   ("ibp_device.h", "ibp_decode_loops.h", "ibp_internal.h", "ibp_meta.hip", "ibp_encode.hip",
                    "ibp_decode.hip", "ibp_decode_pos.hip", "ibp_slots.hip", "ibp_zip.hip", "ibp_api.hip")]
@@ -329,8 +329,10 @@ def run_workload(ctx: Ctx, name: str, headline: bool) -> dict:
     else:
         gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, checks, headline)
 
+    if name in ("llm", "mixed"):
+        position_metadata_variant(ctx, inst, x, sample, meta, S, rec, checks)
     if name == "llm":
-        variants_on_llm(ctx, inst, x, sample, meta, S, rec, checks)
+        zipccl_variant(ctx, inst, x, rec, checks)
     if name == "gnn":
         zero_copy_compress(ctx, meta, inst, x, S, stream_d, off_d, ws, C, rec, checks)
 
@@ -454,9 +456,9 @@ def gather_section(ctx, name, inst, meta, x, stream_v, off_d, C, nseg, U, rec, c
     del out_rows, ids_d
 
 
-def variants_on_llm(ctx, inst, x, sample, meta, S, rec, checks):
-    """On the BF16 tensor: position-dependent metadata, and the ZipCCL exponent codec
-    for comparison (not IBP)."""
+def position_metadata_variant(ctx, inst, x, sample, meta, S, rec, checks):
+    """Position-dependent metadata (one Mask/Bitval per chunk position of a segment)
+    against the single Mask of the same run: ratio, compression and decompression."""
     import numpy as np
 
     torch, ibp, timer, err = ctx.torch, ctx.ibp, ctx.timer, ctx.err
@@ -486,12 +488,20 @@ def variants_on_llm(ctx, inst, x, sample, meta, S, rec, checks):
     pm = pmeta.mask.cpu().numpy().view(np.uint64)
     pd_alg = PC + 8 * (nseg + 1) + U
     rec["position_metadata"] = {
-        "ratio": U / PC, "positions": S, "sample_rows": n_rows_sample,
-        "positions_whose_mask_differs": int((pm != np.uint64(meta.mask)).sum()),
-        "compress_kernel_ms": pc_ms, "decompress_kernel_ms": pd_ms,
-        "decompress_hbm_fraction": pd_alg / pd_ms / 1e6 / HBM_PEAK_GBPS}
+        "ratio": U / PC, "ratio_single_mask": rec["ratio"]["r_stream"], "positions": S,
+        "sample_rows": n_rows_sample, "positions_whose_mask_differs": int((pm != np.uint64(meta.mask)).sum()),
+        "compress_kernel_ms": pc_ms, "compress_hbm_fraction": pd_alg / pc_ms / 1e6 / HBM_PEAK_GBPS,
+        "decompress_kernel_ms": pd_ms, "decompress_hbm_fraction": pd_alg / pd_ms / 1e6 / HBM_PEAK_GBPS}
+    log(f"{inst.w.name}: position metadata ratio {U / PC:.4f} (single Mask {rec['ratio']['r_stream']:.4f}), "
+        f"compress {pc_ms:.3f} ms, decompress {pd_ms:.3f} ms")
     del pstream, pout, pview, poff, ws
 
+
+def zipccl_variant(ctx, inst, x, rec, checks):
+    """On a BF16 tensor: the ZipCCL exponent codec, for comparison (not IBP)."""
+    torch, ibp, timer, err = ctx.torch, ctx.ibp, ctx.timer, ctx.err
+    dev = ctx.dev
+    U = inst.data.nbytes
     table = ibp.ibp_zip_table_from_sigma(inst.w.sigma)
     n16 = U // 2
     z = ibp.ibp_zip_compress(table, x, err=err)
@@ -778,10 +788,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20, help="timed steps of the headline workload")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--configs", default=",".join(CONFIG_ORDER),
-                    help="workloads to run, in order (tiny,gnn,dlrm,llm,ids; variants: sparse,llm16)")
+                    help="workloads to run, in order (tiny,gnn,dlrm,llm,ids; variants: sparse,llm16,mixed)")
     ap.add_argument("--headline", default=None,
                     help="the workload whose step is timed K times (default: ids when it runs, else the first)")
-    ap.add_argument("--variants", action="store_true", help="also run the sparse and W = 16 variants")
+    ap.add_argument("--variants", action="store_true", help="also run the sparse, W = 16 and mixed feature-row variants")
     ap.add_argument("--scale", type=float, default=1.0, help="shrink every workload (testing only)")
     ap.add_argument("--cpu-seconds", type=float, default=0.5, help="oracle time per operation on one thread")
     ap.add_argument("--no-cpu-baseline", action="store_true")

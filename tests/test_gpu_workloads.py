@@ -26,7 +26,7 @@ def _bits(buf: np.ndarray, a: int, b: int) -> np.ndarray:
     return np.unpackbits(chunk, bitorder="little")[a % 8:a % 8 + (b - a)]
 
 
-@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids", "sparse", "llm16"])
+@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids", "sparse", "llm16", "mixed"])
 def test_workload_full_size(name):
     import bit_packing_amd as ibp
 
@@ -84,7 +84,7 @@ def test_workload_full_size(name):
     assert int(err.item()) == 0
 
 
-@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids", "sparse", "llm16"])
+@pytest.mark.parametrize("name", ["tiny", "gnn", "dlrm", "llm", "ids", "sparse", "llm16", "mixed"])
 def test_workload_variants_full_size(name):
     """The variants bench.py also times, at the workloads' full sizes: the gather from
     the HBM-resident table, the fixed-slot table in pinned memory, position-dependent

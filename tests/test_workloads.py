@@ -60,13 +60,17 @@ EXPECTED = {
     # the llm tensor one bf16 per chunk: the same exponent bits per element, matched with
     # P = 0.97468, so 16 / (17 - 5 * 0.97468) = 1.3194 (one participation bit per element)
     "llm16": (0x7C00, 0x3800, 1.3194),
+    # ids keep their 12 high bits at 0, N(0,1) floats no bit in >= 98% of the rows
+    # (|x| < 2 holds for 95.4%), so no bit is invariant across the whole row: every
+    # chunk keeps its 64 bits plus its participation bit, 64 / 65
+    "mixed": (0x0, 0x0, 0.98462),
 }
 
 
 @pytest.mark.parametrize("name", list(EXPECTED))
 def test_expected_metadata_and_ratio(name):
     inst = workloads.generate(name, {"tiny": 1, "gnn": 0.02, "dlrm": 0.002, "llm": 0.002, "ids": 0.002, "sparse": 0.02,
-                                    "llm16": 0.002}[name])
+                                    "llm16": 0.002, "mixed": 0.005}[name])
     W = inst.w.W
     mask, bitval, _ = oracle.build_meta(inst.sample, W, inst.w.T)
     em, eb, er = EXPECTED[name]
@@ -75,3 +79,21 @@ def test_expected_metadata_and_ratio(name):
     off = oracle.offsets(x, W, mask, bitval, inst.w.S)
     ratio = x.nbytes * 8 / int(off[-1])
     assert abs(ratio / er - 1) < 0.01, ratio
+
+
+def test_mixed_rows_position_metadata():
+    """Feature rows (32 ids < 2^20, then 32 N(0,1) floats): the per-position tables
+    find each id chunk's 2 x 12 zero bits and nothing in the float chunks, so a row
+    of 32 chunks costs 16 (65 - 24) + 16 x 65 = 1696 bits for 2048: ratio 1.2075."""
+    inst = workloads.generate("mixed", 0.005)
+    ids = inst.data[:, :32]
+    dense = inst.data[:, 32:].view(np.float32)
+    assert ids.max() < (1 << 20) and ids.max() > (1 << 19)
+    assert abs(dense.std() - 1.0) < 0.02 and abs(dense.mean()) < 0.02
+    W, S, T = inst.w.W, inst.w.S, inst.w.T
+    pm, pb, _ = oracle.build_meta_pos(inst.sample.reshape(-1).view(np.uint8), W, S, T)
+    assert (pm[:16] == np.uint64(0xFFF00000FFF00000)).all() and (pm[16:] == 0).all() and (pb == 0).all()
+    x = inst.data.reshape(-1)
+    off = oracle.offsets_pos(x, W, pm, pb, S)
+    assert int(off[-1]) == inst.data.shape[0] * 1696
+    assert abs(x.nbytes * 8 / int(off[-1]) - 2048 / 1696) < 1e-12

@@ -15,12 +15,16 @@ ids    500,000,000 int64 ~ U[0,2^24), 5% U[0,2^40)  64    0.999  256   first 1,0
                                                                       the 5% replacement)
 sparse 1,000,000 x 128 fp32, 95% +0, rest |N(0,1)|   32    0.9    128   10,000 distinct rows
 llm16  the llm tensor (same bytes), one bf16/chunk  16    0.97   1024  first 2^20 elements
+mixed  2,000,000 rows x (32 uint32 ids ~ U[0,2^20), 64    0.98   32    100,000 distinct rows
+       then 32 fp32 ~ N(0,1))
 =====  ==========================================  ====  =====  ====  =========================
 
 The first five are the measured configurations; "sparse" is the sparse-feature
 regime of the IBP page's "Risultati" section (a GNN cache whose features are
 mostly exact zeros); "llm16" codes the llm tensor with one bf16 element per
-chunk (W = 16) instead of four.  gnn, dlrm and sparse rows are one segment each (S = one row) and are read back by gathers:
+chunk (W = 16) instead of four; "mixed" is a feature table whose rows put
+categorical ids before dense features, so which bits are invariant depends on
+the chunk's position in the row (the case per-position metadata is for).  gnn, dlrm and sparse rows are one segment each (S = one row) and are read back by gathers:
 65,536 uniform row ids per step (gnn) and 32,768 Zipf(1.05) row ids per step (dlrm).
 ``scale`` shrinks the row/element counts (same distributions) for CPU-sized tests.
 All randomness comes from ``gen.c`` (counter-based SplitMix64), keyed by
@@ -80,6 +84,7 @@ def _load():
         L.gen_sample_rows.argtypes = [u64, u64, u64, vp]
         L.gen_sample_rows.restype = ctypes.c_int
         L.gen_uniform_ids.argtypes = [u64, u64, u64, vp]
+        L.gen_feature_rows.argtypes = [u64, u64, uint, uint, uint, vp]
         L.gen_zipf_ids.argtypes = [u64, u64, dbl, u64, vp]
         L.gen_zipf_ids.restype = ctypes.c_int
         L.gen_take_rows.argtypes = [vp, u64, vp, u64, vp]
@@ -124,12 +129,14 @@ WORKLOADS = {
                        32, 0.9, 128, "float32", 128, 65536),
     "llm16": Workload(7, "llm16", "LLM gradient buffer (the llm tensor) coded per element: 2^30 bf16, W=16", 16, 0.97,
                       1024, "uint16", 0, 0, 1e-3),
+    "mixed": Workload(8, "mixed", "Feature rows: 2,000,000 x (32 uint32 ids ~ U[0, 2^20), then 32 fp32 ~ N(0,1))", 64,
+                      0.98, 32, "uint32", 64, 0),
 }
 
 FULL_SIZE = {"tiny": 262_144, "gnn": 1_000_000, "dlrm": 10_000_000, "llm": 1 << 30, "ids": 500_000_000,
-             "sparse": 1_000_000, "llm16": 1 << 30}
+             "sparse": 1_000_000, "llm16": 1 << 30, "mixed": 2_000_000}
 SAMPLE_SIZE = {"tiny": 4096, "gnn": 10_000, "dlrm": 100_000, "llm": 1 << 20, "ids": 1_000_000, "sparse": 10_000,
-               "llm16": 1 << 20}
+               "llm16": 1 << 20, "mixed": 100_000}
 
 
 @dataclass
@@ -155,7 +162,7 @@ def size_at(name: str, scale: float) -> int:
     n = int(FULL_SIZE[name] * scale)
     if name in ("llm", "llm16"):
         n -= n % 4  # whole 64-bit chunks of bf16 (llm16 codes the same tensor)
-    return max(n, 1 if name in ("gnn", "dlrm", "sparse") else 64)
+    return max(n, 1 if name in ("gnn", "dlrm", "sparse", "mixed") else 64)
 
 
 def generate(name: str, scale: float = 1.0) -> Instance:
@@ -178,6 +185,9 @@ def generate(name: str, scale: float = 1.0) -> Instance:
     elif name == "sparse":
         data = np.empty((n, w.row_elems), np.float32)
         L.gen_sparse_abs_normal_f32(k_data, data.size, 0.05, data.ctypes.data)
+    elif name == "mixed":
+        data = np.empty((n, w.row_elems), np.uint32)
+        L.gen_feature_rows(k_data, n, 32, 32, 20, data.ctypes.data)
     elif name in ("llm", "llm16"):
         data = np.empty(n, np.uint16)
         L.gen_bf16_grad(key(WORKLOADS["llm"].seed, 1), n, 1e-3, 1e-3, data.ctypes.data)
@@ -191,7 +201,7 @@ def generate(name: str, scale: float = 1.0) -> Instance:
         return Instance(w, data, sample, None)
     else:
         raise KeyError(name)
-    # gather workloads: distinct uniformly sampled rows, copied contiguously
+    # row workloads: distinct uniformly sampled rows, copied contiguously
     m = min(max(int(SAMPLE_SIZE[name] * scale), 1), n) if scale < 1 else SAMPLE_SIZE[name]
     rows = np.empty(m, np.int64)
     rc = L.gen_sample_rows(key(w.seed, 3), n, m, rows.ctypes.data)

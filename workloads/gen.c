@@ -1,7 +1,8 @@
 /*
  * gen.c -- seeded synthetic inputs for the IBP workloads (GNN feature cache,
  * DLRM embedding table, LLM gradient buffer, integer id stream, a small fp32
- * gradient tensor) and their sample / gather index sets.
+ * gradient tensor, mixed id/dense feature rows) and their sample / gather index
+ * sets.
  *
  * Holds no codec arithmetic: random numbers and value distributions only.  Both
  * the GPU path and the CPU oracle consume the bytes produced here.
@@ -85,6 +86,25 @@ void gen_bf16_grad(uint64_t key, uint64_t n, double sigma, double p_out, uint16_
   for (int64_t i = 0; i < (int64_t)n; ++i) {
     const double z = u01(k_sel, (uint64_t)i) < p_out ? normal(k_out, (uint64_t)i) : normal(key, (uint64_t)i) * sigma;
     out[i] = f32_to_bf16_rne((float)z);
+  }
+}
+
+/* Feature rows of a recommender's input: each row holds n_ids categorical ids
+ * ~ U[0, 2^id_bits) as uint32, then n_dense dense features fp32(N(0,1)), all as
+ * 32-bit words (a float's bits); 1 <= id_bits <= 32. */
+void gen_feature_rows(uint64_t key, uint64_t nrows, unsigned n_ids, unsigned n_dense, unsigned id_bits,
+                      uint32_t *out) {
+  const uint64_t k_dense = gen_key(key, 1);
+  const uint64_t row = (uint64_t)n_ids + n_dense;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < (int64_t)nrows; ++r) {
+    uint32_t *o = out + (uint64_t)r * row;
+    for (unsigned j = 0; j < n_ids; ++j)
+      o[j] = (uint32_t)(gen_u64(key, (uint64_t)r * n_ids + j) >> (64 - id_bits));
+    for (unsigned j = 0; j < n_dense; ++j) {
+      const float f = (float)normal(k_dense, (uint64_t)r * n_dense + j);
+      memcpy(&o[n_ids + j], &f, 4);
+    }
   }
 }
 
