@@ -348,6 +348,38 @@ __device__ __forceinline__ uint32_t pos_segment(uint32_t S, const uint4 *tab, ui
   return pos_row1<T, kShift>(S, tab, n, stg, lb, le, o, lane);
 }
 
+// ------------------------------------------------------------------ S dividing 64
+
+// S divides 64 and every segment of the tile is whole: a pass of 64 chunks holds
+// 64/S whole segments, so a lane's saved bits are the wave scan less its value just
+// before the segment's first lane (no segment continues into the next pass).
+template <typename T, bool kShift>
+__device__ __forceinline__ uint32_t pos_small(const DecodeArgs &a, const uint4 *tab, uint32_t n, const uint32_t *stg,
+                                              const uint32_t *lbeg, const uint32_t *lend, uint32_t nch, T *out,
+                                              uint32_t lane) {
+  constexpr uint32_t W = sizeof(T) * 8;
+  const uint32_t i = lane & (a.S - 1u);  // position in the segment
+  const uint32_t first = lane - i;       // the segment's first lane
+  uint32_t err = 0;
+  for (uint32_t p0 = 0; p0 < nch; p0 += kWave) {
+    const uint32_t cl = p0 + lane;
+    const uint32_t lb = cl < nch ? lbeg[cl >> a.s_log2] : kBad;  // lanes past the tile: whole segments too
+    const bool ok = lb != kBad;
+    const bool h = ok && lds_bit(stg, lb + i);
+    const uint32_t pci = ok ? pos_pc<T>(tab, n, i) : 0u;
+    const uint32_t sv = h ? pci : 0u;
+    const uint32_t x = wave_incl_scan(sv);
+    const uint32_t xs = __shfl(x, first == 0u ? 0u : first - 1u, kWave);
+    const uint32_t pos = ok ? lb + a.S + i * W - (x - sv - (first == 0u ? 0u : xs)) : 0u;
+    const T xv = lds_field<T>(stg, pos);
+    if (ok) {
+      store_nt(&out[cl], h ? pos_apply<T, kShift>(tab, n, i, xv) : xv);
+      if (i == a.S - 1u && pos + (h ? W - pci : W) != lend[cl >> a.s_log2]) err |= IBP_DEVERR_CORRUPT;
+    }
+  }
+  return err;
+}
+
 // ------------------------------------------------------------------ any S
 
 // Per pass of 64 tile chunks: the savings scan, less the part before the
@@ -427,6 +459,9 @@ __global__ void __launch_bounds__(pos_block<sizeof(T) * 8>()) decode_pos_kernel(
           err |= shift ? pos_segment<T, true>(a.S, tab, n, stg, lb, le, o, lane)
                        : pos_segment<T, false>(a.S, tab, n, stg, lb, le, o, lane);
         }
+      } else if (kWave % a.S == 0 && nch == nu * a.S) {
+        err |= shift ? pos_small<T, true>(a, tab, n, stg, lbeg, lend, nch, out, lane)
+                     : pos_small<T, false>(a, tab, n, stg, lbeg, lend, nch, out, lane);
       } else {
         err |= shift ? pos_general<T, true>(a, tab, n, stg, lbeg, lend, carry, nu, nch, out, lane)
                      : pos_general<T, false>(a, tab, n, stg, lbeg, lend, carry, nu, nch, out, lane);

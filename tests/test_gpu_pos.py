@@ -56,7 +56,7 @@ def _meta(ibp, dev, W, S, masks, bitvals):
 
 
 @pytest.mark.parametrize("W", [16, 32, 64])
-@pytest.mark.parametrize("S", [1, 3, 32, 64, 100, 128, 192, 256, 1000, 1024])
+@pytest.mark.parametrize("S", [1, 3, 8, 16, 32, 64, 100, 128, 192, 256, 1000, 1024])
 def test_pos_compress_decompress_parity(ibp, W, S):
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(31 * W + S)
@@ -99,9 +99,12 @@ def _data_rows(rng, n, W, masks, bitvals, S, p):
 # n above what four times the resident workgroups cover in one sweep (the grid is
 # capped there and each workgroup loops over tiles), for the paths: W = 16 pairs
 # with shift steps, W = 32 any S, W = 64 one chunk per lane; the smaller cases add
-# the W = 16 one-per-lane and W = 32 pair paths and a W = 64 S of one tile per wave.
+# the W = 16 one-per-lane and W = 32 pair paths, a W = 64 S of one tile per wave, and
+# W = 64 with S dividing 64 (whole segments per pass; the ragged last tile takes the
+# general path).
 @pytest.mark.parametrize("W,S,n", [(16, 1024, (1 << 25) + 77), (32, 100, 20_000_077), (64, 256, (1 << 24) + 77),
-                                   (16, 64, 1_000_077), (32, 256, 1_000_077), (64, 1000, 1_000_077)])
+                                   (16, 64, 1_000_077), (32, 256, 1_000_077), (64, 1000, 1_000_077),
+                                   (64, 32, 2_000_077)])
 def test_pos_decode_many_tiles(ibp, W, S, n):
     """Large inputs (each workgroup loops over many tiles): the decode of the
     oracle's stream equals the input, and so do decodes into outputs one and two
