@@ -197,7 +197,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       const uint32_t sv = h ? popc(m) : 0u;
       const uint32_t x = wave_incl_scan(sv);
       svx[q] = x - sv;
-      wpre[cl] = (uint16_t)x;
+      // segments of a multiple of 64 chunks start on a block, so the per-chunk
+      // prefix is neither needed nor allocated there
+      if constexpr (kMode != kModeLargeS) wpre[cl] = (uint16_t)x;
       if (lane == kWave - 1) bal[q * kWaves + wave] = x;  // the block's saved bits
     } else {
       B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
@@ -237,9 +239,11 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     return pref[b] + (o ? popc(bal[b] & low_lanes(o)) : 0u);
   };
   // bits saved by the matching chunks among tile chunks [0, x), any x < tile size
+  // (position metadata with S a multiple of 64: segment starts only)
   auto cost = [&](uint32_t x) -> uint32_t {
     if constexpr (kPos) {
       const uint32_t b = x >> 6, o = x & 63u;
+      if constexpr (kMode == kModeLargeS) return pref[b];  // x is a segment start: o == 0
       return pref[b] + (o ? (uint32_t)wpre[x - 1] : 0u);
     } else {
       return pc * g(x);
@@ -596,8 +600,9 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   size_t shmem = (size_t)a.obuf_dw * 4 + (tile / kWave) * 8 + ((tile / kWave) + 2) * 4;
   if (a.obuf_dw % 4 != 0) return hipErrorInvalidValue;
   if (a.pmask) {
-    // position tables and per-chunk saved-bit prefixes
-    shmem += (size_t)a.S * 16 + (size_t)tile * 2;
+    // position tables and per-chunk saved-bit prefixes (not for S a multiple of 64,
+    // whose segments start on 64-chunk blocks)
+    shmem += (size_t)a.S * 16 + (a.S % kWave == 0 ? 0 : (size_t)tile * 2);
     if (p.W == 16) return launch_encode_pos_w<uint16_t>(a, p, shmem, s);
     return p.W == 32 ? launch_encode_pos_w<uint32_t>(a, p, shmem, s) : launch_encode_pos_w<uint64_t>(a, p, shmem, s);
   }
