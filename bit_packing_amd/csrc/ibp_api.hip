@@ -291,7 +291,7 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   // whole 64-chunk blocks and the input allows it
   a.pair = (p.W == 16 && !pmask && S % kWave == 0 && aligned(d_in, 4)) ? 1u : 0u;
   a.halves = n >= g_halves_min.load() ? enc_halves(pmask != nullptr, a.pair != 0u, p.W, S) : 1u;
-  a.big = enc_big(p.W, a.halves, p.pc) ? 1u : 0u;
+  a.big = !pmask && enc_big(p.W, a.halves, p.pc) ? 1u : 0u;
   a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W, a.halves, a.big != 0u);
   a.ntiles = (nseg + a.G - 1) / a.G;  // at most the workspace's tile count (its tiles are the smallest)
   a.tails = a.status + a.ntiles;
@@ -301,7 +301,7 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   a.S = S;
   a.s_log2 = log2_if_pow2(S);
   a.tile_chunks = a.G * S;
-  if (a.halves == 2 && a.tile_chunks != enc_tile_chunks(false, false, p.W, 2, a.big != 0u))
+  if (a.halves == 2 && a.tile_chunks != enc_tile_chunks(pmask != nullptr, false, p.W, 2, a.big != 0u))
     return IBP_ERR_INVALID_ARG;
   // image (one half's when halves == 2) from the 16-byte block of the first bit
   a.obuf_dw = ((127 + a.tile_chunks / a.halves * (p.W + 1) + 31) / 32 + 2 + 3) & ~3u;

@@ -79,11 +79,11 @@ __device__ __forceinline__ uint64_t interleave32(uint32_t e, uint32_t o) {
 // The pair form asks for 8 wavefronts per SIMD (its 16 unrolled passes otherwise
 // take enough scalar registers to allow only 7: 1.28 -> 1.11 ms per 2^30 chunks).
 template <typename T, uint32_t kMode, uint32_t NR, bool kPos, bool kPair = false, uint32_t kHalves = 1, bool kBig = false>
-__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair || kHalves == 2) ? 8 : 1)
+__global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair || (kHalves == 2 && !kPos)) ? 8 : 1)
     encode_kernel(EncodeArgs a, CodecParams p) {
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
-  static_assert(kHalves == 1 || (!kPos && !kPair && kMode != kModeGeneral), "halves: one Mask, S a power of two");
+  static_assert(kHalves == 1 || (!kPair && kMode != kModeGeneral), "halves: S a power of two");
   static_assert(!kBig || (kHalves == 2 && sizeof(T) == 8), "1024-thread tiles: 64-bit chunks in halves");
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = enc_threads(kPos, W, kBig);
@@ -348,9 +348,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
         const uint32_t gs = uniform(pref[s0 >> 6]);
         const uint32_t m = min(a.S, nch - s0);
         const uint32_t segbase = s0 * (W + 1) - gs;
-        if (lane == 0) lds_or_field(obuf, segbase + (cb - s0), B[q]);  // 64 header bits
+        if (lane == 0) lds_or_field(obuf, segbase + (cb - s0) - H, B[q]);  // 64 header bits
         const uint32_t c_cl = uniform(pref[blk]) + svx[q];
-        if (valid) lds_or_field(obuf, segbase + m + (cl - s0) * W - (c_cl - gs), payload());
+        if (valid) lds_or_field(obuf, segbase + m + (cl - s0) * W - (c_cl - gs) - H, payload());
       } else {
         const uint32_t s0 = seg_start(cb);
         const uint32_t m = min(a.S, nch - s0);
@@ -364,9 +364,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       if constexpr (kPos) {
         const uint32_t gs = cost(min(s0, nch - 1u));
         const uint32_t segbase = s0 * (W + 1) - gs;
-        if (valid && i_lane == 0) lds_or_field(obuf, segbase, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
+        if (valid && i_lane == 0) lds_or_field(obuf, segbase - H, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
         const uint32_t c_cl = uniform(pref[blk]) + svx[q];
-        if (valid) lds_or_field(obuf, segbase + m + i_lane * W - (c_cl - gs), payload());
+        if (valid) lds_or_field(obuf, segbase + m + i_lane * W - (c_cl - gs) - H, payload());
       } else {
         const uint32_t gs = pc * (pref_at(q * kWaves, 1u) + popc(B[q] & seg_below));
         if (valid && i_lane == 0)
@@ -507,7 +507,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   } else {
     // a tile larger than the buffer holds more than kTile / 2 chunks, so it has two
     // halves; the first half's segments end at chunk kTile / 2
-    const uint64_t agg0 = (uint64_t)(kTile / 2) * (W + 1) - (uint64_t)pc * pref[kBal / 2];
+    const uint64_t agg0 = (uint64_t)(kTile / 2) * (W + 1) - (uint64_t)cost(kTile / 2);
     store(excl, agg0, false, true, 0u);
     __syncthreads();  // the first half's image has been read
     for (uint32_t d = 4 * tid; d < a.obuf_dw; d += 4 * kThreads)
@@ -530,17 +530,17 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  if constexpr (sizeof(T) >= 4 && !kPos && !kPair && M != kModeGeneral) {
+  if constexpr (sizeof(T) >= 4 && !kPair && M != kModeGeneral) {
     if (a.halves == 2) {
-      if constexpr (sizeof(T) == 8) {
+      if constexpr (sizeof(T) == 8 && !kPos) {
         if (a.big) {
           hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2, true>), dim3((uint32_t)a.ntiles),
                              dim3(enc_threads(false, 64, true)), shmem, s, a, p);
           return hipGetLastError();
         }
       }
-      hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2>), dim3((uint32_t)a.ntiles),
-                         dim3(enc_threads(false, sizeof(T) * 8)), shmem, s, a, p);
+      hipLaunchKernelGGL((encode_kernel<T, M, NR, kPos, false, 2>), dim3((uint32_t)a.ntiles),
+                         dim3(enc_threads(kPos, sizeof(T) * 8)), shmem, s, a, p);
       return hipGetLastError();
     }
   }

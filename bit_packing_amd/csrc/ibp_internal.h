@@ -33,9 +33,13 @@ constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t hal
 // one for four.  32-bit chunks: 16384-chunk tiles (32 per thread) through the
 // image of 8192, so a tile moves 64 KB of input, as at W = 64, with half the
 // look-backs per byte of 8192-chunk tiles.  A tile whose stream fits the half-size
-// image is packed whole before its look-back and stored once.
+// image is packed whole before its look-back and stored once.  Position metadata
+// takes the same form at W = 64 (same tile, half the image: the registers, not the
+// LDS, then bound the workgroups per CU; ids 2.00 -> 1.79 ms, llm 1.38 -> 1.29 ms,
+// S = 32 feature rows 0.345 -> 0.305 ms); at W = 32 its two-half kernels need 139+
+// VGPRs, while the one-image ones already fit six waves per SIMD.
 inline uint32_t enc_halves(bool pos, bool pair, uint32_t W, uint32_t S) {
-  return (W == 64 || W == 32) && !pos && !pair && S != 0 && (S & (S - 1)) == 0 ? 2u : 1u;
+  return (W == 64 || (W == 32 && !pos)) && !pair && S != 0 && (S & (S - 1)) == 0 ? 2u : 1u;
 }
 // A tile saves at most popcount(Mask) bits per chunk, so only when popcount(Mask) >
 // (W + 1) / 2 can a whole tile fit the half-size image.  For such 64-bit chunks the

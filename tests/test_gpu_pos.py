@@ -67,14 +67,21 @@ def test_pos_compress_decompress_parity(ibp, W, S):
         say(f"pos W={W} S={S} n={n}")
         v = _data(rng, n, W, masks, bitvals, S)
         x = torch.from_numpy(v.view(np.uint8).copy()).to(dev)
-        comp = ibp.ibp_compress_pos(meta, x, err=err)
         ref_stream, ref_off = oracle.encode_pos(v, W, masks, bitvals, S)
-        assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off), f"n={n}: offsets"
         nb = ref_stream.size
-        got = comp.stream[:nb].cpu().numpy()
-        if not np.array_equal(got, ref_stream):
-            bad = int(np.nonzero(got != ref_stream)[0][0])
-            raise AssertionError(f"n={n}: stream differs first at byte {bad} of {nb}")
+        # both compression tile forms: the size-chosen one, and the two-half tiles
+        # forced on this small input (threshold 0; W = 64 with S a power of two)
+        for form, threshold in (("default tiles", 0xFFFFFFFFFFFFFFFF), ("two-half tiles", 0)):
+            ibp.ibp_set_halves_min_chunks(threshold)
+            try:
+                comp = ibp.ibp_compress_pos(meta, x, err=err)
+            finally:
+                ibp.ibp_set_halves_min_chunks(0xFFFFFFFFFFFFFFFF)
+            assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off), f"n={n}, {form}: offsets"
+            got = comp.stream[:nb].cpu().numpy()
+            if not np.array_equal(got, ref_stream):
+                bad = int(np.nonzero(got != ref_stream)[0][0])
+                raise AssertionError(f"n={n}, {form}: stream differs first at byte {bad} of {nb}")
         out = ibp.ibp_decompress_pos(meta, comp.stream, comp.offsets, n, err=err)
         assert torch.equal(out, x), f"n={n}: round trip"
         s2 = torch.from_numpy(ref_stream.copy()).to(dev)
