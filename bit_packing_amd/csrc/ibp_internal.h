@@ -26,9 +26,10 @@ constexpr uint32_t enc_threads(bool pos, uint32_t W, bool big = false) {
 constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t halves = 1, bool big = false) {
   return (pair || (halves == 2 && W == 32) ? 32u : 16u) * enc_threads(pos, W, big);
 }
-// A compression tile of 32- or 64-bit chunks with one Mask and S a power of two is
-// packed and stored in two halves (segments end at the middle) through an LDS
-// image of half the size.  64-bit chunks: 8192-chunk tiles, whose full-size image
+// From 2^23 chunks on (ibp_set_halves_min_chunks; smaller launches do not fill the
+// GPU and finish sooner with one-image tiles), a compression tile of 32- or 64-bit
+// chunks with one Mask and S a power of two is packed and stored in two halves
+// (segments end at the middle) through an LDS image of half the size.  64-bit chunks: 8192-chunk tiles, whose full-size image
 // (8192 chunks x 65 bits) would leave room for two workgroups per CU, the half-size
 // one for four.  32-bit chunks: 16384-chunk tiles (32 per thread) through the
 // image of 8192, so a tile moves 64 KB of input, as at W = 64, with half the
