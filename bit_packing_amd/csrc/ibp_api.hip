@@ -75,7 +75,8 @@ bool total_fits(uint64_t n_chunks, uint32_t W) {
 }
 
 uint32_t meta_blocks(uint64_t n) {
-  const uint64_t want = (n + (uint64_t)kBlock * 16 - 1) / ((uint64_t)kBlock * 16);
+  // about four samples per thread: one round of four in-flight steps per wavefront
+  const uint64_t want = (n + (uint64_t)kMetaThreads * 4 - 1) / ((uint64_t)kMetaThreads * 4);
   return (uint32_t)(want < 1 ? 1 : (want > kMetaMaxBlocks ? kMetaMaxBlocks : want));
 }
 

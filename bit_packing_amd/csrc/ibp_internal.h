@@ -55,6 +55,7 @@ constexpr uint32_t kDecMaxUnits = 128;
 constexpr uint32_t kGatherMaxRows = 8;   // rows per wavefront of a gather from HBM
 // Metadata count kernel: at most this many workgroups (one per CU) write partial counts.
 constexpr uint32_t kMetaMaxBlocks = 256;
+constexpr uint32_t kMetaThreads = 1024;  // threads per workgroup of the one-count kernel
 
 // Status words of the compression look-back: 2-bit flag above a 62-bit value.
 constexpr uint64_t kFlagAggregate = 1ull << 62;

@@ -17,22 +17,23 @@ using namespace dev;
 // lanes is column b of the step's 64 x W bit matrix, and its popcount goes to a
 // wave-uniform counter.  The counters stay scalar, so no wavefront ends with W
 // shuffle reductions (2^20-chunk sample of 64-bit ids: 23.1 -> 18.0 us; 10,000
-// 512-byte rows: 15.7 -> 12.7 us).  A workgroup sums its wavefronts' counters into
-// one row of partials.  A wavefront
-// counts at most ceil(n / (kMetaMaxBlocks * kWavesPerBlock)) samples, below 2^32 for
-// any sample that fits in memory.
+// 512-byte rows: 15.7 -> 12.7 us).  Workgroups of kMetaThreads threads, so that the
+// at most kMetaMaxBlocks workgroups (one row of partials each) still give every SIMD
+// several wavefronts.  A wavefront counts at most ceil(n / (kMetaMaxBlocks *
+// kMetaThreads / 64)) samples, below 2^32 for any sample that fits in memory.
 template <typename T>
-__global__ void __launch_bounds__(kBlock) count_ones_kernel(MetaArgs a) {
+__global__ void __launch_bounds__(kMetaThreads) count_ones_kernel(MetaArgs a) {
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kU = 4;  // steps whose loads are in flight together
-  __shared__ uint32_t red[kWavesPerBlock][W];
+  constexpr uint32_t kWaves = kMetaThreads / kWave;
+  __shared__ uint32_t red[kWaves][W];
   const T *in = static_cast<const T *>(a.in);
   const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWave);
   uint32_t c[W];  // wave-uniform
 #pragma unroll
   for (uint32_t b = 0; b < W; ++b) c[b] = 0;
-  const uint64_t step = (uint64_t)gridDim.x * kBlock;  // samples per step of all wavefronts
-  for (uint64_t base = ((uint64_t)blockIdx.x * kWavesPerBlock + wave) * kWave; base < a.n; base += kU * step) {
+  const uint64_t step = (uint64_t)gridDim.x * kMetaThreads;  // samples per step of all wavefronts
+  for (uint64_t base = ((uint64_t)blockIdx.x * kWaves + wave) * kWave; base < a.n; base += kU * step) {
     T v[kU];
 #pragma unroll
     for (uint32_t u = 0; u < kU; ++u) {
@@ -52,7 +53,7 @@ __global__ void __launch_bounds__(kBlock) count_ones_kernel(MetaArgs a) {
   __syncthreads();
   if (threadIdx.x < W) {
     uint64_t s = 0;
-    for (uint32_t w = 0; w < kWavesPerBlock; ++w) s += red[w][threadIdx.x];
+    for (uint32_t w = 0; w < kWaves; ++w) s += red[w][threadIdx.x];
     a.partial[(uint64_t)blockIdx.x * W + threadIdx.x] = s;
   }
 }
@@ -150,11 +151,11 @@ hipError_t launch_meta_pos(const MetaArgs &a, uint32_t S, uint64_t *d_mask, uint
 hipError_t launch_meta(const MetaArgs &a, hipStream_t s) {
   if (a.n) {
     if (a.W == 16)
-      hipLaunchKernelGGL(count_ones_kernel<uint16_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL(count_ones_kernel<uint16_t>, dim3(a.blocks), dim3(kMetaThreads), 0, s, a);
     else if (a.W == 32)
-      hipLaunchKernelGGL(count_ones_kernel<uint32_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL(count_ones_kernel<uint32_t>, dim3(a.blocks), dim3(kMetaThreads), 0, s, a);
     else
-      hipLaunchKernelGGL(count_ones_kernel<uint64_t>, dim3(a.blocks), dim3(kBlock), 0, s, a);
+      hipLaunchKernelGGL(count_ones_kernel<uint64_t>, dim3(a.blocks), dim3(kMetaThreads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
