@@ -530,7 +530,8 @@ static inline uint64_t host_min(uint64_t x, uint64_t y) { return x < y ? x : y; 
 
 template <typename T, uint32_t M, uint32_t NR, bool kPos = false, bool kPair = false>
 static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, size_t shmem, hipStream_t s) {
-  if constexpr (sizeof(T) >= 4 && !kPair && M != kModeGeneral) {
+  // two-half tiles: 32-bit chunks with one Mask, 64-bit chunks (enc_halves)
+  if constexpr (sizeof(T) >= 4 && !kPair && M != kModeGeneral && !(kPos && sizeof(T) == 4)) {
     if (a.halves == 2) {
       if constexpr (sizeof(T) == 8 && !kPos) {
         if (a.big) {

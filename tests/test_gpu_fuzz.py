@@ -116,7 +116,13 @@ def test_random_single_mask(ibp, seed):
 @pytest.mark.parametrize("seed", range(1000, 1128))
 def test_random_position_tables(ibp, seed):
     rng, W, S, n, p = _case(seed)
-    masks = np.array([_rand_mask(rng, W) for _ in range(S)], np.uint64)
+    if seed % 3 == 0:
+        # every position's invariant bits at the top (its free bits one run from bit 0)
+        full = (1 << W) - 1
+        ks = rng.integers(0, W + 1, S)
+        masks = np.array([(full >> (W - int(k))) << (W - int(k)) if k else 0 for k in ks], np.uint64)
+    else:
+        masks = np.array([_rand_mask(rng, W) for _ in range(S)], np.uint64)
     bitvals = np.array([int(_rand_words(rng, 1, W)[0]) & int(m) for m in masks], np.uint64)
     say(f"fuzz pos {seed}: W={W} S={S} n={n} p={p}")
     dev = torch.device("cuda:0")
