@@ -147,12 +147,20 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     *reinterpret_cast<uint4 *>(obuf + d) = make_uint4(0u, 0u, 0u, 0u);
   uint32_t ip[kQ];   // kPos: position of chunk q * kThreads + tid in its segment (tiles start on a segment)
   uint32_t svx[kQ];  // kPos: saved bits of the earlier chunks of its 64-chunk block
+  // kPos: whether some position's free bits are not one run from bit 0 (per 32-bit
+  // half at W = 64).  When none is, a matching chunk's payload is its value AND its
+  // free bits; the packing passes are instantiated for both cases, chosen once.
+  bool multi = false;
   if constexpr (kPos) {
     const uint64_t full = W >= 64 ? ~0ull : ((1ull << W) - 1ull);
+    int mine = 0;
     for (uint32_t i = tid; i < a.S; i += kThreads) {
       const uint64_t m = a.pmask[i] & full;
       mtab[i] = m;
       btab[i] = a.pbitval[i] & m;
+      const uint64_t F = ~m & full;
+      const uint32_t Flo = (uint32_t)F, Fhi = (uint32_t)(F >> 32);
+      if ((Flo & (Flo + 1u)) != 0u || (Fhi & (Fhi + 1u)) != 0u) mine = 1;
     }
     const uint32_t step = kThreads % a.S;
     uint32_t i0 = tid % a.S;
@@ -162,7 +170,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       i0 += step;
       if (i0 >= a.S) i0 -= a.S;
     }
-    __syncthreads();
+    multi = uniform((uint32_t)__syncthreads_or(mine)) != 0u;
   }
   uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
   // kPair: participation of the even and of the odd chunk of pass q's pair (taken
@@ -315,7 +323,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   // the passes of half h of the tile (kHalves == 2: the tile's two halves of
   // kTile / 2 chunks are packed and stored one after the other through an image of
   // half the size, whose bit 0 is the half's first bit, tile image bit H)
-  auto pack = [&](auto hc, uint32_t H) {
+  auto pack_form = [&](auto hc, uint32_t H, auto mc) __attribute__((always_inline)) {
   constexpr uint32_t qb = decltype(hc)::value * (kQ / kHalves), qe = qb + kQ / kHalves;
 #pragma unroll
   for (uint32_t q = qb; q < (kPair ? 0u : qe); ++q) {
@@ -331,11 +339,20 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
         if (!h) return v[q];
         const uint64_t F = ~mtab[ip[q]];
         const uint32_t Flo = (uint32_t)F, Fhi = (uint32_t)(F >> 32);
-        const uint64_t lo = extract_runs<uint32_t>((uint32_t)v[q], Flo);
-        const uint64_t hi = extract_runs<uint32_t>((uint32_t)((uint64_t)v[q] >> 32), Fhi);
+        uint64_t lo, hi;
+        if constexpr (decltype(mc)::value) {
+          lo = extract_runs<uint32_t>((uint32_t)v[q], Flo);
+          hi = extract_runs<uint32_t>((uint32_t)((uint64_t)v[q] >> 32), Fhi);
+        } else {
+          lo = (uint32_t)v[q] & Flo;
+          hi = (uint32_t)((uint64_t)v[q] >> 32) & Fhi;
+        }
         return (T)(lo | (hi << __builtin_popcount(Flo)));
       } else if constexpr (kPos) {
-        return h ? (T)extract_runs<uint32_t>((uint32_t)v[q], (uint32_t)(~mtab[ip[q]] & low_lanes(W))) : v[q];
+        if (!h) return v[q];
+        const uint32_t F = (uint32_t)(~mtab[ip[q]] & low_lanes(W));
+        if constexpr (decltype(mc)::value) return (T)extract_runs<uint32_t>((uint32_t)v[q], F);
+        else return (T)((uint32_t)v[q] & F);
       } else {
         return h ? extract_free<T, NR>(v[q], p.runs) : v[q];
       }
@@ -397,6 +414,15 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6] - H, hdr);
     }
   }
+  };
+  // one copy of the passes per extraction form; multi is uniform
+  auto pack = [&](auto hc, uint32_t H) __attribute__((always_inline)) {
+    if constexpr (kPos) {
+      if (multi) pack_form(hc, H, std::true_type{});
+      else pack_form(hc, H, std::false_type{});
+    } else {
+      pack_form(hc, H, std::true_type{});
+    }
   };
   // kHalves == 2: a tile whose whole image fits the half-size buffer (at most the
   // size of half a tile stored raw) is packed entirely before the look-back and
