@@ -216,7 +216,8 @@ IBP_API uint64_t ibp_metadata_workspace_bytes(uint64_t n_sample_chunks, uint32_t
 
 IBP_API uint64_t ibp_compress_workspace_bytes(uint64_t n_chunks, uint32_t S) {
   if (S == 0) return 0;
-  return 8 + 16 * enc_tiles(n_chunks, S, true, false, 32);  // the smallest tiles (position metadata, W > 16)
+  const uint64_t t = enc_tiles(n_chunks, S, true, false, 32);  // the smallest tiles (position metadata, W > 16)
+  return 8 + 8 * (status_words(t) + t);  // control, status words, hand-over words
 }
 
 IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, uint32_t W, double T,
@@ -295,7 +296,8 @@ static int compress_common(const CodecParams &p, const uint64_t *pmask, const ui
   a.big = !pmask && enc_big(p.W, a.halves, p.pc) ? 1u : 0u;
   a.G = enc_segs_per_tile(S, pmask != nullptr, a.pair != 0u, p.W, a.halves, a.big != 0u);
   a.ntiles = (nseg + a.G - 1) / a.G;  // at most the workspace's tile count (its tiles are the smallest)
-  a.tails = a.status + a.ntiles;
+  a.st_lg = status_lg(a.ntiles);
+  a.tails = a.status + status_words(a.ntiles);
   a.err = d_err_word;
   a.n_chunks = n;
   a.nseg = nseg;
@@ -641,7 +643,10 @@ IBP_API int ibp_zip_table_from_sigma(double sigma, uint8_t *table_out) {
 
 IBP_API uint64_t ibp_zip_blocks(uint64_t n) { return (n + kZipBlock - 1) / kZipBlock; }
 IBP_API uint64_t ibp_zip_codes_bytes(uint64_t n) { return ibp_zip_blocks(n) * (3 * kZipBlock / 8); }
-IBP_API uint64_t ibp_zip_workspace_bytes(uint64_t n) { return 8 + 8 * ibp_zip_blocks(n); }
+IBP_API uint64_t ibp_zip_workspace_bytes(uint64_t n) {
+  // control word, then the look-back status words of the compressor's workgroups
+  return n ? 8 + 8 * status_words((ibp_zip_blocks(n) + kZipWG - 1) / kZipWG) : 8;
+}
 
 static bool zip_table_ok(const uint8_t *t) {
   if (!t) return false;
@@ -681,6 +686,7 @@ IBP_API int ibp_zip_compress(const uint8_t *table, const void *d_in, uint64_t n,
   a.nblk = nblk;
   for (int k = 0; k < 7; ++k) a.table[k] = table[k];
   a.wait_limit = g_wait_limit.load();
+  a.st_lg = status_lg((nblk + kZipWG - 1) / kZipWG);
   return status_of(launch_zip_encode(a, s));
 }
 

@@ -270,8 +270,13 @@ __device__ __forceinline__ void atomic_store_agent32(uint32_t *p, uint32_t v) {
 // it: successors walk past its aggregate to the same unpublished predecessor, and
 // either find it published later (their prefixes are then right) or give up too.
 // lookback_publish: tile t's aggregate agg (tile 0: its inclusive prefix); one thread.
-__device__ inline void lookback_publish(uint64_t *status, uint64_t t, uint64_t agg) {
-  atomic_store_agent(&status[t], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
+// Tile t's status word: word t >> lg of 16-word line t mod 2^lg (status_lg).
+__device__ __forceinline__ uint64_t status_slot(uint64_t t, uint32_t lg) {
+  return ((t & ((1ull << lg) - 1ull)) << 4) | (t >> lg);
+}
+
+__device__ inline void lookback_publish(uint64_t *status, uint32_t lg, uint64_t t, uint64_t agg) {
+  atomic_store_agent(&status[status_slot(t, lg)], (t == 0 ? kFlagPrefix : kFlagAggregate) | agg);
 }
 
 // Summary of one window of 64 status words s (lane 0 the nearest predecessor):
@@ -296,14 +301,14 @@ __device__ inline uint32_t lookback_window(uint64_t s, uint32_t lane, uint64_t &
 // back from base 64 at a time until an inclusive prefix, waiting (bounded) for
 // unpublished predecessors, then publishes tile t's inclusive prefix and returns
 // the exclusive one.
-__device__ inline uint64_t lookback_finish(uint64_t *status, uint32_t *control, uint32_t *err, uint64_t t,
+__device__ inline uint64_t lookback_finish(uint64_t *status, uint32_t lg, uint32_t *control, uint32_t *err, uint64_t t,
                                            int64_t base, uint64_t excl, uint64_t agg, uint32_t wait_limit,
                                            uint32_t lane, bool &timed_out) {
   timed_out = false;
   uint32_t spins = 0;
   while (base >= 0) {
     const int64_t j = base - (int64_t)lane;
-    const uint64_t s = j >= 0 ? atomic_load_agent(&status[j]) : kFlagPrefix;
+    const uint64_t s = j >= 0 ? atomic_load_agent(&status[status_slot((uint64_t)j, lg)]) : kFlagPrefix;
     uint64_t sum;
     const uint32_t st = lookback_window(s, lane, sum);
     if (st == kLbWait) {
@@ -327,7 +332,7 @@ __device__ inline uint64_t lookback_finish(uint64_t *status, uint32_t *control, 
     if (st == kLbPrefix) break;
     base -= 64;
   }
-  if (lane == 0) atomic_store_agent(&status[t], kFlagPrefix | ((excl + agg) & kValueMask));
+  if (lane == 0) atomic_store_agent(&status[status_slot(t, lg)], kFlagPrefix | ((excl + agg) & kValueMask));
   return excl;
 }
 

@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
   static_assert(kHalves == 1 || (!kPair && kMode != kModeGeneral), "halves: S a power of two");
-  static_assert(!kBig || (kHalves == 2 && sizeof(T) == 8), "1024-thread tiles: 64-bit chunks in halves");
+  static_assert(!kBig || (kHalves == 2 && sizeof(T) >= 4), "1024-thread tiles: 32- or 64-bit chunks in halves");
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = enc_threads(kPos, W, kBig);
   constexpr uint32_t kWaves = kThreads / kWave;
@@ -173,6 +173,19 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     multi = uniform((uint32_t)__syncthreads_or(mine)) != 0u;
   }
   uint64_t B[kQ];  // this wavefront's participation ballots, one per pass
+  // One Mask with more than 16 passes (32-bit chunks in 16,384-chunk tiles): pass
+  // q's participation ballot is taken again where it is needed rather than held in
+  // scalar registers (32 ballots do not fit beside the rest and are spilled to
+  // vector-register lanes, four instructions per pass).  The lanes past the
+  // tile's end (a scalar mask; none in a full tile) take no part.
+  constexpr bool kRetake = !kPos && !kPair && kQ > 16;
+  const bool full_tile = nch == kTile;
+  auto match_ballot = [&](uint32_t q) -> uint64_t {
+    const uint64_t b = ballot(((v[q] ^ bitval) & mask) == 0);
+    if (full_tile) return b;
+    const uint32_t base = q * kThreads + wave * kWave;
+    return b & (base >= nch ? 0ull : low_lanes(min(nch - base, kWave)));
+  };
   // kPair: participation of the even and of the odd chunk of pass q's pair (taken
   // again when packing rather than held in scalar registers across the barriers)
   auto even_odd = [&](uint32_t q, bool &h0, bool &h1) {
@@ -210,8 +223,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       if constexpr (kMode != kModeLargeS) wpre[cl] = (uint16_t)x;
       if (lane == kWave - 1) bal[q * kWaves + wave] = x;  // the block's saved bits
     } else {
-      B[q] = ballot(cl < nch && ((v[q] ^ bitval) & mask) == 0);
-      if (lane == 0) bal[q * kWaves + wave] = B[q];
+      const uint64_t b = match_ballot(q);
+      if constexpr (!kRetake) B[q] = b;
+      if (lane == 0) bal[q * kWaves + wave] = b;
     }
   }
   // Every input load has been consumed.  An explicit wait for all vector memory
@@ -261,7 +275,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
 
   // publish the tile's size at once, so successors can look back past it while
   // this tile packs
-  if (tid == 0) lookback_publish(a.status, t, agg);
+  if (tid == 0) lookback_publish(a.status, a.st_lg, t, agg);
 
   // 4. pack into LDS, from bit 0 of the image (the tile's first bit); the store
   //    shifts the image to the tile's place in the stream.  Segment s0's header
@@ -317,7 +331,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       }
       const uint32_t a0 = h0 ? (ext & 0xFFFFu) : (x & 0xFFFFu), a1 = h1 ? (ext >> 16) : (x >> 16);
       const uint32_t field = a0 | (a1 << (h0 ? W - pc : W));
-      lds_or_bits(obuf, c < nch ? pos : 0u, c < nch ? field : 0u);  // lanes past the tile hold 0
+      lds_or_bits(obuf, pos, field);  // lanes past the tile's end hold 0 (chunks read as 0, not matching)
     }
   }
   // the passes of half h of the tile (kHalves == 2: the tile's two halves of
@@ -332,7 +346,8 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     if (cb >= nch) continue;                         // uniform
     const uint32_t cl = cb + lane;
     const bool valid = cl < nch;
-    const bool h = __builtin_amdgcn_inverse_ballot_w64(B[q]);
+    const uint64_t Bq = kRetake ? match_ballot(q) : B[q];
+    const bool h = __builtin_amdgcn_inverse_ballot_w64(Bq);
     auto payload = [&]() -> T {
       if constexpr (kPos && W == 64) {
         // in 32-bit halves: the free bits of the low half come first
@@ -365,15 +380,18 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
         const uint32_t gs = uniform(pref[s0 >> 6]);
         const uint32_t m = min(a.S, nch - s0);
         const uint32_t segbase = s0 * (W + 1) - gs;
-        if (lane == 0) lds_or_field(obuf, segbase + (cb - s0) - H, B[q]);  // 64 header bits
+        if (lane == 0) lds_or_field(obuf, segbase + (cb - s0) - H, Bq);  // 64 header bits
         const uint32_t c_cl = uniform(pref[blk]) + svx[q];
         if (valid) lds_or_field(obuf, segbase + m + (cl - s0) * W - (c_cl - gs) - H, payload());
       } else {
+        // chunk cl's payload bit: a scalar part, the lane's W l, less pc times the
+        // compressed chunks of this block below the lane.  Lanes past the tile's end
+        // hold payload 0 (their chunk reads as 0 and does not match), so they OR
+        // nothing and their position is never used.
         const uint32_t s0 = seg_start(cb);
         const uint32_t m = min(a.S, nch - s0);
-        const uint32_t saved = __umul24(pc, pref_at(q * kWaves, 1u) + count_below(B[q]));
-        const uint32_t pos = (s0 + m + cb * W) + lane_bits - saved - H;
-        lds_or_bits(obuf, valid ? pos : 0u, payload());  // invalid lanes hold 0
+        const uint32_t k = s0 + m + cb * W - pc * pref_at(q * kWaves, 1u) - H;
+        lds_or_bits(obuf, lane_bits + k - __umul24(pc, count_below(Bq)), payload());
       }
     } else if constexpr (kMode == kModeSmallS) {
       const uint32_t s0 = cb + (lane & ~(a.S - 1u));
@@ -381,15 +399,15 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       if constexpr (kPos) {
         const uint32_t gs = cost(min(s0, nch - 1u));
         const uint32_t segbase = s0 * (W + 1) - gs;
-        if (valid && i_lane == 0) lds_or_field(obuf, segbase - H, (uint32_t)((B[q] >> lane) & low_lanes(m)));  // header
+        if (valid && i_lane == 0) lds_or_field(obuf, segbase - H, (uint32_t)((Bq >> lane) & low_lanes(m)));  // header
         const uint32_t c_cl = uniform(pref[blk]) + svx[q];
         if (valid) lds_or_field(obuf, segbase + m + i_lane * W - (c_cl - gs) - H, payload());
       } else {
-        const uint32_t gs = pc * (pref_at(q * kWaves, 1u) + popc(B[q] & seg_below));
+        const uint32_t gs = pc * (pref_at(q * kWaves, 1u) + popc(Bq & seg_below));
         if (valid && i_lane == 0)
-          lds_or_bits(obuf, s0 * (W + 1) - gs - H, (uint32_t)((B[q] >> lane) & low_lanes(m)));
-        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(q * kWaves, 1u) + count_below(B[q])) - H;
-        lds_or_bits(obuf, valid ? pos : 0u, payload());
+          lds_or_bits(obuf, s0 * (W + 1) - gs - H, (uint32_t)((Bq >> lane) & low_lanes(m)));
+        const uint32_t pos = s0 + m + cl * W - __umul24(pc, pref_at(q * kWaves, 1u) + count_below(Bq)) - H;
+        lds_or_bits(obuf, pos, payload());  // lanes past the tile's end hold 0
       }
     } else {
       if (valid) {
@@ -399,7 +417,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
         const uint32_t m = min(a.S, nch - s0);
         const uint32_t segbase = s0 * (W + 1) - gs;
         if (h) atomicOr(&obuf[(segbase + i) >> 5], 1u << ((segbase + i) & 31u));
-        const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : __umul24(pc, uniform(pref[blk]) + count_below(B[q]));
+        const uint32_t c_cl = kPos ? uniform(pref[blk]) + svx[q] : __umul24(pc, uniform(pref[blk]) + count_below(Bq));
         lds_or_field(obuf, segbase + m + i * W - (c_cl - gs), payload());
       }
     }
@@ -438,7 +456,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   if (wave == 0) {
     bool timed_out = false;
     const uint64_t excl = t == 0 ? 0ull
-                                 : lookback_finish(a.status, a.control, a.err, t, (int64_t)t - 1, 0, agg,
+                                 : lookback_finish(a.status, a.st_lg, a.control, a.err, t, (int64_t)t - 1, 0, agg,
                                                    a.wait_limit, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
@@ -559,10 +577,10 @@ static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, siz
   // two-half tiles: 32-bit chunks with one Mask, 64-bit chunks (enc_halves)
   if constexpr (sizeof(T) >= 4 && !kPair && M != kModeGeneral && !(kPos && sizeof(T) == 4)) {
     if (a.halves == 2) {
-      if constexpr (sizeof(T) == 8 && !kPos) {
+      if constexpr (!kPos) {
         if (a.big) {
           hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2, true>), dim3((uint32_t)a.ntiles),
-                             dim3(enc_threads(false, 64, true)), shmem, s, a, p);
+                             dim3(enc_threads(false, sizeof(T) * 8, true)), shmem, s, a, p);
           return hipGetLastError();
         }
       }
@@ -620,7 +638,7 @@ hipError_t launch_encode(const EncodeArgs &a, const CodecParams &p, hipStream_t 
   if (a.ntiles > 0x7FFFFFFFull) return hipErrorInvalidValue;
   // clear the control words, status and hand-over words (a kernel, not a
   // memset node, so the sequence stays valid inside a captured graph)
-  hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 2 * a.ntiles + 1, s);
+  hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 1 + status_words(a.ntiles) + a.ntiles, s);
   if (e != hipSuccess) return e;
   // image, ballots (kBal words), block prefixes (kBal + 1 words, padded to 8 bytes)
   const uint32_t tile = enc_tile_chunks(a.pmask != nullptr, a.pair != 0u, p.W, a.halves, a.big != 0u);

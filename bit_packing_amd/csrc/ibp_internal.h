@@ -24,7 +24,7 @@ constexpr uint32_t enc_threads(bool pos, uint32_t W, bool big = false) {
   return big ? 1024u : (pos && W != 16 ? 256u : 512u);
 }
 constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t halves = 1, bool big = false) {
-  return (pair || (halves == 2 && W == 32) ? 32u : 16u) * enc_threads(pos, W, big);
+  return (pair || (halves == 2 && W == 32 && !big) ? 32u : 16u) * enc_threads(pos, W, big);
 }
 // From 2^23 chunks on (ibp_set_halves_min_chunks; smaller launches do not fill the
 // GPU and finish sooner with one-image tiles), a compression tile of 32- or 64-bit
@@ -47,7 +47,11 @@ inline uint32_t enc_halves(bool pos, bool pair, uint32_t W, uint32_t S) {
 // tile doubles (1024 threads, 16384 chunks, two workgroups per CU): each look-back
 // then covers 128 KB (measured on the id stream, which fits: 1.19 -> 1.12 ms; tiles
 // that do not fit ran 2-13% slower at this size, so the others keep 512 threads).
+#ifdef IBP_BIG32
+inline bool enc_big(uint32_t W, uint32_t halves, uint32_t pc) { return halves == 2 && ((W == 64 && 2 * pc > W + 1) || W == 32); }
+#else
 inline bool enc_big(uint32_t W, uint32_t halves, uint32_t pc) { return halves == 2 && W == 64 && 2 * pc > W + 1; }
+#endif
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
@@ -58,6 +62,18 @@ constexpr uint32_t kMetaMaxBlocks = 256;
 constexpr uint32_t kMetaThreads = 1024;  // threads per workgroup of the one-count kernel
 
 // Status words of the compression look-back: 2-bit flag above a 62-bit value.
+// Look-back status words, one per tile, are spread so that tiles in flight together
+// do not share a 128-byte line: tile t's word is word t / 2^lg of line t mod 2^lg
+// (2^lg lines of 16 words, 2^lg >= ntiles / 16), so the 16 tiles of a line lie 2^lg
+// apart.  Packed 16 to a line, consecutive tiles' publishing stores and their
+// successors' polling loads contended for the same lines (measured: compression
+// 8-10% slower on every workload).
+inline uint32_t status_lg(uint64_t ntiles) {
+  uint32_t lg = 0;
+  while ((16ull << lg) < ntiles) ++lg;
+  return lg;
+}
+inline uint64_t status_words(uint64_t ntiles) { return 16ull << status_lg(ntiles); }  // < 2 ntiles + 32
 constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagPrefix = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
@@ -100,7 +116,7 @@ struct EncodeArgs {
   const void *in;
   uint32_t *stream;    // dword view of the output stream
   uint64_t *off;       // nseg + 1 bit offsets
-  uint64_t *status;    // ntiles look-back words
+  uint64_t *status;    // status_words(ntiles) look-back words, tile t's at status_slot(t, st_lg)
   uint64_t *tails;     // ntiles hand-over words (the dword shared by tiles t and t + 1)
   uint32_t *control;   // [0] unused, [1] abort flag
   uint32_t *err;       // optional
@@ -116,6 +132,7 @@ struct EncodeArgs {
   uint32_t obuf_dw;    // LDS dwords for the packed tile
   uint32_t pair;       // 1: W = 16 chunk pairs (one Mask, S a multiple of 64, input 4-byte aligned)
   uint32_t wait_limit; // look-back polls of one unpublished predecessor before a tile gives up
+  uint32_t st_lg;      // status_lg(ntiles)
   uint32_t halves;     // 2: the tile is packed and stored in two halves through a half-size image
   uint32_t big;        // 1: 1024-thread tiles (enc_big)
 };
@@ -172,6 +189,7 @@ struct SlotArgs {
 
 // Comparison codec (BF16 exponent coding): elements per block.
 constexpr uint32_t kZipBlock = 4096;
+constexpr uint32_t kZipWG = 4;  // blocks per compressor workgroup (one look-back each)
 
 struct ZipArgs {
   const uint16_t *in;  // compress: BF16 words (16-byte aligned)
@@ -181,13 +199,14 @@ struct ZipArgs {
   uint8_t *esc;        // escape exponents
   uint64_t esc_bytes;  // decompress: readable escape bytes
   uint64_t *eoff;      // nblk + 1 escape offsets
-  uint64_t *status;    // compress: look-back words, nblk
+  uint64_t *status;    // compress: status_words(workgroups) look-back words (status_slot, st_lg)
   uint32_t *control;   // compress: [0] unused, [1] abort flag
   uint32_t *err;       // optional
   uint64_t n;
   uint64_t nblk;
   uint32_t table[7];   // exponents of codes 1..7, distinct
   uint32_t wait_limit; // compress: look-back polls of one unpublished predecessor before giving up
+  uint32_t st_lg;      // compress: status_lg(workgroups)
 };
 
 constexpr uint32_t kNotPow2 = 0xFFFFFFFFu;

@@ -26,7 +26,6 @@ using namespace dev;
 constexpr uint32_t kGroup = 8;                          // consecutive elements per thread and group
 constexpr uint32_t kHalf = kZipBlock / 2;               // elements per group pass
 constexpr uint32_t kPlane = kZipBlock / 8;              // bytes per code plane
-constexpr uint32_t kZipWG = 4;                          // blocks per compressor workgroup
 
 // Inclusive scan of v over the workgroup (256 threads); *total gets the sum.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t lane, uint32_t wave, uint32_t *wsum,
@@ -140,7 +139,7 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   }
   // the workgroup's escape count first, published at once for the successors'
   // look-back; then the sign-mantissa bytes and code planes, which need no offset
-  if (tid == 0) lookback_publish(a.status, g, wtot);
+  if (tid == 0) lookback_publish(a.status, a.st_lg, g, wtot);
 #pragma unroll
   for (uint32_t b = 0; b < kZipWG; ++b) {
     if (b >= nbw) continue;
@@ -164,7 +163,7 @@ __global__ void __launch_bounds__(kBlock) zip_encode_kernel(ZipArgs a) {
   if (wave == 0) {
     bool timed_out = false;
     const uint64_t excl = g == 0 ? 0ull
-                                 : lookback_finish(a.status, a.control, a.err, g, (int64_t)g - 1, 0, wtot,
+                                 : lookback_finish(a.status, a.st_lg, a.control, a.err, g, (int64_t)g - 1, 0, wtot,
                                                    a.wait_limit, lane, timed_out);
     if (lane == 0) {
       s_excl = excl;
@@ -311,9 +310,10 @@ hipError_t launch_zip_encode(const ZipArgs &a, hipStream_t s) {
   if (a.nblk == 0) return hipSuccess;
   if (a.nblk > 0x7FFFFFFFull) return hipErrorInvalidValue;
   // clear the control words and status words (a kernel, not a memset node)
-  hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), a.nblk + 1, s);
+  const uint64_t groups = (a.nblk + kZipWG - 1) / kZipWG;
+  hipError_t e = launch_zero(reinterpret_cast<uint64_t *>(a.control), 1 + status_words(groups), s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(zip_encode_kernel, dim3((uint32_t)((a.nblk + kZipWG - 1) / kZipWG)), dim3(kBlock), 0, s, a);
+  hipLaunchKernelGGL(zip_encode_kernel, dim3((uint32_t)groups), dim3(kBlock), 0, s, a);
   return hipGetLastError();
 }
 

@@ -314,7 +314,8 @@ IBP_API int ibp_decompress_pos(const ibp_pos_meta_t *meta, const void *stream_in
  * decreasing mass order, equal masses by smaller exponent: 7 bytes to table_out. */
 IBP_API int ibp_zip_table_from_sigma(double sigma, uint8_t *table_out);
 
-/* ceil(n / 4096); code plane bytes 1536 * blocks; compression workspace 8 + 8 * blocks. */
+/* ceil(n / 4096); code plane bytes 1536 * blocks; compression workspace 8 bytes plus
+ * 8 per look-back status word (16 per line over 2^k lines, 16 * 2^k >= ceil(blocks / 4)). */
 IBP_API uint64_t ibp_zip_blocks(uint64_t n);
 IBP_API uint64_t ibp_zip_codes_bytes(uint64_t n);
 IBP_API uint64_t ibp_zip_workspace_bytes(uint64_t n);

@@ -50,10 +50,15 @@ def test_size_queries(ibp):
     assert ibp.ibp_stream_bytes(0) == 0
     assert ibp.ibp_stream_bytes(1) == 16
     assert ibp.ibp_stream_bytes(129) == 32
-    # 8 bytes of control words + 16 per compression tile of 4096 chunks (whole segments)
-    assert ibp.ibp_compress_workspace_bytes(4096, 256) == 8 + 16 * 1
-    assert ibp.ibp_compress_workspace_bytes(4097, 256) == 8 + 16 * 2
-    assert ibp.ibp_compress_workspace_bytes(4096, 1000) == 8 + 16 * 2  # 4 segments of 1000 per tile
+    # 8 bytes of control words, then for T compression tiles of 4096 chunks (whole
+    # segments) the look-back status words, 16 to a line over the smallest power-of-two
+    # number of lines that holds T, and T hand-over words
+    assert ibp.ibp_compress_workspace_bytes(4096, 256) == 8 + 8 * (16 + 1)
+    assert ibp.ibp_compress_workspace_bytes(4097, 256) == 8 + 8 * (16 + 2)
+    assert ibp.ibp_compress_workspace_bytes(4096, 1000) == 8 + 8 * (16 + 2)  # 4 segments of 1000 per tile
+    assert ibp.ibp_compress_workspace_bytes(16 * 4096, 256) == 8 + 8 * (16 + 16)
+    assert ibp.ibp_compress_workspace_bytes(17 * 4096, 256) == 8 + 8 * (32 + 17)
+    assert ibp.ibp_compress_workspace_bytes(100 * 4096, 256) == 8 + 8 * (128 + 100)
     assert ibp.ibp_metadata_workspace_bytes(10, 64) == (64 + 66) * 8
 
 
@@ -144,7 +149,8 @@ def test_zip_table_matches_oracle(ibp):
     lib = ibp.load_library()
     assert lib.ibp_zip_table_from_sigma(0.0, (ctypes.c_uint8 * 7)()) == ibp.IBP_ERR_INVALID_ARG
     assert ibp.load_library().ibp_zip_blocks(4097) == 2 and lib.ibp_zip_codes_bytes(4097) == 3072
-    assert lib.ibp_zip_workspace_bytes(4096) == 16
+    assert lib.ibp_zip_workspace_bytes(4096) == 8 + 8 * 16  # one workgroup's status line
+    assert lib.ibp_zip_workspace_bytes(4096 * 4 * 17) == 8 + 8 * 32  # 17 workgroups of four blocks
     t = (ctypes.c_uint8 * 7)(1, 2, 3, 4, 5, 6, 6)  # repeated exponent
     assert lib.ibp_zip_compress(t, FAKE, 16, FAKE, FAKE, FAKE, 16, FAKE, FAKE, 64, None, None) == ibp.IBP_ERR_INVALID_ARG
 
