@@ -217,7 +217,7 @@ IBP_API uint64_t ibp_metadata_workspace_bytes(uint64_t n_sample_chunks, uint32_t
 IBP_API uint64_t ibp_compress_workspace_bytes(uint64_t n_chunks, uint32_t S) {
   if (S == 0) return 0;
   const uint64_t t = enc_tiles(n_chunks, S, true, false, 32);  // the smallest tiles (position metadata, W > 16)
-  return 8 + 8 * (status_words(t) + t);  // control, status words, hand-over words
+  return t ? 8 + 8 * (status_words(t) + t) : 8;  // control, status words, hand-over words
 }
 
 IBP_API int ibp_build_metadata(const void *d_samples, uint64_t n_sample_chunks, uint32_t W, double T,

@@ -53,6 +53,7 @@ def test_size_queries(ibp):
     # 8 bytes of control words, then for T compression tiles of 4096 chunks (whole
     # segments) the look-back status words, 16 to a line over the smallest power-of-two
     # number of lines that holds T, and T hand-over words
+    assert ibp.ibp_compress_workspace_bytes(0, 256) == 8  # the control words only
     assert ibp.ibp_compress_workspace_bytes(4096, 256) == 8 + 8 * (16 + 1)
     assert ibp.ibp_compress_workspace_bytes(4097, 256) == 8 + 8 * (16 + 2)
     assert ibp.ibp_compress_workspace_bytes(4096, 1000) == 8 + 8 * (16 + 2)  # 4 segments of 1000 per tile
