@@ -177,10 +177,13 @@ __device__ __forceinline__ void lds_or_field(uint32_t *s, uint32_t q, uint64_t x
 // q + 64 for a 64-bit field, must lie inside the array).  ubfe(x, 32 - sh, sh) is
 // x >> (32 - sh), and 0 for sh == 0.
 __device__ __forceinline__ void lds_or_bits(uint32_t *s, uint32_t q, uint32_t x) {
-  const uint32_t d = q >> 5, sh = q & 31u;
   if (x) {
-    atomicOr(&s[d], x << sh);
-    atomicOr(&s[d + 1], __builtin_amdgcn_ubfe(x, 32u - sh, sh));
+    // the shift and the bit-field extract read only the low 5 bits of their
+    // amounts, so q serves as the shift (q mod 32) and 32 - q as the extract offset
+    // (width q mod 32 = 0 extracts nothing)
+    uint32_t *p = s + (q >> 5);
+    atomicOr(p, x << (q & 31u));
+    atomicOr(p + 1, __builtin_amdgcn_ubfe(x, 32u - q, q));
   }
 }
 

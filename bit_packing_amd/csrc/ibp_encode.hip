@@ -186,20 +186,27 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     const uint32_t base = q * kThreads + wave * kWave;
     return b & (base >= nch ? 0ull : low_lanes(min(nch - base, kWave)));
   };
-  // kPair: participation of the even and of the odd chunk of pass q's pair (taken
-  // again when packing rather than held in scalar registers across the barriers)
-  auto even_odd = [&](uint32_t q, bool &h0, bool &h1) {
-    const uint32_t c = 2u * (q * kThreads + tid);
-    const uint32_t m32 = (uint32_t)mask, b32 = (uint32_t)bitval;
-    h0 = c < nch && (((v2[q] & 0xFFFFu) ^ b32) & m32) == 0u;
-    h1 = c + 1u < nch && (((v2[q] >> 16) ^ b32) & m32) == 0u;
+  // kPair: participation ballots of the even (E) and the odd (O) chunks of pass q's
+  // pairs, from one XOR-AND of the pair word with Bitval and Mask in both halves; lanes
+  // whose chunk lies past the tile's end take no part (scalar masks; none in a full
+  // tile).  Taken again when packing rather than held across the barriers.
+  auto pair_ballots = [&](uint32_t q, uint64_t &E, uint64_t &O) {
+    const uint32_t m2 = (uint32_t)mask * 0x10001u, b2 = (uint32_t)bitval * 0x10001u;
+    const uint32_t d = (v2[q] ^ b2) & m2;
+    E = ballot((d & 0xFFFFu) == 0u);
+    O = ballot(d < 0x10000u);
+    if (!full_tile) {
+      const uint32_t cb = 2u * (q * kThreads + wave * kWave);  // the pass's first chunk
+      const uint32_t left = cb < nch ? nch - cb : 0u;         // chunks of the pass in the tile
+      E &= low_lanes(min((left + 1u) >> 1, kWave));
+      O &= low_lanes(min(left >> 1, kWave));
+    }
   };
   if constexpr (kPair) {
 #pragma unroll
     for (uint32_t q = 0; q < kQP; ++q) {
-      bool h0, h1;
-      even_odd(q, h0, h1);
-      const uint64_t E = ballot(h0), O = ballot(h1);
+      uint64_t E, O;
+      pair_ballots(q, E, O);
       if (lane == 0) {  // the span's two 64-chunk blocks: lanes 0-31, lanes 32-63
         const uint32_t b = 2u * (q * kWaves + wave);
         bal[b] = (E & 0xFFFFFFFFull) | (O << 32);
@@ -305,22 +312,34 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   };
   const uint32_t i_lane = lane & (a.S - 1u);                   // small-S: index in segment
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
-  if constexpr (kPair) {
+  // kPair: the passes, in one copy for S a multiple of 128 (a pass's two 64-chunk
+  // blocks lie in one segment, whose start and length are then scalar) and one for
+  // S = 64 mod 128 (the blocks may lie in different segments)
+  auto pair_passes = [&](auto one_seg) __attribute__((always_inline)) {
 #pragma unroll
     for (uint32_t q = 0; q < kQP; ++q) {
       const uint32_t blk = 2u * (q * kWaves + wave);  // first of the span's two 64-chunk blocks
       const uint32_t cb = blk * kWave;
       if (cb >= nch) continue;  // uniform
       const uint32_t c = cb + 2u * lane;
-      // the two blocks may lie in different segments (S = 64)
-      const uint32_t s_lo = seg_start(cb), s_hi = seg_start(min(cb + kWave, nch - 1u));
-      const uint32_t s0 = lane < 32u ? s_lo : s_hi;
+      const uint32_t s_lo = seg_start(cb);
+      uint32_t s0 = s_lo;
+      if constexpr (!decltype(one_seg)::value) {
+        const uint32_t s_hi = seg_start(min(cb + kWave, nch - 1u));
+        s0 = lane < 32u ? s_lo : s_hi;
+      }
       const uint32_t m = min(a.S, nch - s0);
-      bool h0, h1;
-      even_odd(q, h0, h1);
-      const uint32_t saved =
-          __umul24(pc, pref_at(2u * q * kWaves, 2u) + count_below(ballot(h0)) + count_below(ballot(h1)));
-      const uint32_t pos = s0 + m + c * W - saved;
+      uint64_t E, O;
+      pair_ballots(q, E, O);
+      const bool h0 = __builtin_amdgcn_inverse_ballot_w64(E), h1 = __builtin_amdgcn_inverse_ballot_w64(O);
+      // compressed chunks before the lane's pair: the block prefix, then the even and
+      // the odd chunks of the lower lanes, accumulated by the lane-count instructions
+      uint32_t cnt = pref_at(2u * q * kWaves, 2u);
+      cnt = __builtin_amdgcn_mbcnt_lo((uint32_t)E, cnt);
+      cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(E >> 32), cnt);
+      cnt = __builtin_amdgcn_mbcnt_lo((uint32_t)O, cnt);
+      cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(O >> 32), cnt);
+      const uint32_t pos = s0 + m + c * W - __umul24(pc, cnt);
       const uint32_t x = v2[q];
       uint32_t ext = 0;
       if constexpr (NR == 0) {
@@ -333,6 +352,14 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       const uint32_t field = a0 | (a1 << (h0 ? W - pc : W));
       lds_or_bits(obuf, pos, field);  // lanes past the tile's end hold 0 (chunks read as 0, not matching)
     }
+  };
+  if constexpr (kPair) {
+    // the pair words are opaque from here on, so the compiler takes the ballots again
+    // instead of keeping 32 of them (or their per-lane flags) across the barriers
+#pragma unroll
+    for (uint32_t q = 0; q < kQP; ++q) asm volatile("" : "+v"(v2[q]));
+    if ((a.S & 127u) == 0u) pair_passes(std::true_type{});
+    else pair_passes(std::false_type{});
   }
   // the passes of half h of the tile (kHalves == 2: the tile's two halves of
   // kTile / 2 chunks are packed and stored one after the other through an image of
