@@ -473,6 +473,12 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   // size of half a tile stored raw) is packed entirely before the look-back and
   // stored once
   const bool whole = agg <= (uint64_t)(kTile / 2) * (W + 1);
+  if constexpr (kRetake) {
+    // as in the pair form: the chunks are opaque from here on, so the ballots are
+    // taken again when packing rather than kept across the barriers
+#pragma unroll
+    for (uint32_t q = 0; q < kQ; ++q) asm volatile("" : "+v"(v[q]));
+  }
   pack(std::integral_constant<uint32_t, 0>{}, 0u);
   if constexpr (kHalves == 2) {
     if (whole) pack(std::integral_constant<uint32_t, 1>{}, 0u);
