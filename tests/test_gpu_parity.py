@@ -542,3 +542,47 @@ def test_lookback_give_up_path(ibp):
     assert int(err.item()) == 0
     assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off)
     assert np.array_equal(comp.stream[:nb].cpu().numpy(), ref_stream)
+
+
+@pytest.mark.parametrize("tiles", [1, 15, 16, 17, 31, 32, 33, 255, 256, 257])
+def test_lookback_status_layout_tile_counts(ibp, tiles):
+    """Tile counts on both sides of the status layout's line counts (16 status words
+    to a line over a power-of-two number of lines: a new line count from 16 * 2^k + 1
+    tiles on), for the one-Mask compressor (8192-chunk tiles at W = 64), the
+    position-metadata compressor (4096-chunk tiles) and the BF16 exponent codec
+    (workgroups of 16,384 elements), each against the oracle; every input ends in a
+    ragged last tile."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(7000 + tiles)
+    W, S = 64, 256
+    mask, bitval = 0x7C007C007C007C00, 0x3800380038003800
+    v = _data(rng, tiles * 8192 - 100, W, mask, bitval, 0.9)
+    _run_case(ibp, dev, v, W, S, mask, bitval, f"{tiles} tiles")
+    # position metadata: 4096-chunk tiles
+    n = tiles * 4096 - 37
+    masks = rng.integers(0, 1 << 62, S, dtype=np.uint64) & np.uint64(0xFFFF0000FFFF0000)
+    bitvals = rng.integers(0, 1 << 62, S, dtype=np.uint64) & masks
+    vp = rng.integers(0, 1 << 62, n, dtype=np.uint64)
+    pos = np.arange(n) % S
+    keep = rng.random(n) < 0.8
+    vp[keep] = (vp[keep] & ~masks[pos[keep]]) | bitvals[pos[keep]]
+    say(f"position tables: {tiles} tiles, n={n}")
+    meta = ibp.PosMeta(W, S, torch.from_numpy(masks.view(np.int64)).to(dev),
+                       torch.from_numpy(bitvals.view(np.int64)).to(dev))
+    x = torch.from_numpy(vp.view(np.uint8).copy()).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    ref_stream, ref_off = oracle.encode_pos(vp, W, masks, bitvals, S)
+    comp = ibp.ibp_compress_pos(meta, x, err=err)
+    assert np.array_equal(comp.offsets.cpu().numpy().view(np.uint64), ref_off), "position tables: offsets"
+    assert np.array_equal(comp.stream[: ref_stream.size].cpu().numpy(), ref_stream), "position tables: stream"
+    # BF16 exponent codec: workgroups of four 4096-element blocks
+    m = tiles * 16384 - 5
+    u = (rng.standard_normal(m).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    say(f"BF16 exponent codec: {tiles} workgroups, n={m}")
+    table = oracle.zip_table(1.0)
+    z = ibp.ibp_zip_compress(bytes(table), torch.from_numpy(u.view(np.int16).copy()).to(dev), err=err)
+    sm, codes, esc, eoff = oracle.zip_encode(u, table)
+    assert np.array_equal(z.eoff.cpu().numpy().view(np.uint64), eoff), "BF16 codec: escape offsets"
+    assert np.array_equal(z.esc[: esc.size].cpu().numpy(), esc), "BF16 codec: escapes"
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
