@@ -84,7 +84,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   static_assert(!kPair || (sizeof(T) == 2 && kMode == 2 && !kPos), "pairs: W = 16, S a multiple of 64, one Mask");
   static_assert(enc_threads(kPos, sizeof(T) * 8) > kWave, "the two hand-over atomics come from two wavefronts");
   static_assert(kHalves == 1 || (!kPair && kMode != kModeGeneral), "halves: S a power of two");
-  static_assert(!kBig || (kHalves == 2 && sizeof(T) >= 4), "1024-thread tiles: 32- or 64-bit chunks in halves");
+  static_assert(!kBig || (kHalves == 2 && sizeof(T) == 8), "1024-thread tiles: 64-bit chunks in halves");
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kThreads = enc_threads(kPos, W, kBig);
   constexpr uint32_t kWaves = kThreads / kWave;
@@ -610,10 +610,10 @@ static hipError_t launch_encode_t(const EncodeArgs &a, const CodecParams &p, siz
   // two-half tiles: 32-bit chunks with one Mask, 64-bit chunks (enc_halves)
   if constexpr (sizeof(T) >= 4 && !kPair && M != kModeGeneral && !(kPos && sizeof(T) == 4)) {
     if (a.halves == 2) {
-      if constexpr (!kPos) {
+      if constexpr (sizeof(T) == 8 && !kPos) {
         if (a.big) {
           hipLaunchKernelGGL((encode_kernel<T, M, NR, false, false, 2, true>), dim3((uint32_t)a.ntiles),
-                             dim3(enc_threads(false, sizeof(T) * 8, true)), shmem, s, a, p);
+                             dim3(enc_threads(false, 64, true)), shmem, s, a, p);
           return hipGetLastError();
         }
       }

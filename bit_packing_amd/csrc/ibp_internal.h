@@ -24,7 +24,7 @@ constexpr uint32_t enc_threads(bool pos, uint32_t W, bool big = false) {
   return big ? 1024u : (pos && W != 16 ? 256u : 512u);
 }
 constexpr uint32_t enc_tile_chunks(bool pos, bool pair, uint32_t W, uint32_t halves = 1, bool big = false) {
-  return (pair || (halves == 2 && W == 32 && !big) ? 32u : 16u) * enc_threads(pos, W, big);
+  return (pair || (halves == 2 && W == 32) ? 32u : 16u) * enc_threads(pos, W, big);
 }
 // From 2^23 chunks on (ibp_set_halves_min_chunks; smaller launches do not fill the
 // GPU and finish sooner with one-image tiles), a compression tile of 32- or 64-bit
@@ -47,11 +47,7 @@ inline uint32_t enc_halves(bool pos, bool pair, uint32_t W, uint32_t S) {
 // tile doubles (1024 threads, 16384 chunks, two workgroups per CU): each look-back
 // then covers 128 KB (measured on the id stream, which fits: 1.19 -> 1.12 ms; tiles
 // that do not fit ran 2-13% slower at this size, so the others keep 512 threads).
-#ifdef IBP_BIG32
-inline bool enc_big(uint32_t W, uint32_t halves, uint32_t pc) { return halves == 2 && ((W == 64 && 2 * pc > W + 1) || W == 32); }
-#else
 inline bool enc_big(uint32_t W, uint32_t halves, uint32_t pc) { return halves == 2 && W == 64 && 2 * pc > W + 1; }
-#endif
 // Decompression tile: a wavefront decodes about this many chunks at a time,
 // with at most this many segments (rows) per tile.
 constexpr uint32_t kDecTileChunks = 512;
@@ -61,7 +57,6 @@ constexpr uint32_t kGatherMaxRows = 8;   // rows per wavefront of a gather from 
 constexpr uint32_t kMetaMaxBlocks = 256;
 constexpr uint32_t kMetaThreads = 1024;  // threads per workgroup of the one-count kernel
 
-// Status words of the compression look-back: 2-bit flag above a 62-bit value.
 // Look-back status words, one per tile, are spread so that tiles in flight together
 // do not share a 128-byte line: tile t's word is word t / 2^lg of line t mod 2^lg
 // (2^lg lines of 16 words, 2^lg >= ntiles / 16), so the 16 tiles of a line lie 2^lg
@@ -74,6 +69,7 @@ inline uint32_t status_lg(uint64_t ntiles) {
   return lg;
 }
 inline uint64_t status_words(uint64_t ntiles) { return 16ull << status_lg(ntiles); }  // < 2 ntiles + 32
+// Status words of the compression look-back: 2-bit flag above a 62-bit value.
 constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagPrefix = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1;
