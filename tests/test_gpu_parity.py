@@ -383,6 +383,30 @@ def test_zero_copy_compress(ibp, src, dst):
     assert int(err.item()) == 0
 
 
+@pytest.mark.parametrize("W,S", [(64, 256), (16, 1024), (32, 100), (64, 3)])
+def test_pinned_stream_decompress(ibp, W, S):
+    """Whole-tensor decompression with the oracle's stream in pinned host memory, read
+    zero-copy by the decoder (offsets in HBM): the output equals the input, over many
+    tiles and a ragged last segment."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(W * 3 + S)
+    mask = {16: 0x7C00, 32: 0x78000000, 64: 0x7C007C007C007C00}[W]
+    bitval = mask & 0x3838383838383838
+    n = 400 * S + S // 2 + 1
+    v = _data(rng, n, W, mask, bitval, 0.95)
+    meta = ibp.make_meta(W, mask, bitval)
+    ref_stream, ref_off = oracle.encode(v, W, mask, bitval, S)
+    host = torch.zeros(ibp.ibp_stream_bytes(int(ref_off[-1])), dtype=torch.uint8, pin_memory=True)
+    host[: ref_stream.size].copy_(torch.from_numpy(ref_stream))
+    off = torch.from_numpy(ref_off.view(np.int64).copy()).to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    say(f"pinned stream decompress W={W} S={S} n={n}")
+    back = ibp.ibp_decompress(meta, host, off, n, S, err=err)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().numpy(), v.view(np.uint8))
+    assert int(err.item()) == 0
+
+
 @pytest.mark.parametrize("W,S", [(32, 128), (64, 32), (32, 100), (64, 1024), (32, 4), (16, 64), (16, 200)])
 @pytest.mark.parametrize("where", ["device", "pinned"])
 def test_slots_parity(ibp, W, S, where):
