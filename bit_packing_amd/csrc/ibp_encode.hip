@@ -190,27 +190,38 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   // pairs, from one XOR-AND of the pair word with Bitval and Mask in both halves; lanes
   // whose chunk lies past the tile's end take no part (scalar masks; none in a full
   // tile).  Taken again when packing rather than held across the barriers.
+  // Mask and Bitval in both halves are held in vector registers (opaque to the
+  // compiler): with both in scalar registers, the one three-operand logic op per
+  // pass would need two of them, more than one instruction may read.
+  // The low-half test compares against a zero held the same way (the compare that
+  // selects a half takes no constant operand).
+  uint32_t m2 = (uint32_t)mask * 0x10001u, b2 = (uint32_t)bitval * 0x10001u, zero = 0u;
+  if constexpr (kPair) asm volatile("" : "+v"(m2), "+v"(b2), "+v"(zero));
   auto pair_ballots = [&](uint32_t q, uint64_t &E, uint64_t &O) {
-    const uint32_t m2 = (uint32_t)mask * 0x10001u, b2 = (uint32_t)bitval * 0x10001u;
-    const uint32_t d = (v2[q] ^ b2) & m2;
-    E = ballot((d & 0xFFFFu) == 0u);
+    uint32_t d = (v2[q] ^ b2) & m2;
+    asm("" : "+v"(d));  // one three-operand logic op, both tests on its result
+    E = ballot((d & 0xFFFFu) == zero);
     O = ballot(d < 0x10000u);
     if (!full_tile) {
       const uint32_t cb = 2u * (q * kThreads + wave * kWave);  // the pass's first chunk
-      const uint32_t left = cb < nch ? nch - cb : 0u;         // chunks of the pass in the tile
+      const uint32_t left = uniform(cb < nch ? nch - cb : 0u);  // chunks of the pass in the tile
       E &= low_lanes(min((left + 1u) >> 1, kWave));
       O &= low_lanes(min(left >> 1, kWave));
     }
   };
   if constexpr (kPair) {
+    // the span's two 64-chunk blocks are lanes 0-31 and 32-63: words 2p and 2p + 1
+    // hold the even and the odd ballot whole, low halves for the first block (the
+    // wavefront's base address in a vector register, the pass in the offset field)
+    uint32_t bw = 2u * wave;
+    asm volatile("" : "+v"(bw));
 #pragma unroll
     for (uint32_t q = 0; q < kQP; ++q) {
       uint64_t E, O;
       pair_ballots(q, E, O);
-      if (lane == 0) {  // the span's two 64-chunk blocks: lanes 0-31, lanes 32-63
-        const uint32_t b = 2u * (q * kWaves + wave);
-        bal[b] = (E & 0xFFFFFFFFull) | (O << 32);
-        bal[b + 1] = (E >> 32) | (O & 0xFFFFFFFF00000000ull);
+      if (lane == 0) {
+        bal[bw + 2u * q * kWaves] = E;
+        bal[bw + 2u * q * kWaves + 1u] = O;
       }
     }
   }
@@ -249,7 +260,12 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
 #pragma unroll
     for (uint32_t k = 0; k < kPer; ++k) {
       const uint32_t b = kPer * lane + k;
-      cs[k] = b < kBal ? (kPos ? (uint32_t)bal[b] : popc(bal[b])) : 0u;
+      if constexpr (kPair) {
+        const uint32_t sh = (b & 1u) * 32u;
+        cs[k] = b < kBal ? popc((uint32_t)(bal[b & ~1u] >> sh)) + popc((uint32_t)(bal[b | 1u] >> sh)) : 0u;
+      } else {
+        cs[k] = b < kBal ? (kPos ? (uint32_t)bal[b] : popc(bal[b])) : 0u;
+      }
       c += cs[k];
     }
     uint32_t x = wave_incl_scan(c) - c;
@@ -262,9 +278,10 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     if (lane == kWave - 1) pref[kBal] = x;
   }
   __syncthreads();
-  // compressed chunks among tile chunks [0, x), any x <= tile size
+  // compressed chunks among tile chunks [0, x), any x <= tile size (kPair: x a
+  // multiple of 64, segments of a multiple of 64 chunks)
   auto g = [&](uint32_t x) -> uint32_t {
-    const uint32_t b = x >> 6, o = x & 63u;
+    const uint32_t b = x >> 6, o = kPair ? 0u : x & 63u;
     return pref[b] + (o ? popc(bal[b] & low_lanes(o)) : 0u);
   };
   // bits saved by the matching chunks among tile chunks [0, x), any x < tile size
@@ -312,6 +329,13 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
   };
   const uint32_t i_lane = lane & (a.S - 1u);                   // small-S: index in segment
   const uint64_t seg_below = low_lanes(lane & ~(a.S - 1u));     // small-S: earlier segments' lanes
+  // kPair: per-lane terms of the passes kept in vector registers (opaque, so they
+  // are not formed again from scalar values in every pass): the lane's first
+  // chunk's bit if every chunk before it were raw (2 W per lane), -popcount(Mask)
+  // for the one multiply-add, and W - popcount(Mask), a compressed chunk's payload
+  uint32_t lane2w = lane * 2u * W, wpc = W - pc;
+  int32_t npc = -(int32_t)pc;
+  if constexpr (kPair) asm volatile("" : "+v"(lane2w), "+v"(wpc), "+v"(npc));
   // kPair: the passes, in one copy for S a multiple of 128 (a pass's two 64-chunk
   // blocks lie in one segment, whose start and length are then scalar) and one for
   // S = 64 mod 128 (the blocks may lie in different segments)
@@ -321,7 +345,6 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       const uint32_t blk = 2u * (q * kWaves + wave);  // first of the span's two 64-chunk blocks
       const uint32_t cb = blk * kWave;
       if (cb >= nch) continue;  // uniform
-      const uint32_t c = cb + 2u * lane;
       const uint32_t s_lo = seg_start(cb);
       uint32_t s0 = s_lo;
       if constexpr (!decltype(one_seg)::value) {
@@ -332,14 +355,16 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
       uint64_t E, O;
       pair_ballots(q, E, O);
       const bool h0 = __builtin_amdgcn_inverse_ballot_w64(E), h1 = __builtin_amdgcn_inverse_ballot_w64(O);
-      // compressed chunks before the lane's pair: the block prefix, then the even and
-      // the odd chunks of the lower lanes, accumulated by the lane-count instructions
-      uint32_t cnt = pref_at(2u * q * kWaves, 2u);
-      cnt = __builtin_amdgcn_mbcnt_lo((uint32_t)E, cnt);
+      // compressed chunks before the lane's pair: the block prefix (in the scalar
+      // part), then the even and the odd chunks of the lower lanes, accumulated by
+      // the lane-count instructions
+      uint32_t cnt = __builtin_amdgcn_mbcnt_lo((uint32_t)E, 0u);
       cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(E >> 32), cnt);
       cnt = __builtin_amdgcn_mbcnt_lo((uint32_t)O, cnt);
       cnt = __builtin_amdgcn_mbcnt_hi((uint32_t)(O >> 32), cnt);
-      const uint32_t pos = s0 + m + c * W - __umul24(pc, cnt);
+      uint32_t base = s0 + m + cb * W - pc * pref_at(2u * q * kWaves, 2u);
+      if constexpr (decltype(one_seg)::value) base = uniform(base);  // formed by scalar instructions
+      const uint32_t pos = base + lane2w + __mul24(npc, (int)cnt);
       const uint32_t x = v2[q];
       uint32_t ext = 0;
       if constexpr (NR == 0) {
@@ -349,7 +374,7 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
         for (uint32_t r = 0; r < NR; ++r) ext |= (x >> p.runs.shift[r]) & ((uint32_t)p.runs.pmask[r] * 0x10001u);
       }
       const uint32_t a0 = h0 ? (ext & 0xFFFFu) : (x & 0xFFFFu), a1 = h1 ? (ext >> 16) : (x >> 16);
-      const uint32_t field = a0 | (a1 << (h0 ? W - pc : W));
+      const uint32_t field = a0 | (a1 << (h0 ? wpc : W));
       lds_or_bits(obuf, pos, field);  // lanes past the tile's end hold 0 (chunks read as 0, not matching)
     }
   };
@@ -455,7 +480,9 @@ __global__ void __launch_bounds__(enc_threads(kPos, sizeof(T) * 8, kBig), (kPair
     const uint32_t blk = lane * kWaves + wave, cb = blk * kWave;
     if (lane >= qb && lane < qe && cb < nch) {
       const uint32_t s0 = seg_start(cb);
-      const uint64_t hdr = kPair ? interleave32((uint32_t)bal[blk], (uint32_t)(bal[blk] >> 32)) : bal[blk];
+      const uint32_t sh = (blk & 1u) * 32u;
+      const uint64_t hdr = kPair ? interleave32((uint32_t)(bal[blk & ~1u] >> sh), (uint32_t)(bal[blk | 1u] >> sh))
+                                 : bal[blk];
       lds_or_bits(obuf, s0 * W + cb - pc * pref[s0 >> 6] - H, hdr);
     }
   }
