@@ -208,27 +208,49 @@ template <typename T, uint32_t NR> struct Row4 {
   static_assert(sizeof(T) == 2, "four chunks per lane for W = 16");
   static constexpr uint32_t W = 16;
   static constexpr uint32_t kStep = 4 * kWave;
-  uint32_t hp = 0, base = 0;  // hp: this lane's first participation bit
+  // hd, hsh: the dword and the bit in it of this lane's first participation bit (a
+  // pass is 256 bits, so hsh is the same in every pass and hd moves by 8); lw: 4 W
+  // times the lane; wpc: W - popcount(Mask), a compressed chunk's payload.  The
+  // per-lane terms are opaque to the compiler, so they stay in vector registers
+  // rather than being formed again from scalar values in every pass.
+  uint32_t hd = 0, hsh = 0, base = 0, lw = 0, wpc = 0;
   uint64_t *op = nullptr;
   Row4() = default;
   __device__ __forceinline__ Row4(uint32_t S, uint32_t lb, T *out, uint32_t lane)
-      : hp(lb + 4u * lane), base(lb + S), op(reinterpret_cast<uint64_t *>(out) + lane) {}
+      : base(lb + S), lw(lane * 4u * W), op(reinterpret_cast<uint64_t *>(out) + lane) {
+    const uint32_t hp = lb + 4u * lane;
+    hd = hp >> 5;
+    hsh = hp & 31u;
+    asm volatile("" : "+v"(hd), "+v"(hsh), "+v"(lw));
+  }
   __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
     const uint32_t pc = p.pc;
-    const uint32_t b4 = lds_field<uint32_t>(stg, hp);
+    if (q == 0u) {
+      wpc = W - pc;
+      asm volatile("" : "+v"(wpc));
+    }
+    const uint32_t b4 = __builtin_amdgcn_alignbit(stg[hd + 1u], stg[hd], hsh);
     // the selects below take the ballots back (one compare per bit)
     const uint64_t B0 = ballot((b4 & 1u) != 0u), B1 = ballot((b4 & 2u) != 0u);
     const uint64_t B2 = ballot((b4 & 4u) != 0u), B3 = ballot((b4 & 8u) != 0u);
     const bool h0 = __builtin_amdgcn_inverse_ballot_w64(B0), h1 = __builtin_amdgcn_inverse_ballot_w64(B1);
     const bool h2 = __builtin_amdgcn_inverse_ballot_w64(B2), h3 = __builtin_amdgcn_inverse_ballot_w64(B3);
-    const uint32_t below = count_below(B0) + count_below(B1) + count_below(B2) + count_below(B3);
-    const uint64_t w = lds_field<uint64_t>(stg, base + lane * 4u * W - __umul24(pc, below));
-    const uint32_t o1 = h0 ? W - pc : W, o2 = o1 + (h1 ? W - pc : W), o3 = o2 + (h2 ? W - pc : W);
+    // compressed chunks before chunk 4 lane: one chain of the lane-count instructions
+    uint32_t below = __builtin_amdgcn_mbcnt_lo((uint32_t)B0, 0u);
+    below = __builtin_amdgcn_mbcnt_hi((uint32_t)(B0 >> 32), below);
+    below = __builtin_amdgcn_mbcnt_lo((uint32_t)B1, below);
+    below = __builtin_amdgcn_mbcnt_hi((uint32_t)(B1 >> 32), below);
+    below = __builtin_amdgcn_mbcnt_lo((uint32_t)B2, below);
+    below = __builtin_amdgcn_mbcnt_hi((uint32_t)(B2 >> 32), below);
+    below = __builtin_amdgcn_mbcnt_lo((uint32_t)B3, below);
+    below = __builtin_amdgcn_mbcnt_hi((uint32_t)(B3 >> 32), below);
+    const uint64_t w = lds_field<uint64_t>(stg, (base + lw) + __mul24(-(int32_t)pc, (int32_t)below));
+    const uint32_t o1 = h0 ? wpc : W, o2 = o1 + (h1 ? wpc : W), o3 = o2 + (h2 ? wpc : W);
     const uint32_t xa = ((uint32_t)w & 0xFFFFu) | ((uint32_t)(w >> o1) << 16);
     const uint32_t xb = ((uint32_t)(w >> o2) & 0xFFFFu) | ((uint32_t)(w >> o3) << 16);
     store_nt(&op[q / 4], (uint64_t)merge16x2<NR>(p, xa, h0, h1) | ((uint64_t)merge16x2<NR>(p, xb, h2, h3) << 32));
     base += 4u * kWave * W - pc * (popc(B0) + popc(B1) + popc(B2) + popc(B3));
-    hp += 4u * kWave;
+    hd += 4u * kWave / 32u;
   }
 };
 
