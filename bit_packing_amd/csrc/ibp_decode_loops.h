@@ -168,26 +168,15 @@ template <typename T, uint32_t NR> struct Row2 {
   static constexpr uint32_t kStep = 2 * kWave;
   using P = typename std::conditional<(W == 32), uint64_t, uint32_t>::type;  // a pair of chunks
   // hd, hsh: the dword and the bit in it of this lane's first participation bit (a
-  // pass is 128 bits, so hsh is the same in every pass and hd moves by 4); lw: 2 W
-  // times the lane; wpc: W - popcount(Mask).  The per-lane terms are opaque to the
-  // compiler, so they stay in vector registers rather than being formed again from
-  // scalar values in every pass.
-  uint32_t hd = 0, hsh = 0, base = 0, lw = 0, wpc = 0;
+  // pass is 128 bits, so hsh is the same in every pass and hd moves by 4)
+  uint32_t hd = 0, hsh = 0, base = 0;
   P *op = nullptr;
   Row2() = default;
   __device__ __forceinline__ Row2(uint32_t S, uint32_t lb, T *out, uint32_t lane)
-      : base(lb + S), lw(lane * 2u * W), op(reinterpret_cast<P *>(out) + lane) {
-    const uint32_t hp = lb + 2u * lane;
-    hd = hp >> 5;
-    hsh = hp & 31u;
-    asm volatile("" : "+v"(hd), "+v"(hsh), "+v"(lw));
-  }
+      : hd((lb + 2u * lane) >> 5), hsh((lb + 2u * lane) & 31u), base(lb + S),
+        op(reinterpret_cast<P *>(out) + lane) {}
   __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
     const uint32_t pc = p.pc;
-    if (q == 0u) {
-      wpc = W - pc;
-      asm volatile("" : "+v"(wpc));
-    }
     const uint32_t b2 = __builtin_amdgcn_alignbit(stg[hd + 1u], stg[hd], hsh);
     // the selects below take the ballots back (one compare per bit)
     const uint64_t E = ballot((b2 & 1u) != 0u), O = ballot((b2 & 2u) != 0u);
@@ -196,13 +185,13 @@ template <typename T, uint32_t NR> struct Row2 {
     below = __builtin_amdgcn_mbcnt_hi((uint32_t)(E >> 32), below);
     below = __builtin_amdgcn_mbcnt_lo((uint32_t)O, below);
     below = __builtin_amdgcn_mbcnt_hi((uint32_t)(O >> 32), below);
-    const uint32_t pos0 = (base + lw) + __mul24(-(int32_t)pc, (int32_t)below);
+    const uint32_t pos0 = base + lane * 2u * W + __mul24(-(int32_t)pc, (int32_t)below);
     if constexpr (W == 16) {
       const uint32_t w = lds_field<uint32_t>(stg, pos0);
       const uint32_t x = (w & 0xFFFFu) | ((w << (h0 ? pc : 0u)) & 0xFFFF0000u);
       store_nt(&op[q / 2], (P)merge16x2<NR>(p, x, h0, h1));
     } else {
-      const uint32_t pos1 = pos0 + (h0 ? wpc : W);
+      const uint32_t pos1 = pos0 + (h0 ? W - pc : W);
       const T x0 = lds_field<T>(stg, pos0), x1 = lds_field<T>(stg, pos1);
       const T v0 = h0 ? (T)(deposit_free<T, NR>(x0, p.runs) | (T)p.bitval) : x0;
       const T v1 = h1 ? (T)(deposit_free<T, NR>(x1, p.runs) | (T)p.bitval) : x1;
