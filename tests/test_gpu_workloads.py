@@ -68,6 +68,15 @@ def test_workload_full_size(name):
     assert torch.equal(out, x), "round trip differs"
     del out
 
+    if not w.gather:
+        # the whole tensor from its stream in pinned host memory, read zero-copy
+        say(f"workload {name}: decompress from the stream in pinned host memory")
+        host = torch.zeros(ibp.ibp_stream_bytes(total), dtype=torch.uint8, pin_memory=True)
+        host[: stream_h.size].copy_(torch.from_numpy(stream_h))
+        out = ibp.ibp_decompress(meta, host, comp.offsets, comp.n_chunks, S, err=err)
+        assert torch.equal(out, x), "round trip from pinned memory differs"
+        del out, host
+
     if w.gather:
         say(f"workload {name}: gather from pinned host memory")
         n_rows = inst.data.shape[0]
