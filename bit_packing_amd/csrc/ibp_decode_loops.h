@@ -124,7 +124,7 @@ template <typename T, uint32_t NR> struct Row1 {
   uint32_t hp = 0, base = 0;
   T *o = nullptr;
   Row1() = default;
-  __device__ __forceinline__ Row1(uint32_t S, uint32_t lb, T *out, uint32_t lane)
+  __device__ __forceinline__ Row1(const CodecParams &, uint32_t S, uint32_t lb, T *out, uint32_t lane)
       : hp(lb), base(lb + S), o(out + lane) {}
   __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
     const uint64_t H = uniform64(lds_field<uint64_t>(stg, hp));  // this pass's participation bits
@@ -172,7 +172,7 @@ template <typename T, uint32_t NR> struct Row2 {
   uint32_t hd = 0, hsh = 0, base = 0;
   P *op = nullptr;
   Row2() = default;
-  __device__ __forceinline__ Row2(uint32_t S, uint32_t lb, T *out, uint32_t lane)
+  __device__ __forceinline__ Row2(const CodecParams &, uint32_t S, uint32_t lb, T *out, uint32_t lane)
       : hd((lb + 2u * lane) >> 5), hsh((lb + 2u * lane) & 31u), base(lb + S),
         op(reinterpret_cast<P *>(out) + lane) {}
   __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
@@ -223,19 +223,15 @@ template <typename T, uint32_t NR> struct Row4 {
   uint32_t hd = 0, hsh = 0, base = 0, lw = 0, wpc = 0;
   uint64_t *op = nullptr;
   Row4() = default;
-  __device__ __forceinline__ Row4(uint32_t S, uint32_t lb, T *out, uint32_t lane)
-      : base(lb + S), lw(lane * 4u * W), op(reinterpret_cast<uint64_t *>(out) + lane) {
+  __device__ __forceinline__ Row4(const CodecParams &p, uint32_t S, uint32_t lb, T *out, uint32_t lane)
+      : base(lb + S), lw(lane * 4u * W), wpc(W - p.pc), op(reinterpret_cast<uint64_t *>(out) + lane) {
     const uint32_t hp = lb + 4u * lane;
     hd = hp >> 5;
     hsh = hp & 31u;
-    asm volatile("" : "+v"(hd), "+v"(hsh), "+v"(lw));
+    asm volatile("" : "+v"(hd), "+v"(hsh), "+v"(lw), "+v"(wpc));
   }
   __device__ __forceinline__ void pass(const CodecParams &p, const uint32_t *stg, uint32_t q, uint32_t lane) {
     const uint32_t pc = p.pc;
-    if (q == 0u) {
-      wpc = W - pc;
-      asm volatile("" : "+v"(wpc));
-    }
     const uint32_t b4 = __builtin_amdgcn_alignbit(stg[hd + 1u], stg[hd], hsh);
     // the selects below take the ballots back (one compare per bit)
     const uint64_t B0 = ballot((b4 & 1u) != 0u), B1 = ballot((b4 & 2u) != 0u);
@@ -265,7 +261,7 @@ template <typename R, typename T>
 __device__ __forceinline__ uint32_t decode_one(const CodecParams &p, uint32_t S, const uint32_t *stg, uint32_t lb,
                                                uint32_t le, T *o, uint32_t lane) {
   if (lb == kBad) return 0u;
-  R r(S, lb, o, lane);
+  R r(p, S, lb, o, lane);
   for (uint32_t q = 0; q < S; q += R::kStep) r.pass(p, stg, q, lane);
   return r.base != le ? IBP_DEVERR_CORRUPT : 0u;
 }
@@ -305,7 +301,7 @@ __device__ __forceinline__ uint32_t decode_interleaved(const CodecParams &p, uin
                                                        uint32_t lane) {
   R rows[K] = {};
 #pragma unroll
-  for (uint32_t k = 0; k < K; ++k) rows[k] = R(S, lb[k], o + (uint64_t)k * S, lane);
+  for (uint32_t k = 0; k < K; ++k) rows[k] = R(p, S, lb[k], o + (uint64_t)k * S, lane);
   for (uint32_t q = 0; q < S; q += R::kStep) {
 #pragma unroll
     for (uint32_t k = 0; k < K; ++k) rows[k].pass(p, stg, q, lane);
