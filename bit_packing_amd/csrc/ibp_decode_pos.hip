@@ -424,8 +424,12 @@ __device__ __forceinline__ uint32_t pos_general(const DecodeArgs &a, const uint4
 
 // ------------------------------------------------------------------ kernel
 
-template <typename T>
-__global__ void __launch_bounds__(pos_block<sizeof(T) * 8>()) decode_pos_kernel(DecodeArgs a, CodecParams p) {
+// kOcc8: registers bounded for 8 wavefronts per SIMD (the compiler otherwise takes
+// about 106 scalar registers, which leaves room for 7, so 3 workgroups of 512 threads
+// per CU); the host launches this form where it gives more resident workgroups.
+template <typename T, bool kOcc8>
+__global__ void __launch_bounds__(pos_block<sizeof(T) * 8>(), kOcc8 ? 8 : 1)
+    decode_pos_kernel(DecodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
   constexpr uint32_t kWaves = pos_block<W>() / kWave;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
@@ -479,18 +483,27 @@ template <typename T> hipError_t launch(const DecodeArgs &a, const CodecParams &
   // four times as many workgroups as fit on the device at once, each looping over
   // its share of the tiles (measured: 1x leaves the GNN-shaped W = 32 decode 25%
   // slower, from uneven ends; 4x costs four table builds per workgroup slot)
-  int dev = 0, cus = 0, per_cu = 0;
+  // The 8-wavefront form where it fits more workgroups per CU (W >= 32; measured:
+  // mixed feature rows 210 -> 182 us, GNN-shaped rows 218 -> 207 us; where the LDS
+  // already bounds the workgroups, as for the llm tensor's 256 positions, its
+  // spilled scalar registers cost 1%, and at W = 16 4%)
+  int dev = 0, cus = 0, per_cu = 0, per_cu8 = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_pos_kernel<T>, (int)kPosBlock, shmem);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_pos_kernel<T, false>, (int)kPosBlock, shmem);
+  if (e == hipSuccess && W >= 32)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu8, decode_pos_kernel<T, true>, (int)kPosBlock, shmem);
   if (e != hipSuccess) return e;
+  const bool occ8 = per_cu8 > per_cu;
+  if (occ8) per_cu = per_cu8;
   if (per_cu < 1) return hipErrorInvalidConfiguration;
   const uint64_t tiles = (a.n_units + a.G - 1) / a.G;
   const uint64_t need = (tiles + kPosWaves - 1) / kPosWaves;
   const uint64_t fit = (uint64_t)cus * (uint64_t)per_cu;
   const dim3 grid((uint32_t)(need < 4 * fit ? need : 4 * fit));
-  hipLaunchKernelGGL(decode_pos_kernel<T>, grid, dim3(kPosBlock), shmem, s, a, p);
+  if (occ8) hipLaunchKernelGGL((decode_pos_kernel<T, true>), grid, dim3(kPosBlock), shmem, s, a, p);
+  else hipLaunchKernelGGL((decode_pos_kernel<T, false>), grid, dim3(kPosBlock), shmem, s, a, p);
   return hipGetLastError();
 }
 
