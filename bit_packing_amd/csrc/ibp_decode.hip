@@ -38,7 +38,8 @@ namespace {
 using namespace dev;
 
 template <typename T, bool kGather, uint32_t kMode, uint32_t NR>
-__global__ void __launch_bounds__(kBlock) decode_kernel(DecodeArgs a, CodecParams p) {
+__global__ void __launch_bounds__(kBlock, (kGather && sizeof(T) == 4) ? 8 : 1)
+    decode_kernel(DecodeArgs a, CodecParams p) {
   constexpr uint32_t W = sizeof(T) * 8;
   extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
   const uint32_t lane = lane_id(), wave = uniform(threadIdx.x / kWave);
